@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of the SP-TP linear layer on MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input, inputs resident
+in HBM:
+  1. agmm_chunked        sequence all-gather (SDMA chunk staging on a side stream) overlapped
+                         with the column-parallel chunk GEMMs (bf16 MFMA, fp32 accumulate);
+  2. gemm_partial        row-parallel GEMM producing this rank's bf16 partial sum
+                         (input = the column GEMM's bf16 output, same weight);
+  3. reduce_residual_rmsnorm   own partial + the peers' partials + residual, RMSNorm;
+  4. dtp_accumulate      delayed-TP update (own partial now, peers' partials of an earlier
+                         module), RMSNorm.
+Per-call times come from HIP events on the compute stream; per-chunk copy/GEMM intervals
+from the library's own event timeline (the events sit on the streams the copies and the
+kernels run on).
+
+Prints ONE JSON line.  `value` is the chunked AG-GEMM throughput in TFLOP/s (2*M*K*N per
+call over the call's wall time, exposed copy included).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 flop/clk/CU (dense)
+PEAK_HBM_GBS = 8000.0        # HBM3E
+DEFAULT_WORKLOAD = "h100_page_8192x4096"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 disables it)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def union_overlap(iv, others):
+    """Length of interval iv covered by the union of `others`."""
+    s, e = iv
+    pts = sorted((max(s, a), min(e, b)) for a, b in others if min(e, b) > max(s, a))
+    tot, cur_s, cur_e = 0.0, None, None
+    for a, b in pts:
+        if cur_e is None or a > cur_e:
+            if cur_e is not None:
+                tot += cur_e - cur_s
+            cur_s, cur_e = a, b
+        else:
+            cur_e = max(cur_e, b)
+    if cur_e is not None:
+        tot += cur_e - cur_s
+    return tot
+
+
+def cpu_baseline(wl, budget_s):
+    """Time the float64 oracle on a bounded sample of the workload (1024-row blocks)."""
+    import oracle.sptl_oracle as O
+    from sp_transformer_linear_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = wl.w_col()
+    cpr = wl.n_chunks // wl.tp
+    rows_c = wl.rows_per_chunk
+    done_rows, t_total = 0, 0.0
+    blocks = 0
+    # chunk-sized row blocks of the gathered input, in gather order, until the budget is spent
+    for q in range(wl.tp):
+        for s in range(cpr):
+            for r0 in range(0, rows_c, 1024):
+                n = min(1024, rows_c - r0)
+                rows = np.arange(s * rows_c + r0, s * rows_c + r0 + n)
+                xb = wl.shard(q, row_idx=rows)
+                t0 = time.perf_counter()
+                O.gemm_partial(xb, w)
+                t_total += time.perf_counter() - t0
+                done_rows += n
+                blocks += 1
+                if t_total >= budget_s:
+                    break
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    flops = 2.0 * done_rows * wl.K * wl.N
+    return {
+        "value": round(flops / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"float64 oracle gather-matmul on {done_rows} of {wl.M} gathered rows "
+                  f"({blocks} blocks of <=1024 rows) x W[{wl.K},{wl.N}], {t_total:.1f} s; "
+                  f"host {platform.processor() or platform.machine()}",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the multi-GPU path is not built.", file=sys.stderr)
+        return 2
+
+    import torch
+    from sp_transformer_linear_amd import sptl, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t_gen = time.perf_counter()
+    shards = [up(wl.shard(q)) for q in range(wl.tp)]
+    w_col = up(wl.w_col())
+    same_w = wl.K == wl.N and wl.K_row == wl.K and wl.H == wl.N
+    w_row = w_col if same_w else up(wl.w_row())
+    peers = [up(wl.partial(p)) for p in range(1, wl.P)]
+    residual = up(wl.residual())
+    gamma = up(wl.gamma())
+    x_res = residual.clone()
+    xg = torch.empty((wl.M, wl.K), dtype=torch.bfloat16, device=dev)
+    y_col = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+    a_row = y_col if wl.N == wl.K_row else up(wl.a_row())
+    own = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
+    y_norm = torch.empty_like(h)
+    y_dtp = torch.empty_like(h)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    ctx = sptl.Context(0)
+    cs = torch.cuda.current_stream()
+    delta = wl.delta if wl.delta is not None else 1
+    dtp_peers = peers[:wl.tp - 1]
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(rec=None):
+        if rec:
+            rec[0].record(cs)
+        sptl.agmm_chunked(shards, xg, w_col, y_col, n_chunks=wl.n_chunks, rank=0, compute=cs,
+                          timing=True, ctx=ctx)
+        if rec:
+            rec[1].record(cs)
+        sptl.gemm_partial(a_row, w_row, own, stream=cs, ctx=ctx)
+        if rec:
+            rec[2].record(cs)
+        sptl.reduce_residual_rmsnorm([own] + peers, residual, gamma, wl.eps, y_norm, residual_out=h,
+                                     stream=cs, ctx=ctx)
+        if rec:
+            rec[3].record(cs)
+        sptl.dtp_accumulate(x_res, own, dtp_peers, gamma, wl.eps, y_dtp, tp=wl.tp, delta=delta,
+                            module_idx=delta, stream=cs, ctx=ctx)
+        if rec:
+            rec[4].record(cs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    recs = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    timelines = []
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record(cs)
+    for i in range(args.steps):
+        step(recs[i])
+        # read the chunk timeline of this step's agmm call (blocks on its events; the host
+        # then runs ahead again while the rest of the step executes)
+        timelines.append(ctx.timeline(wl.n_chunks))
+    t_end.record(cs)
+    torch.cuda.synchronize()
+
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    agmm_ms = np.array([r[0].elapsed_time(r[1]) for r in recs])
+    gemmp_ms = np.array([r[1].elapsed_time(r[2]) for r in recs])
+    red_ms = np.array([r[2].elapsed_time(r[3]) for r in recs])
+    dtp_ms = np.array([r[3].elapsed_time(r[4]) for r in recs])
+
+    M, K, N = wl.M, wl.K, wl.N
+    agmm_flops = 2.0 * M * K * N
+    agmm_tflops = agmm_flops / (agmm_ms.mean() * 1e-3) / 1e12
+
+    # chunk GEMM launches: per-launch durations from the library's events
+    chunk_ms, hidden, copy_total, copy_rates = [], 0.0, 0.0, []
+    chunk_bytes = (M // wl.n_chunks) * K * 2
+    for tl in timelines:
+        gemm_iv = [(g0, g1) for (_, _, g0, g1) in tl]
+        chunk_ms.extend(g1 - g0 for (g0, g1) in gemm_iv)
+        for (c0, c1, _, _) in tl:
+            if c0 < 0 or c1 <= c0:
+                continue
+            copy_total += c1 - c0
+            hidden += union_overlap((c0, c1), gemm_iv)
+            copy_rates.append(chunk_bytes / ((c1 - c0) * 1e-3) / 1e9)
+    chunk_ms = np.array(chunk_ms)
+    chunk_flops = 2.0 * (M // wl.n_chunks) * K * N
+    gemm_achieved = chunk_flops / (chunk_ms.mean() * 1e-3) / 1e12
+    hidden_frac = hidden / copy_total if copy_total > 0 else None
+
+    P = wl.P
+    red_bytes = (P + 1) * M * wl.H * 2 + 2 * M * wl.H * 2 + wl.H * 2
+    dtp_bytes = (1 + 1 + (wl.tp - 1)) * M * wl.H * 2 + 2 * M * wl.H * 2 + wl.H * 2
+    red_gbs = red_bytes / (red_ms.mean() * 1e-3) / 1e9
+    dtp_gbs = dtp_bytes / (dtp_ms.mean() * 1e-3) / 1e9
+    gemmp_flops = 2.0 * M * wl.K_row * wl.H
+    gemmp_tflops = gemmp_flops / (gemmp_ms.mean() * 1e-3) / 1e12
+
+    out = {
+        "metric": "AG-GEMM TFLOP/s & %MFMA peak; reduce+RMSNorm GB/s & %HBM; % copy hidden",
+        "value": round(agmm_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal bf16 inputs, random-init weights)",
+        "config": {
+            "workload": wl.name,
+            "seq_len": M, "hidden": K, "n_local": N, "k_row": wl.K_row, "tp": wl.tp,
+            "n_chunks": wl.n_chunks, "rank": 0, "partials": P, "dtp_delta": delta,
+            "parallelism": "one GPU's share of SP-TP (peer chunks staged from local HBM)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_bf16_kernel (one chunk GEMM of agmm_chunked)",
+            "achieved": round(gemm_achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "launch_flop": chunk_flops,
+            "avg_launch_us": round(chunk_ms.mean() * 1e3, 2),
+        },
+        "agmm": {
+            "tflops": round(agmm_tflops, 2), "frac_peak": round(agmm_tflops / PEAK_BF16_TFLOPS, 4),
+            "ms": round(float(agmm_ms.mean()), 4),
+            "copy_hidden_frac": None if hidden_frac is None else round(hidden_frac, 4),
+            "copy_ms_per_call": round(copy_total / len(timelines), 4),
+            "copy_GBps_per_chunk": round(float(np.mean(copy_rates)), 1) if copy_rates else None,
+        },
+        "gemm_partial": {"tflops": round(gemmp_tflops, 2), "frac_peak": round(gemmp_tflops / PEAK_BF16_TFLOPS, 4),
+                         "ms": round(float(gemmp_ms.mean()), 4)},
+        "reduce_residual_rmsnorm": {"GBps": round(red_gbs, 1), "frac_hbm": round(red_gbs / PEAK_HBM_GBS, 4),
+                                    "ms": round(float(red_ms.mean()), 4), "bytes": red_bytes},
+        "dtp_accumulate": {"GBps": round(dtp_gbs, 1), "frac_hbm": round(dtp_gbs / PEAK_HBM_GBS, 4),
+                           "ms": round(float(dtp_ms.mean()), 4), "bytes": dtp_bytes},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+        "input_gen_s": round(t_gen, 2),
+    }
+    if args.cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

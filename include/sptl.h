@@ -1,0 +1,193 @@
+/*
+ * sptl.h - C ABI of libsptl.so: one GPU's share of the sequence-parallel tensor-parallel
+ * (SP-TP) linear layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources are web pages; each call below names the passage it implements):
+ *   [AReaL] "[Feature] Async Tensor Parallelism for Archon Engine" (AReaL issue),
+ *           sections "TP Communication Is on Activations, Not Weights" and
+ *           "Potential Solution".
+ *   [DTP]   "Affinity-Aware Sharding for Delayed Tensor Parallelism" (arXiv abstract).
+ *   [MLM]   "Add forward all-gather overlap" (Megatron-LM pull request #5513),
+ *           sections "Summary", "Notes from the review meeting", "Observations" and
+ *           "Recommendations".
+ *
+ * Conventions for every call
+ *   - Tensors are row-major with the last dimension contiguous and no padding.  bf16 is
+ *     IEEE bfloat16 (upper half of a binary32); results are rounded to nearest-even.
+ *   - Every tensor pointer is a DEVICE pointer on the context's device and must be 16-byte
+ *     aligned.  Pointer arrays (shard_src, partials, delayed_peers) are HOST arrays of
+ *     device pointers; the library reads them during the call only.
+ *   - Streams are hipStream_t values passed as void*; NULL means the null stream.
+ *   - Ownership: the caller owns every buffer and stream.  The library never allocates,
+ *     frees or retains caller memory.  A context owns only HIP events and, lazily, one
+ *     copy stream.  Inputs must stay valid until the stream work of the call completes.
+ *   - Every call is asynchronous (stream-ordered) and returns an sptl_status.  All
+ *     arguments are validated BEFORE anything is enqueued: on any non-OK status nothing
+ *     was enqueued and sptl_last_error() holds a message.  HIP failures after validation
+ *     return SPTL_E_HIP with the HIP error text.  No call aborts or throws.
+ *   - ctx may be NULL: the call then uses a per-device default context for the current
+ *     device, created on first use.  Argument validation happens before that, so a call
+ *     with invalid arguments makes no HIP call at all.
+ *   - Sizes are element counts.  Empty work (seq_len == 0) is valid and enqueues nothing.
+ */
+#ifndef SPTL_H
+#define SPTL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sptl_ctx sptl_ctx;
+
+typedef enum { SPTL_BF16 = 0, SPTL_F32 = 1 } sptl_dtype;
+
+typedef enum {
+    SPTL_OK = 0,
+    SPTL_E_NULL = 1,         /* a required pointer is NULL                                */
+    SPTL_E_SHAPE = 2,        /* a size is negative, zero where it must be positive, or
+                                exceeds a documented limit                               */
+    SPTL_E_DIVISIBILITY = 3, /* seq_len % n_chunks, n_chunks % tp, or a size not a
+                                multiple of 8 (16-byte rows)                             */
+    SPTL_E_ALIGN = 4,        /* a device pointer is not 16-byte aligned                   */
+    SPTL_E_DTYPE = 5,        /* dtype not in sptl_dtype                                   */
+    SPTL_E_RANGE = 6,        /* rank, tp, delta or module index out of range, or a pointer
+                                given/omitted against the delayed-TP schedule            */
+    SPTL_E_HIP = 7,          /* a HIP runtime call failed                                 */
+    SPTL_E_UNSUPPORTED = 8   /* valid request this build does not handle                  */
+} sptl_status;
+
+/* Limits. */
+#define SPTL_MAX_PARTIALS 16   /* partial sums per reduce call (tp)                      */
+#define SPTL_MAX_TP 64         /* TP degree of agmm_chunked and dtp_accumulate           */
+#define SPTL_MAX_CHUNKS 512    /* chunk count of agmm_chunked                            */
+
+/* Create a context on HIP device `device` (events are created now; the copy stream
+ * lazily).  *out receives the context.  Returns SPTL_E_NULL if out is NULL,
+ * SPTL_E_RANGE for a bad device, SPTL_E_HIP on runtime failure. */
+int sptl_create(sptl_ctx **out, int device);
+
+/* Destroy a context created by sptl_create: synchronises its copy stream, then releases
+ * its events and stream.  NULL is accepted and ignored. */
+int sptl_destroy(sptl_ctx *ctx);
+
+/* Text describing the last non-OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next sptl call on this thread. */
+const char *sptl_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int sptl_version(void);
+
+/*
+ * (1) Chunked sequence all-gather + column-parallel GEMM, this rank's share.
+ *
+ * [AReaL "Potential Solution", intra-layer overlap]: the all-gather + matmul is split into
+ * chunked, pipelined pieces, and each chunk's matmul starts as soon as the chunk has
+ * arrived.  [AReaL "TP Communication Is on Activations, Not Weights"]: the gather is over
+ * the sequence dimension of the activations.  [MLM "Observations", "Recommendations"]:
+ * the gather runs on its own stream and must not take compute units from the GEMM, so the
+ * staging copies go to the copy engines (SDMA) rather than to a copy kernel; [MLM "Notes
+ * from the review meeting"]: all copies are enqueued before the GEMMs.
+ *
+ *   seq_len  M: gathered sequence length (rows of x_gathered and y)
+ *   hidden   K: hidden size (columns of x_gathered, rows of w); multiple of 8
+ *   n_local  N: this rank's column-shard width (columns of w and y); multiple of 8
+ *   tp       TP degree, 1 <= tp <= SPTL_MAX_TP
+ *   n_chunks chunk count, n_chunks % tp == 0, seq_len % n_chunks == 0,
+ *            n_chunks <= SPTL_MAX_CHUNKS.  Rank q's shard is split into n_chunks/tp
+ *            contiguous sub-chunks of seq_len/n_chunks rows.
+ *   rank     this rank, 0 <= rank < tp
+ *   shard_src  host array [tp] of device pointers; shard_src[q] is rank q's sequence shard
+ *            [seq_len/tp, hidden] bf16.  shard_src[rank] may point at this rank's slot of
+ *            x_gathered (then it is not copied).  For q != rank it stands in for the
+ *            peer's buffer and is read by the copy engine only.
+ *   x_gathered [seq_len, hidden] bf16 output: rank-major concatenation of the shards.
+ *   w        [hidden, n_local] bf16 weight shard (logical [in, out]).
+ *   y, y_dtype  [seq_len, n_local] output, SPTL_BF16 or SPTL_F32; y = x_gathered @ w with
+ *            fp32 accumulation in a fixed order, so every chunking gives identical bits.
+ *   compute  stream that runs the GEMMs; the call is ordered after earlier work on it,
+ *            and later work on it sees x_gathered and y complete.
+ *   copy     stream for the staging copies; NULL = the context's own copy stream.
+ *   timing   0: no timing; 1: record per-chunk copy/GEMM timestamps, read afterwards with
+ *            sptl_agmm_timeline().
+ * Copies: chunks of ranks rank+1, ..., rank+tp-1 (mod tp) in that order, then this rank's
+ * own slot if shard_src[rank] does not alias it.  GEMMs: this rank's chunks first (read
+ * straight from shard_src[rank]), then each other chunk after its copy's event.
+ */
+int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
+                 int tp, int n_chunks, int rank,
+                 const void *const *shard_src, void *x_gathered, const void *w,
+                 void *y, int y_dtype, void *compute, void *copy, int timing);
+
+/* Per-chunk timeline of the last agmm_chunked call on ctx that had timing = 1.  Blocks
+ * until that call's work is done.  out (host) receives n_chunks rows of 4 doubles, in
+ * milliseconds from the call's fork point: copy start, copy end, GEMM start, GEMM end.
+ * Chunks with no copy have copy start = copy end = -1.  Returns SPTL_E_RANGE if n_chunks
+ * differs from the recorded call or no timed call was made. */
+int sptl_agmm_timeline(sptl_ctx *ctx, double *out, int n_chunks);
+
+/*
+ * (2) Row-parallel GEMM producing this rank's partial sum: partial = a @ w.
+ *
+ * [DTP abstract] ("partial output" of a tensor-parallel module); [AReaL "Potential
+ * Solution"] (the partial sums are reduce-scattered at the end of a sub-layer).
+ *   a        [seq_len, k_local] bf16;  k_local multiple of 8
+ *   w        [k_local, hidden]  bf16;  hidden multiple of 8
+ *   partial  [seq_len, hidden], out_dtype SPTL_BF16 (the layer's form) or SPTL_F32;
+ *            fp32 accumulation, same fixed order as agmm_chunked.
+ */
+int gemm_partial(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden,
+                 const void *a, const void *w, void *partial, int out_dtype, void *stream);
+
+/*
+ * (3) Fused reduce + residual + RMSNorm at a sub-layer boundary.
+ *
+ * [AReaL "Potential Solution", sub-layer boundary overlap]: between a sub-layer's
+ * reduce-scatter and the next all-gather sit the residual add and an RMSNorm that reduces
+ * over the hidden dimension.
+ *   h = residual + partials[0] + ... + partials[tp-1]    (fp32, added in this order)
+ *   y = h / sqrt(mean_j h_j^2 + eps) * gamma             (from the unrounded fp32 h)
+ *   tp        number of partials, 0 <= tp <= SPTL_MAX_PARTIALS (0: plain residual norm)
+ *   partials  host array [tp] of device pointers, each [seq_len, hidden] bf16
+ *   residual  [seq_len, hidden] bf16;  hidden multiple of 8
+ *   gamma     [hidden] bf16;  eps >= 0
+ *   residual_out [seq_len, hidden] bf16 receives h; may equal residual (in place);
+ *            NULL = do not write h
+ *   y         [seq_len, hidden] bf16
+ */
+int reduce_residual_rmsnorm(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int tp,
+                            const void *const *partials, const void *residual,
+                            const void *gamma, float eps, void *residual_out, void *y,
+                            void *stream);
+
+/*
+ * (4) Delayed tensor parallelism: residual update of module `module_idx`.
+ *
+ * [DTP abstract]: each device adds its own partial output to its residual stream at once
+ * and adds the other devices' partials delta modules later.
+ *   x <- x + own_partial + [module_idx >= delta] * (peers[0] + ... + peers[tp-2])
+ *   y  = x / sqrt(mean_j x_j^2 + eps) * gamma        (from the unrounded fp32 x)
+ * Summation order (fp32): x, own, then peers in the given order, so delta = 0 gives the
+ * same bits as reduce_residual_rmsnorm with partials [own, peers...].
+ *   residual      [seq_len, hidden] bf16, updated in place
+ *   own_partial   this rank's partial of module module_idx; NULL marks a flush call (after
+ *                 the last module: adds the outstanding peer partials, takes no norm)
+ *   delayed_peers host array [tp-1] of device pointers: the peers' partials of module
+ *                 module_idx - delta.  Must be NULL when module_idx < delta and non-NULL
+ *                 (with non-NULL entries) otherwise.  The caller owns the delay line.
+ *   gamma, eps    RMSNorm gain [hidden] bf16 and epsilon; gamma may be NULL when y is NULL
+ *   y             [seq_len, hidden] bf16 normalised output; required unless a flush call,
+ *                 where it must be NULL.
+ *   tp in [1, SPTL_MAX_PARTIALS], delta >= 0, module_idx >= 0.
+ */
+int dtp_accumulate(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int tp, int delta,
+                   int module_idx, void *residual, const void *own_partial,
+                   const void *const *delayed_peers, const void *gamma, float eps,
+                   void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPTL_H */

@@ -1,0 +1,456 @@
+// C ABI of libsptl.so: argument validation, contexts, and the copy/compute scheduler of the
+// chunked all-gather + column-parallel GEMM.  The declarations, with argument meaning,
+// layout, ownership and error behaviour, are in include/sptl.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "sptl.h"
+#include "sptl_internal.h"
+
+struct sptl_ctx {
+    int device = 0;
+    hipStream_t copy_stream = nullptr;  // created on first use
+    hipEvent_t fork = nullptr;          // compute stream -> copy stream
+    hipEvent_t join = nullptr;          // copy stream -> compute stream
+    std::vector<hipEvent_t> ready;      // per chunk: its staging copy has landed
+    // timeline of the last timed agmm_chunked call
+    hipEvent_t t_base = nullptr;
+    std::vector<hipEvent_t> t_copy_start, t_gemm_start, t_gemm_end;
+    std::vector<char> t_has_copy;
+    int t_chunks = -1;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(SPTL_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define SPTL_HIP(call)                                  \
+    do {                                                \
+        hipError_t e_ = (call);                         \
+        if (e_ != hipSuccess) return hip_fail(e_, #call); \
+    } while (0)
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Switches to the context's device for the duration of a call.
+struct DeviceGuard {
+    int prev = -1;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+        else if (err == hipSuccess) prev = -1;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+int make_event(hipEvent_t *e) {
+    SPTL_HIP(hipEventCreate(e));
+    return SPTL_OK;
+}
+
+int grow_events(std::vector<hipEvent_t> &v, size_t n) {
+    while (v.size() < n) {
+        hipEvent_t e;
+        int rc = make_event(&e);
+        if (rc) return rc;
+        v.push_back(e);
+    }
+    return SPTL_OK;
+}
+
+int create_ctx(sptl_ctx **out, int device) {
+    int count = 0;
+    SPTL_HIP(hipGetDeviceCount(&count));
+    if (device < 0 || device >= count)
+        return fail(SPTL_E_RANGE, "device %d out of range [0, %d)", device, count);
+    DeviceGuard g(device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    auto *c = new (std::nothrow) sptl_ctx;
+    if (!c) return fail(SPTL_E_HIP, "out of host memory");
+    c->device = device;
+    int rc = SPTL_OK;
+    if (!rc) rc = make_event(&c->fork);
+    if (!rc) rc = make_event(&c->join);
+    if (!rc) rc = make_event(&c->t_base);
+    if (!rc) rc = grow_events(c->ready, 64);
+    if (rc) {
+        sptl_destroy(c);
+        return rc;
+    }
+    *out = c;
+    return SPTL_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_default_mu;
+sptl_ctx *g_default[kMaxDevices] = {};
+
+// Resolves a NULL ctx to the current device's default context.
+int resolve_ctx(sptl_ctx *&ctx) {
+    if (ctx) return SPTL_OK;
+    int dev = 0;
+    SPTL_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SPTL_E_RANGE, "device %d unsupported", dev);
+    std::lock_guard<std::mutex> lk(g_default_mu);
+    if (!g_default[dev]) {
+        int rc = create_ctx(&g_default[dev], dev);
+        if (rc) return rc;
+    }
+    ctx = g_default[dev];
+    return SPTL_OK;
+}
+
+int copy_stream_of(sptl_ctx *ctx, hipStream_t *out) {
+    if (!ctx->copy_stream) SPTL_HIP(hipStreamCreateWithFlags(&ctx->copy_stream, hipStreamNonBlocking));
+    *out = ctx->copy_stream;
+    return SPTL_OK;
+}
+
+int check_gemm_dims(int64_t m, int64_t k, int64_t n) {
+    if (m < 0 || k <= 0 || n <= 0)
+        return fail(SPTL_E_SHAPE, "bad GEMM sizes m=%lld k=%lld n=%lld", (long long)m, (long long)k,
+                    (long long)n);
+    if (k % 8 || n % 8)
+        return fail(SPTL_E_DIVISIBILITY, "k=%lld and n=%lld must be multiples of 8", (long long)k,
+                    (long long)n);
+    // grid of 128 x 128 tiles must fit a 32-bit dimension
+    if (((m + 127) / 128) * ((n + 127) / 128) > 0x7fffffffLL)
+        return fail(SPTL_E_SHAPE, "GEMM too large for one launch");
+    return SPTL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sptl_version(void) { return 100; }
+
+const char *sptl_last_error(void) { return g_err.c_str(); }
+
+int sptl_create(sptl_ctx **out, int device) {
+    if (!out) return fail(SPTL_E_NULL, "out is NULL");
+    *out = nullptr;
+    return create_ctx(out, device);
+}
+
+int sptl_destroy(sptl_ctx *ctx) {
+    if (!ctx) return SPTL_OK;
+    DeviceGuard g(ctx->device);
+    if (ctx->copy_stream) {
+        (void)hipStreamSynchronize(ctx->copy_stream);
+        (void)hipStreamDestroy(ctx->copy_stream);
+    }
+    for (hipEvent_t e : {ctx->fork, ctx->join, ctx->t_base})
+        if (e) (void)hipEventDestroy(e);
+    for (auto *v : {&ctx->ready, &ctx->t_copy_start, &ctx->t_gemm_start, &ctx->t_gemm_end})
+        for (hipEvent_t e : *v) (void)hipEventDestroy(e);
+    for (int d = 0; d < kMaxDevices; ++d)
+        if (g_default[d] == ctx) g_default[d] = nullptr;
+    delete ctx;
+    return SPTL_OK;
+}
+
+int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local, int tp,
+                 int n_chunks, int rank, const void *const *shard_src, void *x_gathered,
+                 const void *w, void *y, int y_dtype, void *compute, void *copy, int timing) {
+    // ---- validation: nothing is enqueued on failure ------------------------------------
+    if (!shard_src || !x_gathered || !w || !y) return fail(SPTL_E_NULL, "agmm_chunked: NULL pointer argument");
+    if (seq_len < 0 || hidden <= 0 || n_local <= 0)
+        return fail(SPTL_E_SHAPE, "agmm_chunked: bad sizes seq_len=%lld hidden=%lld n_local=%lld",
+                    (long long)seq_len, (long long)hidden, (long long)n_local);
+    if (tp < 1 || tp > SPTL_MAX_TP) return fail(SPTL_E_RANGE, "agmm_chunked: tp=%d not in [1, %d]", tp, SPTL_MAX_TP);
+    if (n_chunks < 1 || n_chunks > SPTL_MAX_CHUNKS)
+        return fail(SPTL_E_RANGE, "agmm_chunked: n_chunks=%d not in [1, %d]", n_chunks, SPTL_MAX_CHUNKS);
+    if (rank < 0 || rank >= tp) return fail(SPTL_E_RANGE, "agmm_chunked: rank=%d not in [0, %d)", rank, tp);
+    if (n_chunks % tp) return fail(SPTL_E_DIVISIBILITY, "agmm_chunked: n_chunks=%d not a multiple of tp=%d", n_chunks, tp);
+    if (seq_len % n_chunks)
+        return fail(SPTL_E_DIVISIBILITY, "agmm_chunked: seq_len=%lld not a multiple of n_chunks=%d",
+                    (long long)seq_len, n_chunks);
+    if (y_dtype != SPTL_BF16 && y_dtype != SPTL_F32) return fail(SPTL_E_DTYPE, "agmm_chunked: y_dtype=%d", y_dtype);
+    if (timing != 0 && timing != 1) return fail(SPTL_E_RANGE, "agmm_chunked: timing=%d", timing);
+    if (int rc = check_gemm_dims(seq_len / n_chunks, hidden, n_local)) return rc;
+    for (int q = 0; q < tp; ++q) {
+        if (!shard_src[q]) return fail(SPTL_E_NULL, "agmm_chunked: shard_src[%d] is NULL", q);
+        if (!aligned16(shard_src[q])) return fail(SPTL_E_ALIGN, "agmm_chunked: shard_src[%d] not 16-byte aligned", q);
+    }
+    if (!aligned16(x_gathered) || !aligned16(w) || !aligned16(y))
+        return fail(SPTL_E_ALIGN, "agmm_chunked: x_gathered, w and y must be 16-byte aligned");
+    if (seq_len == 0) return SPTL_OK;
+    if (int rc = resolve_ctx(ctx)) return rc;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+
+    hipStream_t cs = static_cast<hipStream_t>(compute);
+    hipStream_t ps = static_cast<hipStream_t>(copy);
+    if (!ps)
+        if (int rc = copy_stream_of(ctx, &ps)) return rc;
+    if (int rc = grow_events(ctx->ready, n_chunks)) return rc;
+    if (timing) {
+        for (auto *v : {&ctx->t_copy_start, &ctx->t_gemm_start, &ctx->t_gemm_end})
+            if (int rc = grow_events(*v, n_chunks)) return rc;
+        ctx->t_has_copy.assign(n_chunks, 0);
+        ctx->t_chunks = -1;
+    }
+
+    const int cpr = n_chunks / tp;                    // chunks per rank
+    const int64_t rows_c = seq_len / n_chunks;        // rows per chunk
+    const size_t chunk_elems = (size_t)rows_c * (size_t)hidden;
+    const size_t chunk_bytes = chunk_elems * 2;
+    auto *xg = static_cast<uint16_t *>(x_gathered);
+    auto src_chunk = [&](int q, int s) {
+        return static_cast<const uint16_t *>(shard_src[q]) + (size_t)s * chunk_elems;
+    };
+    const bool own_aliased = shard_src[rank] == xg + (size_t)rank * cpr * chunk_elems;
+
+    // ---- fork: copies start only after earlier work on the compute stream -------------
+    if (timing) SPTL_HIP(hipEventRecord(ctx->t_base, cs));
+    SPTL_HIP(hipEventRecord(ctx->fork, cs));
+    SPTL_HIP(hipStreamWaitEvent(ps, ctx->fork, 0));
+
+    // ---- copy stream: every staging copy is enqueued before any GEMM ------------------
+    // Peers in ring order rank+1, rank+2, ... so the order matches arrival in a real ring.
+    // hipMemcpyDeviceToDeviceNoCU keeps the copies on the SDMA engines (a plain
+    // device-to-device copy would run as a copy kernel on the compute units).
+    for (int d = 1; d < tp; ++d) {
+        const int q = (rank + d) % tp;
+        for (int s = 0; s < cpr; ++s) {
+            const int c = q * cpr + s;
+            if (timing) {
+                SPTL_HIP(hipEventRecord(ctx->t_copy_start[c], ps));
+                ctx->t_has_copy[c] = 1;
+            }
+            SPTL_HIP(hipMemcpyAsync(xg + (size_t)c * chunk_elems, src_chunk(q, s), chunk_bytes,
+                                    hipMemcpyDeviceToDeviceNoCU, ps));
+            SPTL_HIP(hipEventRecord(ctx->ready[c], ps));
+        }
+    }
+    if (!own_aliased) {
+        // this rank's own slot; its GEMMs read the source directly and do not wait for it
+        const int c0 = rank * cpr;
+        if (timing) {
+            SPTL_HIP(hipEventRecord(ctx->t_copy_start[c0], ps));
+            for (int s = 0; s < cpr; ++s) ctx->t_has_copy[c0 + s] = 1;
+        }
+        SPTL_HIP(hipMemcpyAsync(xg + (size_t)c0 * chunk_elems, shard_src[rank], chunk_bytes * cpr,
+                                hipMemcpyDeviceToDeviceNoCU, ps));
+        SPTL_HIP(hipEventRecord(ctx->ready[c0], ps));
+        for (int s = 1; s < cpr; ++s) {
+            if (timing) SPTL_HIP(hipEventRecord(ctx->t_copy_start[c0 + s], ps));
+            SPTL_HIP(hipEventRecord(ctx->ready[c0 + s], ps));
+        }
+    }
+    SPTL_HIP(hipEventRecord(ctx->join, ps));
+
+    // ---- compute stream: own chunks first, then each chunk once its copy has landed ----
+    sptl::GemmProblem gp{};
+    gp.b = static_cast<const uint16_t *>(w);
+    gp.m = rows_c;
+    gp.n = n_local;
+    gp.k = hidden;
+    gp.lda = hidden;
+    gp.ldb = n_local;
+    gp.ldc = n_local;
+    gp.c_f32 = y_dtype == SPTL_F32;
+    const size_t esz = gp.c_f32 ? 4 : 2;
+    auto run_chunk = [&](int c, const uint16_t *a) -> int {
+        gp.a = a;
+        gp.c = static_cast<char *>(y) + (size_t)c * (size_t)rows_c * (size_t)n_local * esz;
+        if (timing) SPTL_HIP(hipEventRecord(ctx->t_gemm_start[c], cs));
+        SPTL_HIP(sptl::launch_gemm(gp, cs));
+        if (timing) SPTL_HIP(hipEventRecord(ctx->t_gemm_end[c], cs));
+        return SPTL_OK;
+    };
+    for (int s = 0; s < cpr; ++s)
+        if (int rc = run_chunk(rank * cpr + s, src_chunk(rank, s))) return rc;
+    for (int d = 1; d < tp; ++d) {
+        const int q = (rank + d) % tp;
+        for (int s = 0; s < cpr; ++s) {
+            const int c = q * cpr + s;
+            SPTL_HIP(hipStreamWaitEvent(cs, ctx->ready[c], 0));
+            if (int rc = run_chunk(c, xg + (size_t)c * chunk_elems)) return rc;
+        }
+    }
+    // ---- join: later work on the compute stream sees x_gathered complete ---------------
+    SPTL_HIP(hipStreamWaitEvent(cs, ctx->join, 0));
+    if (timing) ctx->t_chunks = n_chunks;
+    return SPTL_OK;
+}
+
+int sptl_agmm_timeline(sptl_ctx *ctx, double *out, int n_chunks) {
+    if (!out) return fail(SPTL_E_NULL, "sptl_agmm_timeline: out is NULL");
+    if (int rc = resolve_ctx(ctx)) return rc;
+    if (ctx->t_chunks < 0 || n_chunks != ctx->t_chunks)
+        return fail(SPTL_E_RANGE, "sptl_agmm_timeline: no timed call with n_chunks=%d", n_chunks);
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    SPTL_HIP(hipEventSynchronize(ctx->join));
+    for (int c = 0; c < n_chunks; ++c) {
+        float t = 0.0f;
+        double *row = out + 4 * c;
+        if (ctx->t_has_copy[c]) {
+            SPTL_HIP(hipEventSynchronize(ctx->ready[c]));
+            SPTL_HIP(hipEventElapsedTime(&t, ctx->t_base, ctx->t_copy_start[c]));
+            row[0] = t;
+            SPTL_HIP(hipEventElapsedTime(&t, ctx->t_base, ctx->ready[c]));
+            row[1] = t;
+        } else {
+            row[0] = row[1] = -1.0;
+        }
+        SPTL_HIP(hipEventSynchronize(ctx->t_gemm_end[c]));
+        SPTL_HIP(hipEventElapsedTime(&t, ctx->t_base, ctx->t_gemm_start[c]));
+        row[2] = t;
+        SPTL_HIP(hipEventElapsedTime(&t, ctx->t_base, ctx->t_gemm_end[c]));
+        row[3] = t;
+    }
+    return SPTL_OK;
+}
+
+int gemm_partial(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden, const void *a,
+                 const void *w, void *partial, int out_dtype, void *stream) {
+    if (!a || !w || !partial) return fail(SPTL_E_NULL, "gemm_partial: NULL pointer argument");
+    if (out_dtype != SPTL_BF16 && out_dtype != SPTL_F32) return fail(SPTL_E_DTYPE, "gemm_partial: out_dtype=%d", out_dtype);
+    if (int rc = check_gemm_dims(seq_len, k_local, hidden)) return rc;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(partial))
+        return fail(SPTL_E_ALIGN, "gemm_partial: pointers must be 16-byte aligned");
+    if (seq_len == 0) return SPTL_OK;
+    if (int rc = resolve_ctx(ctx)) return rc;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    sptl::GemmProblem gp{};
+    gp.a = static_cast<const uint16_t *>(a);
+    gp.b = static_cast<const uint16_t *>(w);
+    gp.c = partial;
+    gp.m = seq_len;
+    gp.n = hidden;
+    gp.k = k_local;
+    gp.lda = k_local;
+    gp.ldb = hidden;
+    gp.ldc = hidden;
+    gp.c_f32 = out_dtype == SPTL_F32;
+    SPTL_HIP(sptl::launch_gemm(gp, static_cast<hipStream_t>(stream)));
+    return SPTL_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_epilogue_common(const char *fn, int64_t seq_len, int64_t hidden, float eps) {
+    if (seq_len < 0 || hidden <= 0)
+        return fail(SPTL_E_SHAPE, "%s: bad sizes seq_len=%lld hidden=%lld", fn, (long long)seq_len,
+                    (long long)hidden);
+    if (hidden % 8) return fail(SPTL_E_DIVISIBILITY, "%s: hidden=%lld not a multiple of 8", fn, (long long)hidden);
+    if (seq_len > 0x7fffffffLL) return fail(SPTL_E_SHAPE, "%s: seq_len too large", fn);
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(SPTL_E_RANGE, "%s: eps must be finite and >= 0", fn);
+    return SPTL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int reduce_residual_rmsnorm(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int tp,
+                            const void *const *partials, const void *residual, const void *gamma,
+                            float eps, void *residual_out, void *y, void *stream) {
+    if (!residual || !gamma || !y) return fail(SPTL_E_NULL, "reduce_residual_rmsnorm: NULL pointer argument");
+    if (tp < 0 || tp > SPTL_MAX_PARTIALS)
+        return fail(SPTL_E_RANGE, "reduce_residual_rmsnorm: tp=%d not in [0, %d]", tp, SPTL_MAX_PARTIALS);
+    if (tp > 0 && !partials) return fail(SPTL_E_NULL, "reduce_residual_rmsnorm: partials is NULL");
+    if (int rc = check_epilogue_common("reduce_residual_rmsnorm", seq_len, hidden, eps)) return rc;
+    sptl::EpilogueProblem ep{};
+    ep.in[0] = static_cast<const uint16_t *>(residual);
+    for (int p = 0; p < tp; ++p) {
+        if (!partials[p]) return fail(SPTL_E_NULL, "reduce_residual_rmsnorm: partials[%d] is NULL", p);
+        ep.in[1 + p] = static_cast<const uint16_t *>(partials[p]);
+    }
+    ep.n_in = 1 + tp;
+    for (int i = 0; i < ep.n_in; ++i)
+        if (!aligned16(ep.in[i])) return fail(SPTL_E_ALIGN, "reduce_residual_rmsnorm: input %d not 16-byte aligned", i);
+    if (!aligned16(gamma) || !aligned16(y) || !aligned16(residual_out))
+        return fail(SPTL_E_ALIGN, "reduce_residual_rmsnorm: gamma, y, residual_out must be 16-byte aligned");
+    if (seq_len == 0) return SPTL_OK;
+    if (int rc = resolve_ctx(ctx)) return rc;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    ep.gamma = static_cast<const uint16_t *>(gamma);
+    ep.h_out = static_cast<uint16_t *>(residual_out);
+    ep.y_out = static_cast<uint16_t *>(y);
+    ep.rows = seq_len;
+    ep.hidden = hidden;
+    ep.eps = eps;
+    SPTL_HIP(sptl::launch_epilogue(ep, static_cast<hipStream_t>(stream)));
+    return SPTL_OK;
+}
+
+int dtp_accumulate(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int tp, int delta, int module_idx,
+                   void *residual, const void *own_partial, const void *const *delayed_peers,
+                   const void *gamma, float eps, void *y, void *stream) {
+    if (!residual) return fail(SPTL_E_NULL, "dtp_accumulate: residual is NULL");
+    if (tp < 1 || tp > SPTL_MAX_PARTIALS)
+        return fail(SPTL_E_RANGE, "dtp_accumulate: tp=%d not in [1, %d]", tp, SPTL_MAX_PARTIALS);
+    if (delta < 0) return fail(SPTL_E_RANGE, "dtp_accumulate: delta=%d < 0", delta);
+    if (module_idx < 0) return fail(SPTL_E_RANGE, "dtp_accumulate: module_idx=%d < 0", module_idx);
+    const bool flush = own_partial == nullptr;
+    const bool peers_due = module_idx >= delta && tp > 1;
+    if (module_idx < delta && delayed_peers)
+        return fail(SPTL_E_RANGE, "dtp_accumulate: module %d < delta %d has no delayed peers; pass NULL",
+                    module_idx, delta);
+    if (peers_due && !delayed_peers)
+        return fail(SPTL_E_NULL, "dtp_accumulate: module %d needs the peers' partials of module %d",
+                    module_idx, module_idx - delta);
+    if (flush && !peers_due)
+        return fail(SPTL_E_RANGE, "dtp_accumulate: flush call (own_partial NULL) with nothing to add");
+    if (flush && y) return fail(SPTL_E_RANGE, "dtp_accumulate: flush calls take no norm; y must be NULL");
+    if (!flush && !y) return fail(SPTL_E_NULL, "dtp_accumulate: y is NULL");
+    if (y && !gamma) return fail(SPTL_E_NULL, "dtp_accumulate: gamma is NULL");
+    if (int rc = check_epilogue_common("dtp_accumulate", seq_len, hidden, eps)) return rc;
+    sptl::EpilogueProblem ep{};
+    ep.in[0] = static_cast<const uint16_t *>(residual);
+    ep.n_in = 1;
+    if (!flush) ep.in[ep.n_in++] = static_cast<const uint16_t *>(own_partial);
+    if (peers_due)
+        for (int q = 0; q < tp - 1; ++q) {
+            if (!delayed_peers[q]) return fail(SPTL_E_NULL, "dtp_accumulate: delayed_peers[%d] is NULL", q);
+            ep.in[ep.n_in++] = static_cast<const uint16_t *>(delayed_peers[q]);
+        }
+    for (int i = 0; i < ep.n_in; ++i)
+        if (!aligned16(ep.in[i])) return fail(SPTL_E_ALIGN, "dtp_accumulate: input %d not 16-byte aligned", i);
+    if (!aligned16(gamma) || !aligned16(y)) return fail(SPTL_E_ALIGN, "dtp_accumulate: gamma and y must be 16-byte aligned");
+    if (seq_len == 0) return SPTL_OK;
+    if (int rc = resolve_ctx(ctx)) return rc;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    ep.gamma = static_cast<const uint16_t *>(gamma);
+    ep.h_out = static_cast<uint16_t *>(residual);
+    ep.y_out = static_cast<uint16_t *>(y);
+    ep.rows = seq_len;
+    ep.hidden = hidden;
+    ep.eps = eps;
+    SPTL_HIP(sptl::launch_epilogue(ep, static_cast<hipStream_t>(stream)));
+    return SPTL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,337 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI.
+
+Inputs come from the seeded generator (sp_transformer_linear_amd.synth); the oracle sees
+the same bf16 bits.  Sizes here finish in seconds on the oracle and span several tiles with
+ragged tails; full workload sizes are in test_gpu_fullsize.py.
+
+Tolerances: fp32-accumulated outputs |err| <= 1e-3 * ||oracle row||_2 / sqrt(N) + 1e-5;
+bf16-stored outputs |err| <= 8e-3 * |oracle| + 1e-2; chunked vs monolithic GEMM, row splits of
+the epilogue, and delayed TP with delta = 0 vs the reduce are compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle.sptl_oracle as O
+from sp_transformer_linear_amd import synth
+from tests.util import assert_within, bf16_tol, fp32_tol, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sp_transformer_linear_amd import sptl
+    ctx = sptl.Context(0)
+    yield torch, sptl, ctx
+    torch.cuda.synchronize()
+    ctx.close()
+
+
+def dec(t):
+    return O.bf16_bits_to_f64(to_bits(t))
+
+
+def gen(seed, key, rows, cols, var=1.0):
+    return synth.normal_bf16(seed, key, rows, cols, float(np.sqrt(var)))
+
+
+# ------------------------------------------------------------------------------------------
+# chunked all-gather + column GEMM
+# ------------------------------------------------------------------------------------------
+
+AGMM_CASES = [
+    # tp, n_chunks, rows per rank, K, N, rank
+    (2, 2, 128, 256, 512, 0),      # the tiny tp=2 workload's shapes
+    (2, 4, 128, 256, 512, 1),      # two sub-chunks per rank, rank 1
+    (3, 6, 100, 200, 136, 2),      # ragged: rows, K and N off every tile size
+    (4, 4, 300, 320, 264, 0),      # several 128-row tiles plus tails
+    (1, 1, 520, 136, 520, 0),      # tp = 1: nothing to gather
+    (8, 8, 64, 128, 256, 3),       # many small chunks
+]
+
+
+@pytest.mark.parametrize("tp,n_chunks,rows,K,N,rank", AGMM_CASES)
+@pytest.mark.parametrize("y_f32", [True, False])
+def test_agmm_chunked_parity(env, tp, n_chunks, rows, K, N, rank, y_f32):
+    torch, sptl, ctx = env
+    seed = 100 + tp * 7 + rows
+    shards_b = [gen(seed, (0, q), rows, K) for q in range(tp)]
+    w_b = gen(seed, (1,), K, N, 1.0 / K)
+    M = tp * rows
+    shards = [to_dev(b) for b in shards_b]
+    w = to_dev(w_b)
+    xg = torch.full((M, K), float("nan"), dtype=torch.bfloat16, device="cuda")  # poisoned
+    y = torch.empty((M, N), dtype=torch.float32 if y_f32 else torch.bfloat16, device="cuda")
+    sptl.agmm_chunked(shards, xg, w, y, n_chunks=n_chunks, rank=rank, ctx=ctx)
+    torch.cuda.synchronize()
+    x_want, y_want = O.agmm(shards_b, w_b)
+    assert np.array_equal(to_bits(xg), np.concatenate(shards_b)), "x_gathered is not the rank-major concat"
+    if y_f32:
+        assert_within(y.cpu().numpy().astype(np.float64), y_want, fp32_tol(y_want), "y fp32")
+    else:
+        assert_within(dec(y), y_want, bf16_tol(y_want), "y bf16")
+
+
+@pytest.mark.parametrize("tp,n_chunks,rows,K,N,rank", AGMM_CASES[:4])
+def test_agmm_chunked_equals_monolithic_bitwise(env, tp, n_chunks, rows, K, N, rank):
+    """Chunking splits rows only; with one K order the GPU result bits must not change."""
+    torch, sptl, ctx = env
+    seed = 200 + rows
+    shards = [to_dev(gen(seed, (0, q), rows, K)) for q in range(tp)]
+    w = to_dev(gen(seed, (1,), K, N, 1.0 / K))
+    M = tp * rows
+    xg = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    for dt in (torch.float32, torch.bfloat16):
+        y_ch = torch.empty((M, N), dtype=dt, device="cuda")
+        sptl.agmm_chunked(shards, xg, w, y_ch, n_chunks=n_chunks, rank=rank, ctx=ctx)
+        y_mono = torch.empty((M, N), dtype=dt, device="cuda")
+        sptl.gemm_partial(xg, w, y_mono, ctx=ctx)
+        torch.cuda.synchronize()
+        assert torch.equal(y_ch.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                           y_mono.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+
+
+def test_agmm_own_slot_aliased(env):
+    """shard_src[rank] may point into x_gathered's own slot; it is then not copied."""
+    torch, sptl, ctx = env
+    tp, rows, K, N, rank = 4, 96, 128, 192, 2
+    seed = 31
+    shards_b = [gen(seed, (0, q), rows, K) for q in range(tp)]
+    w_b = gen(seed, (1,), K, N, 1.0 / K)
+    xg = torch.zeros((tp * rows, K), dtype=torch.bfloat16, device="cuda")
+    xg[rank * rows:(rank + 1) * rows] = to_dev(shards_b[rank])
+    shards = [to_dev(b) for b in shards_b]
+    shards[rank] = xg[rank * rows:(rank + 1) * rows]
+    y = torch.empty((tp * rows, N), dtype=torch.float32, device="cuda")
+    sptl.agmm_chunked(shards, xg, to_dev(w_b), y, n_chunks=tp, rank=rank, ctx=ctx)
+    torch.cuda.synchronize()
+    _, y_want = O.agmm(shards_b, w_b)
+    assert np.array_equal(to_bits(xg), np.concatenate(shards_b))
+    assert_within(y.cpu().numpy().astype(np.float64), y_want, fp32_tol(y_want), "y")
+
+
+def test_agmm_default_context_and_copy_stream(env):
+    """ctx NULL (per-device default) and a caller-supplied copy stream give the same bits."""
+    torch, sptl, ctx = env
+    tp, rows, K, N = 2, 128, 256, 256
+    shards = [to_dev(gen(5, (0, q), rows, K)) for q in range(tp)]
+    w = to_dev(gen(5, (1,), K, N, 1.0 / K))
+    xg = torch.empty((tp * rows, K), dtype=torch.bfloat16, device="cuda")
+    y1 = torch.empty((tp * rows, N), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y1)
+    sptl.agmm_chunked(shards, xg, w, y1, n_chunks=2, rank=0, ctx=None)
+    side = torch.cuda.Stream()
+    sptl.agmm_chunked(shards, xg, w, y2, n_chunks=2, rank=0, ctx=ctx, copy=side)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_agmm_timeline(env):
+    torch, sptl, ctx = env
+    tp, rows, K, N = 4, 256, 512, 512
+    shards = [to_dev(gen(6, (0, q), rows, K)) for q in range(tp)]
+    w = to_dev(gen(6, (1,), K, N, 1.0 / K))
+    xg = torch.empty((tp * rows, K), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((tp * rows, N), dtype=torch.bfloat16, device="cuda")
+    sptl.agmm_chunked(shards, xg, w, y, n_chunks=tp, rank=1, ctx=ctx, timing=True)
+    tl = ctx.timeline(tp)
+    for c in (0, 2, 3):  # peer chunks: each GEMM starts after its copy has landed
+        cs, ce, gs, ge = tl[c]
+        assert 0.0 <= cs <= ce <= ge
+        assert ce <= gs, "a chunk GEMM started before its copy landed"
+    for c in range(tp):
+        assert tl[c][2] <= tl[c][3]
+    # the own chunk's GEMM does not wait for the copy of the own slot
+    assert tl[1][2] <= tl[0][2]
+    # an aliased own slot has no copy at all
+    shards[1] = xg[rows:2 * rows]
+    sptl.agmm_chunked(shards, xg, w, y, n_chunks=tp, rank=1, ctx=ctx, timing=True)
+    tl = ctx.timeline(tp)
+    assert tl[1][0] == -1.0 and tl[1][1] == -1.0
+
+
+# ------------------------------------------------------------------------------------------
+# row-parallel partial GEMM
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,H", [(256, 512, 256), (300, 200, 136), (1, 8, 8), (777, 1032, 520),
+                                   (2048, 256, 2048)])
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_gemm_partial_parity(env, M, K, H, out_f32):
+    torch, sptl, ctx = env
+    a_b = gen(7 + M, (3,), M, K)
+    w_b = gen(7 + M, (2,), K, H, 1.0 / K)
+    out = torch.empty((M, H), dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
+    sptl.gemm_partial(to_dev(a_b), to_dev(w_b), out, ctx=ctx)
+    torch.cuda.synchronize()
+    want = O.gemm_partial(a_b, w_b)
+    if out_f32:
+        assert_within(out.cpu().numpy().astype(np.float64), want, fp32_tol(want), "partial fp32")
+    else:
+        assert_within(dec(out), want, bf16_tol(want), "partial bf16")
+
+
+def test_gemm_identity_and_permutation_exact(env):
+    """W = I or a permutation makes every output an exact copy of an input element."""
+    torch, sptl, ctx = env
+    M, K = 300, 264
+    a_b = gen(9, (3,), M, K)
+    a = to_dev(a_b)
+    eye = torch.eye(K, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    sptl.gemm_partial(a, eye, out, ctx=ctx)
+    perm = np.random.default_rng(0).permutation(K)
+    pw = torch.zeros((K, K), dtype=torch.bfloat16, device="cuda")
+    pw[torch.from_numpy(perm).cuda(), torch.arange(K, device="cuda")] = 1.0
+    out2 = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    sptl.gemm_partial(a, pw, out2, ctx=ctx)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), a_b)
+    assert np.array_equal(to_bits(out2), a_b[:, perm])
+
+
+# ------------------------------------------------------------------------------------------
+# reduce + residual + RMSNorm
+# ------------------------------------------------------------------------------------------
+
+def epi_inputs(seed, R, H, P):
+    parts = [gen(seed, (4, p), R, H, 0.02) for p in range(P)]
+    res = gen(seed, (5,), R, H)
+    gamma = synth.normal_bf16(seed, (6,), 1, H, 0.1, mean=1.0)[0]
+    return parts, res, gamma
+
+
+@pytest.mark.parametrize("R,H,P", [(256, 256, 2), (37, 4096, 8), (64, 3584, 4), (50, 1024, 4),
+                                   (9, 200, 3), (5, 8, 1), (3, 8200, 2), (7, 16392, 5), (12, 512, 16),
+                                   (4, 2048, 0), (33, 8192, 16)])
+@pytest.mark.parametrize("mode", ["separate", "inplace", "no_h"])
+def test_reduce_residual_rmsnorm_parity(env, R, H, P, mode):
+    torch, sptl, ctx = env
+    parts_b, res_b, g_b = epi_inputs(11 + R + H, R, H, P)
+    parts = [to_dev(b) for b in parts_b]
+    res = to_dev(res_b)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+    h_out = {"separate": torch.empty_like(res), "inplace": res, "no_h": None}[mode]
+    sptl.reduce_residual_rmsnorm(parts, res, to_dev(g_b), 1e-6, y, residual_out=h_out, ctx=ctx)
+    torch.cuda.synchronize()
+    h_want, y_want = O.reduce_residual_rmsnorm(parts_b, res_b, g_b, 1e-6)
+    assert_within(dec(y), y_want, bf16_tol(y_want), "y")
+    if h_out is not None:
+        assert_within(dec(h_out), h_want, bf16_tol(h_want), "h")
+    else:
+        assert np.array_equal(to_bits(res), res_b), "residual modified although residual_out is NULL"
+
+
+def test_reduce_row_split_bitwise(env):
+    """Rows are independent: any split of the rows gives the same bits (norm commutes with the gather)."""
+    torch, sptl, ctx = env
+    R, H, P = 96, 4096, 8
+    parts_b, res_b, g_b = epi_inputs(13, R, H, P)
+    parts = [to_dev(b) for b in parts_b]
+    res, g = to_dev(res_b), to_dev(g_b)
+    y_all = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+    h_all = torch.empty_like(y_all)
+    sptl.reduce_residual_rmsnorm(parts, res, g, 1e-6, y_all, residual_out=h_all, ctx=ctx)
+    y_sp = torch.empty_like(y_all)
+    h_sp = torch.empty_like(y_all)
+    for lo, hi in ((0, 17), (17, 64), (64, 96)):
+        sptl.reduce_residual_rmsnorm([p[lo:hi] for p in parts], res[lo:hi], g, 1e-6, y_sp[lo:hi],
+                                     residual_out=h_sp[lo:hi], ctx=ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(y_all.view(torch.int16), y_sp.view(torch.int16))
+    assert torch.equal(h_all.view(torch.int16), h_sp.view(torch.int16))
+
+
+def test_reduce_closed_forms(env):
+    """Constant rows give c / sqrt(c^2 + eps) * gamma; zero rows give 0."""
+    torch, sptl, ctx = env
+    H = 1024
+    g_b = synth.normal_bf16(3, (6,), 1, H, 0.1, mean=1.0)[0]
+    vals = [0.0, 1.0, -2.5, 0.125, 3.0]
+    res = torch.tensor(vals, dtype=torch.float32).repeat_interleave(H).view(len(vals), H)
+    res = res.to(torch.bfloat16).cuda()
+    y = torch.empty_like(res)
+    sptl.reduce_residual_rmsnorm([], res, to_dev(g_b), 1e-6, y, ctx=ctx)
+    torch.cuda.synchronize()
+    gv = O.bf16_bits_to_f64(g_b)
+    want = np.array([[c / np.sqrt(c * c + 1e-6) * g for g in gv] for c in vals])
+    assert_within(dec(y), want, bf16_tol(want), "constant rows")
+    assert np.all(dec(y)[0] == 0.0)
+
+
+# ------------------------------------------------------------------------------------------
+# delayed tensor parallelism
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H,tp", [(64, 1024, 4), (33, 4096, 8), (10, 264, 2)])
+def test_dtp_delta0_bitwise_equals_reduce(env, T, H, tp):
+    torch, sptl, ctx = env
+    seed = 17 + T
+    own_b = gen(seed, (7, 0), T, H, 0.02)
+    peers_b = [gen(seed, (8, 0, q), T, H, 0.02) for q in range(tp - 1)]
+    res_b = gen(seed, (5,), T, H)
+    g = to_dev(synth.normal_bf16(seed, (6,), 1, H, 0.1, mean=1.0)[0])
+    own, peers = to_dev(own_b), [to_dev(b) for b in peers_b]
+    x = to_dev(res_b)
+    y_dtp = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    sptl.dtp_accumulate(x, own, peers, g, 1e-6, y_dtp, tp=tp, delta=0, module_idx=0, ctx=ctx)
+    res2 = to_dev(res_b)
+    y_red = torch.empty_like(y_dtp)
+    h_red = torch.empty_like(y_dtp)
+    sptl.reduce_residual_rmsnorm([own] + peers, res2, g, 1e-6, y_red, residual_out=h_red, ctx=ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int16), h_red.view(torch.int16))
+    assert torch.equal(y_dtp.view(torch.int16), y_red.view(torch.int16))
+
+
+@pytest.mark.parametrize("delta,L,tp", [(1, 4, 4), (2, 3, 2), (0, 2, 3), (3, 2, 4)])
+def test_dtp_sequence_parity(env, delta, L, tp):
+    """Module by module against the oracle (bf16 residual stream), then the flush steps."""
+    torch, sptl, ctx = env
+    T, H = 96, 1024
+    seed = 23 + delta * 10 + L
+    x0_b = gen(seed, (5,), T, H)
+    owns_b = [gen(seed, (7, l), T, H, 0.02) for l in range(L)]
+    peers_b = [[gen(seed, (8, l, q), T, H, 0.02) for q in range(tp - 1)] for l in range(L)]
+    g_b = synth.normal_bf16(seed, (6,), 1, H, 0.1, mean=1.0)[0]
+    steps, x_final, x_imm = O.dtp_sequence(x0_b, owns_b, peers_b, delta, g_b, 1e-6, store_bf16=True)
+    x = to_dev(x0_b)
+    g = to_dev(g_b)
+    owns = [to_dev(b) for b in owns_b]
+    peers = [[to_dev(b) for b in ps] for ps in peers_b]
+    for l in range(L + delta):
+        own = owns[l] if l < L else None
+        late = peers[l - delta] if l >= delta else None
+        if own is None and late is None:  # a flush step with nothing outstanding (L < delta)
+            assert np.array_equal(steps[l][0], steps[l - 1][0])
+            continue
+        y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda") if l < L else None
+        sptl.dtp_accumulate(x, own, late, g if y is not None else None, 1e-6, y, tp=tp, delta=delta,
+                            module_idx=l, ctx=ctx)
+        torch.cuda.synchronize()
+        xs, ys = steps[l]
+        assert_within(dec(x), xs, bf16_tol(xs), f"x after step {l}")
+        if y is not None:
+            assert_within(dec(y), ys, bf16_tol(ys), f"y of module {l}")
+    # after the flush every partial has been added once: the immediate all-reduce result,
+    # up to the bf16 rounding of the stored residual at each of the L + delta steps (each
+    # step may contribute up to the bf16 bound of the value it stores)
+    tol = sum(8e-3 * np.abs(xs) for xs, _ in steps) + 1e-2
+    assert_within(dec(x), x_imm, tol, "delayed vs immediate")
+
+
+def test_validation_enqueues_nothing(env):
+    """An invalid call returns its status and leaves every buffer untouched."""
+    torch, sptl, ctx = env
+    R, H = 16, 256
+    res = torch.ones((R, H), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((R, H), 7.0, dtype=torch.bfloat16, device="cuda")
+    g = torch.ones((H,), dtype=torch.bfloat16, device="cuda")
+    rc = sptl.raw_reduce_residual_rmsnorm(ctx.handle, R, H, 2, [res.data_ptr(), None], res.data_ptr(),
+                                          g.data_ptr(), 1e-6, res.data_ptr(), y.data_ptr(), None)
+    assert rc == 1
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0) and torch.all(res == 1.0)
