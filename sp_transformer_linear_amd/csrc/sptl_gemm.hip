@@ -6,33 +6,54 @@
 // AReaL async-TP issue; "partial output" in the delayed-TP abstract).
 //
 // Design for gfx950:
-//   * 256 threads = 4 wave64s in a 2 x 2 grid over a BM x BN output tile; each wave owns a
-//     (BM/2) x (BN/2) block made of 32 x 32 blocks of v_mfma_f32_32x32x16_bf16.
-//   * K is walked in stages of 64.  Each stage of A ([BM][64]) and of B, stored transposed as
-//     [BN][64] so both MFMA operands read 8 consecutive k per lane, sits in LDS, double
-//     buffered (256 x 256 tile: 2 x 64 KB of the 160 KB LDS).  The next stage's global loads
-//     are issued before the current stage's MFMAs and written to the other buffer after them,
-//     so one barrier per stage suffices.
-//   * B arrives N-contiguous ([in, out] weight layout); each thread loads an 8 x 8 block
-//     (8 rows of 16 bytes) and transposes it in registers before its 16-byte LDS writes.
-//   * LDS rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r is stored at
-//     c ^ ((r ^ r >> 3) & 7), which keeps both the fragment reads (8 consecutive rows, same
-//     chunk) and the transposed B writes (rows 8 apart, same chunk) free of bank conflicts.
+//   * A workgroup owns a BM x BN output tile; its WGM x WGN wave64s each own a (BM/WGM) x
+//     (BN/WGN) block made of 32 x 32 blocks of v_mfma_f32_32x32x16_bf16.
+//   * K is walked in stages of 64.  A stage of A ([BM][64]) and B ([64][BN]) sits in LDS,
+//     double buffered.  Global loads are buffer loads (one scalar descriptor per operand,
+//     32-bit lane offsets, out-of-range offsets read as zero, which handles every ragged
+//     edge), staged in registers: the next stage's loads are issued at the top of a stage
+//     and written to the other LDS buffer at its end, so one barrier per stage suffices.
+//   * A is read as 8 consecutive k per lane (ds_read_b128).  B keeps the weight's [k][n]
+//     layout in LDS and is read with the gfx950 transposing LDS read, so no thread ever
+//     transposes data in registers.
+//   * The instruction order inside a stage is pinned: the stage's global loads, the first
+//     step's fragment reads, then each MFMA followed by one fragment read of the next step.
 //   * Workgroups are dispatched round-robin over the 8 XCDs; the tile order gives each XCD a
 //     contiguous run of tiles so that neighbouring tiles share that XCD's L2.
-//   * Every tile shape uses the same MFMA instruction and visits K in the same ascending
-//     order, with no split-K, so the result bits do not depend on tiling or chunking.
+//   * Every tile configuration uses the same MFMA instruction and visits K in the same
+//     ascending order, with no split-K, so the result bits do not depend on tiling or
+//     chunking.
+//
+// ds_read_b64_tr_b16, per group of 16 lanes: source lane r supplies the address of 4
+// consecutive bf16; result lane i element j is element (i % 4) of source lane 4 j + i / 4.
+// With source lane r pointing at B[kb + r / 4][nb + 4 (r % 4)], result lane i holds
+// B[kb + 0..3][nb + i]: four consecutive k of one column, half of an MFMA B operand.
+//
+// LDS layouts (bytes):
+//   A stage: BM rows of 128 bytes (64 k); 16-byte chunk c of row r is stored at
+//            c ^ ((r ^ r >> 3) & 7).
+//   B stage: 64 rows (k) of 2 BN bytes; 32-byte unit u (16 columns) of row k is stored at
+//            u ^ ((k & 3) << 1).  The LDS serves 32 lanes (256 bytes, all 64 banks) per
+//            cycle; a transposing read by lanes 0..31 touches rows kb..kb+3 at units u
+//            (lanes 0..15) and u + 1 (lanes 16..31), u even, which this map sends to 8
+//            distinct 32-byte bank groups.
+#include <cstdlib>
+#include <cstring>
+
 #include "sptl_internal.h"
 
 namespace sptl {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
-constexpr int kBK = 64;        // K depth of one LDS stage
-constexpr int kThreads = 256;  // 4 waves in a 2 x 2 grid
+constexpr int kBK = 64;                   // K depth of one LDS stage
+constexpr int kRsrcFlags = 0x00020000;    // raw buffer, 32-bit data format
+constexpr int kOutOfRange = 0x7ffffff0;   // an offset past any num_records used here
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -43,30 +64,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-template <int BM, int BN>
-struct Tile {
-    static constexpr int WM = BM / 2, WN = BN / 2;          // one wave's block
+template <int BM, int BN, int WGM, int WGN>
+struct Cfg {
+    static constexpr int THREADS = 64 * WGM * WGN;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;      // one wave's block
     static constexpr int TM = WM / 32, TN = WN / 32;        // 32 x 32 MFMA blocks per wave
-    static constexpr int A_VEC = BM * kBK / 8 / kThreads;   // 16-byte A vectors per thread
-    static constexpr int B_BLK = (kBK / 8) * (BN / 8);      // 8 x 8 B blocks per stage
-    static constexpr int LDS_A = BM * kBK / 8;              // 16-byte chunks per A stage
-    static constexpr int LDS_B = BN * kBK / 8;
-    static_assert(A_VEC >= 1 && B_BLK <= kThreads, "tile shape");
+    static constexpr int A_STAGE = BM * 128;                // bytes
+    static constexpr int B_STAGE = BN * 128;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int B_ROW = BN * 2;                    // bytes per B row in LDS
+    static constexpr int A_VEC = BM * kBK / 8 / THREADS;    // 16-byte A vectors per thread
+    static constexpr int B_VEC = BN * kBK / 8 / THREADS;
+    static_assert(TM >= 1 && TN >= 1 && A_VEC >= 1 && B_VEC >= 1, "tile shape");
+    static_assert(BN >= 128, "B swizzle needs at least 8 units of 32 bytes per row");
 };
 
-template <int BM, int BN, bool OUT_F32>
-__global__ void __launch_bounds__(kThreads)
+template <int BM, int BN, int WGM, int WGN, bool OUT_F32>
+__global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
-    using T = Tile<BM, BN>;
-    __shared__ u32x4_t smem[2 * (T::LDS_A + T::LDS_B)];
-    u32x4_t *As = smem;                  // [2][BM][8 chunks]
-    u32x4_t *Bs = smem + 2 * T::LDS_A;   // [2][BN][8 chunks], B transposed
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
+    using T = Cfg<BM, BN, WGM, WGN>;
+    constexpr int A_VEC = T::A_VEC, B_VEC = T::B_VEC;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm0 = (wave >> 1) * T::WM;
-    const int wn0 = (wave & 1) * T::WN;
+    const int wm0 = (wave / WGN) * T::WM;
+    const int wn0 = (wave % WGN) * T::WN;
 
     // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes a contiguous run.
     const int nt = tiles_m * tiles_n;
@@ -76,58 +101,77 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     const int t = xcd * per + (xcd < rem ? xcd : rem) + slot;
     const int tm = t / tiles_n, tn = t - tm * tiles_n;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int rows_valid = (int)((p.m - m0) < BM ? (p.m - m0) : BM);
 
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    u32x4_t ra[T::A_VEC];
-    u32x4_t rb[8];
-
-    const int b_kb = tid / (BN / 8), b_nb = tid % (BN / 8);
-    const bool b_active = tid < T::B_BLK;
-
-    auto load_stage = [&](int64_t k0) {
+    // Global -> register staging.  Thread t loads A vectors q = t + THREADS i (row q / 8,
+    // 16-byte chunk q % 8) and B vectors q = t + THREADS i (row q / (BN / 8), columns
+    // 8 (q % (BN / 8)) ..).
+    int a_voff[A_VEC], a_kc[A_VEC], a_lds[A_VEC];
 #pragma unroll
-        for (int i = 0; i < T::A_VEC; ++i) {
-            const int q = tid + i * kThreads;
-            const int r = q >> 3, c = q & 7;
-            const int64_t gm = m0 + r, gk = k0 + c * 8;
-            ra[i] = (gm < p.m && gk < p.k)
-                        ? *reinterpret_cast<const u32x4_t *>(p.a + gm * p.lda + gk) : zero;
-        }
-        if (b_active) {
-            const int64_t gn = n0 + b_nb * 8;
+    for (int i = 0; i < A_VEC; ++i) {
+        const int q = tid + i * T::THREADS;
+        const int row = q >> 3, c = q & 7;
+        a_kc[i] = c * 8;
+        a_voff[i] = (int)((row * p.lda + c * 8) * 2);
+        a_lds[i] = row * 128 + ((c ^ swz(row)) << 4);
+    }
+    int b_voff[B_VEC], b_lds[B_VEC];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t gk = k0 + b_kb * 8 + j;
-                rb[j] = (gk < p.k && gn < p.n)
-                            ? *reinterpret_cast<const u32x4_t *>(p.b + gk * p.ldb + gn) : zero;
-            }
+    for (int i = 0; i < B_VEC; ++i) {
+        const int q = tid + i * T::THREADS;
+        const int row = q / (BN / 8), piece = q % (BN / 8);
+        const int64_t n = n0 + piece * 8;
+        b_voff[i] = n < p.n ? (int)((row * p.ldb + n) * 2) : kOutOfRange;
+        b_lds[i] = row * T::B_ROW + (((piece >> 1) ^ ((row & 3) << 1)) << 5) + ((piece & 1) << 4);
+    }
+    u32x4_t ra[A_VEC], rb[B_VEC];
+
+    const int nk = (int)((p.k + kBK - 1) / kBK);
+    // Loads stage kt into registers.  Stages past the end (kt >= nk) get an empty buffer
+    // range and read zeros, which keeps the loop free of branches.
+    auto load_stage = [&](int kt) {
+        const bool live = kt < nk;
+        const int64_t k0 = live ? (int64_t)kt * kBK : 0;
+        const int64_t a_bytes = live ? ((int64_t)rows_valid * p.lda - k0) * 2 : 0;
+        __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.a + m0 * p.lda + k0), (short)0, (int)a_bytes, kRsrcFlags);
+        const bool k_tail = k0 + kBK > p.k;
+#pragma unroll
+        for (int i = 0; i < A_VEC; ++i) {
+            const int off = (k_tail && k0 + a_kc[i] >= p.k) ? kOutOfRange : a_voff[i];
+            ra[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0));
         }
+        const int64_t k_rows = !live ? 0 : (p.k - k0) < kBK ? (p.k - k0) : kBK;
+        __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.b + k0 * p.ldb), (short)0, (int)(k_rows * p.ldb * 2), kRsrcFlags);
+#pragma unroll
+        for (int i = 0; i < B_VEC; ++i)
+            rb[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(br, b_voff[i], 0, 0));
+    };
+    auto store_stage = [&](char *dst) {
+#pragma unroll
+        for (int i = 0; i < A_VEC; ++i) *reinterpret_cast<u32x4_t *>(dst + a_lds[i]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_VEC; ++i) *reinterpret_cast<u32x4_t *>(dst + T::A_STAGE + b_lds[i]) = rb[i];
     };
 
-    auto store_stage = [&](int buf) {
-        u32x4_t *as = As + buf * T::LDS_A;
+    // fragment read offsets
+    const int a_hi = lane >> 5;
+    int a_row_off[T::TM], a_swz[T::TM];
 #pragma unroll
-        for (int i = 0; i < T::A_VEC; ++i) {
-            const int q = tid + i * kThreads;
-            const int r = q >> 3, c = q & 7;
-            as[r * 8 + (c ^ swz(r))] = ra[i];
-        }
-        if (b_active) {
-            u32x4_t *bs = Bs + buf * T::LDS_B;
+    for (int i = 0; i < T::TM; ++i) {
+        const int r = wm0 + i * 32 + (lane & 31);
+        a_row_off[i] = r * 128;
+        a_swz[i] = swz(r);
+    }
+    const int rr = lane & 15;
+    const int b_k0 = 8 * (lane >> 5) + (rr >> 2);  // k within a 16-k step, first half
+    int b_col_off[T::TN];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                // column c of the 8 x 8 block: k = 0..7 of output feature b_nb * 8 + c
-                const int w = c >> 1, sh = (c & 1) * 16;
-                u32x4_t o;
-                o.x = ((rb[0][w] >> sh) & 0xffffu) | (((rb[1][w] >> sh) & 0xffffu) << 16);
-                o.y = ((rb[2][w] >> sh) & 0xffffu) | (((rb[3][w] >> sh) & 0xffffu) << 16);
-                o.z = ((rb[4][w] >> sh) & 0xffffu) | (((rb[5][w] >> sh) & 0xffffu) << 16);
-                o.w = ((rb[6][w] >> sh) & 0xffffu) | (((rb[7][w] >> sh) & 0xffffu) << 16);
-                const int n = b_nb * 8 + c;
-                bs[n * 8 + (b_kb ^ swz(n))] = o;
-            }
-        }
-    };
+    for (int j = 0; j < T::TN; ++j) {
+        const int n = wn0 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (rr & 3);
+        b_col_off[j] = (((n >> 4) ^ ((b_k0 & 3) << 1)) << 5) + (n & 15) * 2;
+    }
 
     f32x16_t acc[T::TM][T::TN];
 #pragma unroll
@@ -137,42 +181,65 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    auto compute_stage = [&](int buf) {
-        const u32x4_t *as = As + buf * T::LDS_A;
-        const u32x4_t *bs = Bs + buf * T::LDS_B;
+    auto load_frags = [&](const char *as, const char *bs, int s, bf16x8_t *af, bf16x8_t *bfr) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const int ch = (2 * s + a_hi) ^ a_swz[i];
+            af[i] = *reinterpret_cast<const bf16x8_t *>(as + a_row_off[i] + ch * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const char *base = bs + (s * 16 + b_k0) * T::B_ROW + b_col_off[j];
+            bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
+            bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * T::B_ROW));
+            bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+
+    // MFMAs of one stage on `cur`, with the fragments of step s + 1 read during step s.
+    auto compute_stage = [&](const char *cur) {
+        const char *as = cur;
+        const char *bs = cur + T::A_STAGE;
+        bf16x8_t af[2][T::TM], bfr[2][T::TN];
+        load_frags(as, bs, 0, af[0], bfr[0]);
 #pragma unroll
         for (int s = 0; s < kBK / 16; ++s) {
-            const int ch = 2 * s + (lane >> 5);  // 16-byte chunk holding k = 16 s + 8 (lane / 32) ..
-            bf16x8_t af[T::TM], bfr[T::TN];
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i) {
-                const int r = wm0 + i * 32 + (lane & 31);
-                af[i] = __builtin_bit_cast(bf16x8_t, as[r * 8 + (ch ^ swz(r))]);
-            }
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j) {
-                const int n = wn0 + j * 32 + (lane & 31);
-                bfr[j] = __builtin_bit_cast(bf16x8_t, bs[n * 8 + (ch ^ swz(n))]);
-            }
+            if (s + 1 < kBK / 16) load_frags(as, bs, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],
-                                                                        0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][j],
+                                                                        acc[i][j], 0, 0, 0);
+        }
+    };
+    // Instruction order of a stage (see the file comment).
+    auto pin_schedule = [&]() {
+        constexpr int kDsPerStep = T::TM + 2 * T::TN;
+        constexpr int kMfmaPerStep = T::TM * T::TN;
+        constexpr int kSteps = kBK / 16;
+        __builtin_amdgcn_sched_group_barrier(0x020, A_VEC + B_VEC, 0);  // global loads first
+        __builtin_amdgcn_sched_group_barrier(0x100, kDsPerStep, 0);
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+#pragma unroll
+            for (int m = 0; m < kMfmaPerStep; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (s + 1 < kSteps && m < kDsPerStep) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
         }
     };
 
-    const int nk = (int)((p.k + kBK - 1) / kBK);
     load_stage(0);
-    store_stage(0);
+    store_stage(smem);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) load_stage((int64_t)(kt + 1) * kBK);
+        char *cur = smem + (kt & 1) * T::STAGE;
+        char *nxt = smem + ((kt & 1) ^ 1) * T::STAGE;
+        load_stage(kt + 1);
         compute_stage(cur);
-        if (more) store_stage(cur ^ 1);
+        pin_schedule();
+        store_stage(nxt);
         __syncthreads();
     }
 
@@ -196,42 +263,72 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
             }
         }
     }
+#endif
 }
 
-template <int BM, int BN>
-hipError_t launch_tile(const GemmProblem &p, hipStream_t stream) {
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
     const int64_t tm = (p.m + BM - 1) / BM, tn = (p.n + BN - 1) / BN;
     const int64_t nt = tm * tn;
     if (nt == 0) return hipSuccess;
     if (nt > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)nt), block(64 * WGM * WGN);
     if (p.c_f32)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true>), dim3((unsigned)nt), dim3(kThreads), 0,
-                           stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true>), grid, block, 0, stream, p, (int)tm,
+                           (int)tn);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false>), dim3((unsigned)nt), dim3(kThreads), 0,
-                           stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false>), grid, block, 0, stream, p, (int)tm,
+                           (int)tn);
     return hipGetLastError();
 }
 
-GemmTile resolve(const GemmProblem &p, GemmTile t) {
-    if (t != GemmTile::Auto) return t;
+// Tile configurations.  All share the MFMA instruction and the K order.
+enum Config { k256x256w2x2, k256x256w2x4, k256x256w4x2, k128x128w2x2, kNumConfigs };
+
+const char *config_name(int c) {
+    switch (c) {
+        case k256x256w2x2: return "256x256w2x2";
+        case k256x256w2x4: return "256x256w2x4";
+        case k256x256w4x2: return "256x256w4x2";
+        default: return "128x128w2x2";
+    }
+}
+
+// SPTL_GEMM_CFG=<name> forces one configuration for every GEMM (measurement aid).
+int forced_config() {
+    static const int forced = [] {
+        const char *e = getenv("SPTL_GEMM_CFG");
+        if (!e) return -1;
+        for (int c = 0; c < kNumConfigs; ++c)
+            if (!strcmp(e, config_name(c))) return c;
+        return -1;
+    }();
+    return forced;
+}
+
+int resolve(const GemmProblem &p, GemmTile t) {
+    if (forced_config() >= 0) return forced_config();
+    if (t == GemmTile::T256x256) return k256x256w2x2;
+    if (t == GemmTile::T128x128) return k128x128w2x2;
     // One wave of 256 x 256 tiles needs about one workgroup per CU (256 on MI355X); below
     // that, 128 x 128 tiles keep every CU busy.
     const int64_t big = ((p.m + 255) / 256) * ((p.n + 255) / 256);
-    return big >= 240 ? GemmTile::T256x256 : GemmTile::T128x128;
+    return big >= 240 ? k256x256w2x2 : k128x128w2x2;
 }
 
 }  // namespace
 
 int64_t gemm_workgroups(const GemmProblem &p, GemmTile t) {
-    const int s = resolve(p, t) == GemmTile::T256x256 ? 256 : 128;
+    const int s = resolve(p, t) == k128x128w2x2 ? 128 : 256;
     return ((p.m + s - 1) / s) * ((p.n + s - 1) / s);
 }
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile) {
     switch (resolve(p, tile)) {
-        case GemmTile::T256x256: return launch_tile<256, 256>(p, stream);
-        default: return launch_tile<128, 128>(p, stream);
+        case k256x256w2x2: return launch_cfg<256, 256, 2, 2>(p, stream);
+        case k256x256w2x4: return launch_cfg<256, 256, 2, 4>(p, stream);
+        case k256x256w4x2: return launch_cfg<256, 256, 4, 2>(p, stream);
+        default: return launch_cfg<128, 128, 2, 2>(p, stream);
     }
 }
 
