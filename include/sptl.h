@@ -55,7 +55,8 @@ typedef enum {
     SPTL_E_RANGE = 6,        /* rank, tp, delta or module index out of range, or a pointer
                                 given/omitted against the delayed-TP schedule            */
     SPTL_E_HIP = 7,          /* a HIP runtime call failed                                 */
-    SPTL_E_UNSUPPORTED = 8   /* valid request this build does not handle                  */
+    SPTL_E_UNSUPPORTED = 8,  /* valid request this build does not handle                  */
+    SPTL_E_ASYNC = 9         /* an asynchronous failure was recorded (see sptl_ctx_check)  */
 } sptl_status;
 
 /* Limits. */
@@ -78,6 +79,17 @@ const char *sptl_last_error(void);
 
 /* ABI version (major * 100 + minor). */
 int sptl_version(void);
+
+/* Waits until every agmm_chunked call made on ctx has completed on the GPU, then reports
+ * asynchronous failures recorded since the last check: SPTL_E_ASYNC if a staging wait timed
+ * out (the affected call's y is invalid) or a staging copy could not be submitted (the
+ * staged path is then disabled for ctx); SPTL_OK otherwise.  Clears the recorded state. */
+int sptl_ctx_check(sptl_ctx *ctx);
+
+/* Short text naming how agmm_chunked stages chunks on ctx (copy engines driven directly with
+ * a chunk-ordered GEMM, or one copy and one GEMM launch per chunk) and, for the latter, why.
+ * Owned by ctx; valid until ctx is destroyed.  Diagnostic only. */
+const char *sptl_ctx_info(sptl_ctx *ctx);
 
 /*
  * (1) Chunked sequence all-gather + column-parallel GEMM, this rank's share.

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsptl.so")
 ARCH = "gfx950"
 
-SOURCES = ["sptl_abi.cpp", "sptl_gemm.hip", "sptl_epilogue.hip"]
+SOURCES = ["sptl_abi.cpp", "sptl_stager.cpp", "sptl_gemm.hip", "sptl_epilogue.hip"]
 
 # packed-fp32 instructions are disabled for all device code (the compiler would otherwise
 # form them from ordinary float code).
@@ -50,7 +50,8 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(min(len(jobs), 8)) as ex:
         list(ex.map(lambda j: _run(j[0]), jobs))
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o in jobs], "-o", tmp])
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o in jobs], "-o", tmp,
+          "-lhsa-runtime64", "-lpthread"])
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

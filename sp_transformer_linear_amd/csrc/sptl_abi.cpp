@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -12,9 +13,21 @@
 
 #include "sptl.h"
 #include "sptl_internal.h"
+#include "sptl_stager.h"
 
 struct sptl_ctx {
     int device = 0;
+    // SDMA stager (chunk-ordered path); created on first use, null if unavailable
+    sptl::SdmaStager *stager = nullptr;
+    bool stager_tried = false;
+    bool events_only = false;           // SPTL_STAGING=events: always use the per-chunk event path
+    std::string staging_info;           // how agmm_chunked stages chunks, and why
+    int *err_dev = nullptr;             // device flag set by a timed-out staging wait
+    uint64_t *ts_dev = nullptr;         // [3 * kMaxPlanChunks + 1] chunk timestamps
+    int wallclock_khz = 100000;
+    int t_mode = 0;                     // 0: event timeline, 1: chunk-ordered timeline
+    int t_rank_first = 0, t_rank_count = 0;
+    hipEvent_t t_done = nullptr;        // end of the last timed chunk-ordered call
     hipStream_t copy_stream = nullptr;  // created on first use
     hipEvent_t fork = nullptr;          // compute stream -> copy stream
     hipEvent_t join = nullptr;          // copy stream -> compute stream
@@ -96,6 +109,16 @@ int create_ctx(sptl_ctx **out, int device) {
     if (!rc) rc = make_event(&c->join);
     if (!rc) rc = make_event(&c->t_base);
     if (!rc) rc = grow_events(c->ready, 64);
+    if (!rc && hipMalloc(&c->err_dev, 256) != hipSuccess) rc = fail(SPTL_E_HIP, "hipMalloc of the error flag failed");
+    if (!rc && hipMalloc(&c->ts_dev, sizeof(uint64_t) * (3 * sptl::kMaxPlanChunks + 8)) != hipSuccess)
+        rc = fail(SPTL_E_HIP, "hipMalloc of the timestamp buffer failed");
+    if (!rc && hipMemset(c->err_dev, 0, 256) != hipSuccess) rc = fail(SPTL_E_HIP, "hipMemset failed");
+    if (!rc) {
+        (void)hipDeviceGetAttribute(&c->wallclock_khz, hipDeviceAttributeWallClockRate, device);
+        if (c->wallclock_khz <= 0) c->wallclock_khz = 100000;
+        const char *e = getenv("SPTL_STAGING");
+        c->events_only = e && !strcmp(e, "events");
+    }
     if (rc) {
         sptl_destroy(c);
         return rc;
@@ -142,11 +165,127 @@ int check_gemm_dims(int64_t m, int64_t k, int64_t n) {
     return SPTL_OK;
 }
 
+// Whether the chunk-ordered path (SDMA stager + one chunk-ordered GEMM) can serve this call.
+bool staged_path(sptl_ctx *ctx, int64_t rows_c, int n_chunks) {
+    if (ctx->events_only || n_chunks > sptl::kMaxPlanChunks || !sptl::chunk_tile_rows(rows_c)) return false;
+    if (!ctx->stager_tried) {
+        ctx->stager_tried = true;
+        std::string why;
+        ctx->stager = sptl::stager_create(ctx->device, &why);  // null: the event path is used
+        ctx->staging_info = ctx->stager ? "sdma-striped over " + std::to_string(sptl::stager_engine_count(ctx->stager)) +
+                                              " engines, chunk-ordered GEMM"
+                                        : "per-chunk events (copy engines unavailable: " + why + ")";
+    }
+    return ctx->stager && !sptl::stager_failed(ctx->stager);
+}
+
+// Chunk-ordered agmm: all staging copies go to the SDMA stager (striped over the copy
+// engines, released at the fork point), and one GEMM launch processes the row tiles in
+// chunk order, each tile waiting for its chunk's completion signal.  Arguments validated.
+int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local, int tp, int n_chunks,
+                int rank, const void *const *shard_src, uint16_t *xg, const void *w, void *y, int y_dtype,
+                hipStream_t cs, int timing) {
+    const int cpr = n_chunks / tp;
+    const int64_t rows_c = seq_len / n_chunks;
+    const size_t chunk_elems = (size_t)rows_c * (size_t)hidden;
+    const size_t chunk_bytes = chunk_elems * 2;
+    auto src_chunk = [&](int q, int s) {
+        return static_cast<const uint16_t *>(shard_src[q]) + (size_t)s * chunk_elems;
+    };
+    const bool own_aliased = shard_src[rank] == xg + (size_t)rank * cpr * chunk_elems;
+
+    // copies in arrival order (peers rank+1, rank+2, ...), then this rank's own slot
+    std::vector<sptl::CopyPiece> copies;
+    sptl::GemmProblem gp{};
+    sptl::ChunkPlan &plan = gp.plan;
+    int pos = 0;
+    for (int s = 0; s < cpr; ++s) plan.order[pos++] = rank * cpr + s;
+    for (int d = 1; d < tp; ++d) {
+        const int q = (rank + d) % tp;
+        for (int s = 0; s < cpr; ++s) {
+            const int c = q * cpr + s;
+            plan.order[pos++] = c;
+            copies.push_back({xg + (size_t)c * chunk_elems, src_chunk(q, s), chunk_bytes, c});
+        }
+    }
+    if (!own_aliased)
+        copies.push_back({xg + (size_t)rank * cpr * chunk_elems, shard_src[rank], chunk_bytes * cpr, sptl::kJoinChunk});
+    std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies);
+    sptl::StageCall call;
+    std::string why;
+    if (sptl::stager_begin(ctx->stager, pieces, &call, &why))
+        return fail(SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
+
+    const int n = n_chunks;
+    if (timing) {
+        SPTL_HIP(sptl::launch_fill_u64(ctx->ts_dev, 2 * n, ~0ull, cs));
+        SPTL_HIP(sptl::launch_fill_u64(ctx->ts_dev + 2 * n, n + 1, 0ull, cs));
+    }
+    SPTL_HIP(hipEventRecord(call.fork, cs));
+    gp.a = xg;
+    gp.b = static_cast<const uint16_t *>(w);
+    gp.c = y;
+    gp.m = seq_len;
+    gp.n = n_local;
+    gp.k = hidden;
+    gp.lda = hidden;
+    gp.ldb = n_local;
+    gp.ldc = n_local;
+    gp.c_f32 = y_dtype == SPTL_F32;
+    plan.chunk_rows = (int)rows_c;
+    plan.n_chunks = n;
+    plan.own_first = rank * cpr;
+    plan.own_count = cpr;
+    for (int c = 0; c < n; ++c) plan.ready[c] = call.ready[c];
+    for (int s = 0; s < cpr; ++s) plan.ready[rank * cpr + s] = nullptr;  // read from the source
+    plan.join = call.join;
+    plan.own_a = static_cast<const uint16_t *>(shard_src[rank]);
+    plan.err = ctx->err_dev;
+    plan.timeout_ticks = (uint64_t)ctx->wallclock_khz * 10000u;  // 10 s
+    plan.ts = timing ? ctx->ts_dev : nullptr;
+    SPTL_HIP(sptl::launch_gemm(gp, cs));
+    SPTL_HIP(hipEventRecord(call.done, cs));
+    if (sptl::stager_submit(ctx->stager, call, std::move(pieces), &why))
+        return fail(SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
+    if (timing) {
+        ctx->t_mode = 1;
+        ctx->t_chunks = n;
+        ctx->t_done = call.done;
+        ctx->t_rank_first = rank * cpr;
+        ctx->t_rank_count = cpr;
+    }
+    return SPTL_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int sptl_version(void) { return 100; }
+
+const char *sptl_ctx_info(sptl_ctx *ctx) {
+    if (resolve_ctx(ctx)) return "";
+    if (ctx->events_only) return "per-chunk events (forced by SPTL_STAGING=events)";
+    if (!ctx->stager_tried) return "not yet decided (no agmm_chunked call)";
+    return ctx->staging_info.c_str();
+}
+
+int sptl_ctx_check(sptl_ctx *ctx) {
+    if (int rc = resolve_ctx(ctx)) return rc;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    if (ctx->stager && sptl::stager_wait_idle(ctx->stager))
+        return fail(SPTL_E_HIP, "sptl_ctx_check: waiting for staged calls failed");
+    int flag = 0;
+    SPTL_HIP(hipMemcpy(&flag, ctx->err_dev, sizeof flag, hipMemcpyDeviceToHost));
+    if (flag) {
+        SPTL_HIP(hipMemset(ctx->err_dev, 0, sizeof flag));
+        return fail(SPTL_E_ASYNC, "a staging wait timed out; the affected agmm_chunked results are invalid");
+    }
+    if (ctx->stager && sptl::stager_failed(ctx->stager))
+        return fail(SPTL_E_ASYNC, "a staging copy could not be submitted; the staged path is now disabled");
+    return SPTL_OK;
+}
 
 const char *sptl_last_error(void) { return g_err.c_str(); }
 
@@ -159,6 +298,9 @@ int sptl_create(sptl_ctx **out, int device) {
 int sptl_destroy(sptl_ctx *ctx) {
     if (!ctx) return SPTL_OK;
     DeviceGuard g(ctx->device);
+    if (ctx->stager) sptl::stager_destroy(ctx->stager);
+    if (ctx->err_dev) (void)hipFree(ctx->err_dev);
+    if (ctx->ts_dev) (void)hipFree(ctx->ts_dev);
     if (ctx->copy_stream) {
         (void)hipStreamSynchronize(ctx->copy_stream);
         (void)hipStreamDestroy(ctx->copy_stream);
@@ -204,6 +346,12 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
 
     hipStream_t cs = static_cast<hipStream_t>(compute);
+    if (!copy && staged_path(ctx, seq_len / n_chunks, n_chunks)) {
+        ctx->t_chunks = -1;
+        return agmm_staged(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, shard_src,
+                           static_cast<uint16_t *>(x_gathered), w, y, y_dtype, cs, timing);
+    }
+    // ---- event path: one SDMA copy per chunk on a copy stream, one GEMM launch per chunk ----
     hipStream_t ps = static_cast<hipStream_t>(copy);
     if (!ps)
         if (int rc = copy_stream_of(ctx, &ps)) return rc;
@@ -295,7 +443,10 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
     }
     // ---- join: later work on the compute stream sees x_gathered complete ---------------
     SPTL_HIP(hipStreamWaitEvent(cs, ctx->join, 0));
-    if (timing) ctx->t_chunks = n_chunks;
+    if (timing) {
+        ctx->t_mode = 0;
+        ctx->t_chunks = n_chunks;
+    }
     return SPTL_OK;
 }
 
@@ -306,6 +457,25 @@ int sptl_agmm_timeline(sptl_ctx *ctx, double *out, int n_chunks) {
         return fail(SPTL_E_RANGE, "sptl_agmm_timeline: no timed call with n_chunks=%d", n_chunks);
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    if (ctx->t_mode == 1) {
+        // chunk-ordered call: timestamps taken by the GEMM's workgroups (wall clock)
+        const int n = n_chunks;
+        std::vector<uint64_t> ts(3 * n + 1);
+        SPTL_HIP(hipEventSynchronize(ctx->t_done));
+        SPTL_HIP(hipMemcpy(ts.data(), ctx->ts_dev, ts.size() * sizeof(uint64_t), hipMemcpyDeviceToHost));
+        const double per_ms = (double)ctx->wallclock_khz;
+        const uint64_t t0 = ts[3 * n];
+        auto ms = [&](uint64_t t) { return ((double)(int64_t)(t - t0)) / per_ms; };
+        for (int c = 0; c < n; ++c) {
+            double *row = out + 4 * c;
+            const bool own = c >= ctx->t_rank_first && c < ctx->t_rank_first + ctx->t_rank_count;
+            row[0] = own ? -1.0 : 0.0;          // every copy is queued at the fork point
+            row[1] = own ? -1.0 : ms(ts[c]);    // first tile of the chunk found it landed
+            row[2] = ms(ts[n + c]);
+            row[3] = ms(ts[2 * n + c]);
+        }
+        return SPTL_OK;
+    }
     SPTL_HIP(hipEventSynchronize(ctx->join));
     for (int c = 0; c < n_chunks; ++c) {
         float t = 0.0f;

@@ -64,6 +64,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Bounded spin until *word <= 0 (an SDMA completion signal counting down copy pieces).  On
+// timeout sets *plan.err and returns, so every wave exits.
+__device__ __forceinline__ void wait_ready(const int64_t *word, const ChunkPlan &plan) {
+    if (!word) return;
+    const uint64_t t0 = wall_clock64();
+    while (__hip_atomic_load(word, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) > 0) {
+        if (wall_clock64() - t0 > plan.timeout_ticks) {
+            __hip_atomic_store(plan.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(32);
+    }
+}
+
 template <int BM, int BN, int WGM, int WGN>
 struct Cfg {
     static constexpr int THREADS = 64 * WGM * WGN;
@@ -79,7 +93,7 @@ struct Cfg {
     static_assert(BN >= 128, "B swizzle needs at least 8 units of 32 bytes per row");
 };
 
-template <int BM, int BN, int WGM, int WGN, bool OUT_F32>
+template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
@@ -93,15 +107,48 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     const int wm0 = (wave / WGN) * T::WM;
     const int wn0 = (wave % WGN) * T::WN;
 
-    // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes a contiguous run.
-    const int nt = tiles_m * tiles_n;
     const int bid = blockIdx.x;
-    const int per = nt >> 3, rem = nt & 7;
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int t = xcd * per + (xcd < rem ? xcd : rem) + slot;
-    const int tm = t / tiles_n, tn = t - tm * tiles_n;
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const int rows_valid = (int)((p.m - m0) < BM ? (p.m - m0) : BM);
+    int64_t m0, n0;          // output tile origin
+    const uint16_t *a_tile;  // first row of this tile's A rows
+    int rows_valid;
+    const ChunkPlan &plan = p.plan;
+    int chunk = -1;
+    if constexpr (!CHUNKED) {
+        // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes a contiguous run.
+        const int nt = tiles_m * tiles_n;
+        const int per = nt >> 3, rem = nt & 7;
+        const int xcd = bid & 7, slot = bid >> 3;
+        const int t = xcd * per + (xcd < rem ? xcd : rem) + slot;
+        const int tm = t / tiles_n, tn = t - tm * tiles_n;
+        m0 = (int64_t)tm * BM;
+        n0 = (int64_t)tn * BN;
+        a_tile = p.a + m0 * p.lda;
+        rows_valid = (int)((p.m - m0) < BM ? (p.m - m0) : BM);
+    } else {
+        // Chunk-ordered: workgroups are dispatched in index order, so tiles of the chunks
+        // that land first come first.  A chunk is a whole number of tile rows.
+        const int lt = bid / tiles_n, tn = bid - lt * tiles_n;
+        const int tpc = plan.chunk_rows / BM;
+        const int pos = lt / tpc, sub = lt - pos * tpc;
+        chunk = plan.order[pos];
+        m0 = (int64_t)chunk * plan.chunk_rows + (int64_t)sub * BM;
+        n0 = (int64_t)tn * BN;
+        rows_valid = BM;
+        const int own_idx = chunk - plan.own_first;
+        a_tile = (own_idx >= 0 && own_idx < plan.own_count)
+                     ? plan.own_a + ((int64_t)own_idx * plan.chunk_rows + (int64_t)sub * BM) * p.lda
+                     : p.a + m0 * p.lda;
+        if (plan.ts && bid == 0 && tid == 0) plan.ts[3 * plan.n_chunks] = wall_clock64();
+        if (tid == 0) {
+            wait_ready(plan.ready[chunk], plan);  // this chunk's copy pieces have landed
+            if (plan.ts) {
+                const unsigned long long now = wall_clock64();
+                atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + chunk), now);
+                atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + plan.n_chunks + chunk), now);
+            }
+        }
+        __syncthreads();
+    }
 
     // Global -> register staging.  Thread t loads A vectors q = t + THREADS i (row q / 8,
     // 16-byte chunk q % 8) and B vectors q = t + THREADS i (row q / (BN / 8), columns
@@ -134,7 +181,7 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         const int64_t k0 = live ? (int64_t)kt * kBK : 0;
         const int64_t a_bytes = live ? ((int64_t)rows_valid * p.lda - k0) * 2 : 0;
         __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(p.a + m0 * p.lda + k0), (short)0, (int)a_bytes, kRsrcFlags);
+            (void *)(a_tile + k0), (short)0, (int)a_bytes, kRsrcFlags);
         const bool k_tail = k0 + kBK > p.k;
 #pragma unroll
         for (int i = 0; i < A_VEC; ++i) {
@@ -263,7 +310,19 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
             }
         }
     }
+    if (CHUNKED && tid == 0) {
+        if (plan.ts)
+            atomicMax(reinterpret_cast<unsigned long long *>(plan.ts + 2 * plan.n_chunks + chunk),
+                      (unsigned long long)wall_clock64());
+        // the kernel ends only once every copy of the call has landed (own slot included)
+        if (blockIdx.x == gridDim.x - 1) wait_ready(plan.join, plan);
+    }
 #endif
+}
+
+__global__ void fill_u64_kernel(uint64_t *p, int64_t n, uint64_t v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
 }
 
 template <int BM, int BN, int WGM, int WGN>
@@ -273,12 +332,15 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
     if (nt == 0) return hipSuccess;
     if (nt > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nt), block(64 * WGM * WGN);
-    if (p.c_f32)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true>), grid, block, 0, stream, p, (int)tm,
-                           (int)tn);
+    const bool chunked = p.plan.chunk_rows != 0;
+    if (p.c_f32 && chunked)
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
+    else if (p.c_f32)
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
+    else if (chunked)
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false>), grid, block, 0, stream, p, (int)tm,
-                           (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
     return hipGetLastError();
 }
 
@@ -307,20 +369,32 @@ int forced_config() {
 }
 
 int resolve(const GemmProblem &p, GemmTile t) {
+    if (p.plan.chunk_rows) {  // chunk-ordered: the tile height must divide the chunk
+        if (p.plan.chunk_rows % 256 == 0 && forced_config() >= 0 && forced_config() != k128x128w2x2)
+            return forced_config();
+        return p.plan.chunk_rows % 256 == 0 ? k256x256w4x2 : k128x128w2x2;
+    }
     if (forced_config() >= 0) return forced_config();
-    if (t == GemmTile::T256x256) return k256x256w2x2;
+    if (t == GemmTile::T256x256) return k256x256w4x2;
     if (t == GemmTile::T128x128) return k128x128w2x2;
     // One wave of 256 x 256 tiles needs about one workgroup per CU (256 on MI355X); below
     // that, 128 x 128 tiles keep every CU busy.
     const int64_t big = ((p.m + 255) / 256) * ((p.n + 255) / 256);
-    return big >= 240 ? k256x256w2x2 : k128x128w2x2;
+    return big >= 240 ? k256x256w4x2 : k128x128w2x2;
 }
 
 }  // namespace
 
-int64_t gemm_workgroups(const GemmProblem &p, GemmTile t) {
-    const int s = resolve(p, t) == k128x128w2x2 ? 128 : 256;
-    return ((p.m + s - 1) / s) * ((p.n + s - 1) / s);
+int chunk_tile_rows(int64_t chunk_rows) {
+    if (chunk_rows > 0 && chunk_rows % 256 == 0) return 256;
+    if (chunk_rows > 0 && chunk_rows % 128 == 0) return 128;
+    return 0;
+}
+
+hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n, v);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile) {

@@ -1,10 +1,35 @@
-// Internal interfaces between the C-ABI layer and the HIP kernels of libsptl.so.
+// Internal interfaces between the C-ABI layer, the SDMA stager and the HIP kernels of
+// libsptl.so.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace sptl {
+
+constexpr int kMaxPlanChunks = 64;  // chunks of one chunk-ordered GEMM launch
+
+// Chunk-ordered GEMM over a gathered activation (the column GEMM of the chunked all-gather +
+// matmul).  Row tiles are processed in `order` (own chunks first, then the peers' chunks in
+// arrival order); the workgroups of a tile of chunk c wait, with a bounded spin, until
+// *ready[c] <= 0 (an SDMA completion signal counting down the chunk's copy pieces) before
+// reading its rows.  Rows of chunks [own_first, own_first + own_count) are read from own_a
+// (this rank's shard), all others from GemmProblem::a (the gathered buffer).
+struct ChunkPlan {
+    int chunk_rows;                          // rows per chunk, a multiple of the tile height
+    int n_chunks;                            // <= kMaxPlanChunks
+    int own_first, own_count;
+    int order[kMaxPlanChunks];               // processing position -> chunk
+    const int64_t *ready[kMaxPlanChunks];    // per chunk; nullptr: no wait
+    const int64_t *join;                     // waited for by the last workgroup before it exits
+    const uint16_t *own_a;
+    int *err;                                // set to 1 when a wait times out
+    uint64_t timeout_ticks;                  // wall-clock ticks of the bounded waits
+    uint64_t *ts;                            // optional per-chunk timestamps (see below)
+};
+// ts layout (wall-clock ticks, n = n_chunks): ts[c] = first time a tile of chunk c found it
+// ready (min), ts[n + c] = first tile start of chunk c (min), ts[2 n + c] = last tile end of
+// chunk c (max), ts[3 n] = start of workgroup 0.
 
 // C[M, N] = A[M, K] @ B[K, N]; bf16 inputs, fp32 accumulation, bf16 or fp32 output.
 // Row-major with leading dimensions lda, ldb, ldc (elements).  K and N multiples of 8,
@@ -17,6 +42,7 @@ struct GemmProblem {
     int64_t m, n, k;
     int64_t lda, ldb, ldc;
     bool c_f32;
+    ChunkPlan plan;   // plan.chunk_rows == 0: plain GEMM
 };
 
 enum class GemmTile { T256x256, T128x128, Auto };
@@ -25,8 +51,11 @@ enum class GemmTile { T256x256, T128x128, Auto };
 // launch.
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile = GemmTile::Auto);
 
-// Number of workgroups the launch of `p` uses with tile `t` (Auto resolved).
-int64_t gemm_workgroups(const GemmProblem &p, GemmTile t = GemmTile::Auto);
+// Tile height a chunk-ordered launch of `p` would use (0: chunk_rows fits no tile height).
+int chunk_tile_rows(int64_t chunk_rows);
+
+// Fills n 64-bit words with v on `stream` (a kernel, so it is safe inside graph capture).
+hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t stream);
 
 constexpr int kMaxEpilogueInputs = 17;  // residual + 16 partials
 

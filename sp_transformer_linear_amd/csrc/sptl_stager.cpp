@@ -1,0 +1,348 @@
+// SDMA chunk stager for agmm_chunked (see sptl_stager.h).
+//
+// Why: the sequence all-gather must not take compute units from the GEMM (Megatron-LM pull
+// request #5513, "Observations" and "Recommendations": only the copy-engine gather helped).
+// On MI355X one SDMA engine moves ~57 GB/s device to device and a HIP copy stream uses one
+// engine at a time, so a chunk is striped over all available engines (14 on MI355X), driven
+// through HSA, each piece decrementing the chunk's completion signal.  The signals are
+// GPU-only HSA signals, whose values live in device memory where the chunk-ordered GEMM
+// polls them.
+//
+// Ordering: copies must not overwrite the gathered buffer while earlier work on the compute
+// stream still reads it.  A HIP event recorded at the call's fork point is waited for by a
+// worker thread (interrupt-driven), which then submits the pieces with no HSA dependencies.
+// (A dependency on a signal written by a kernel is resolved by the runtime's host thread
+// with millisecond latency, because a kernel store raises no interrupt.)
+//
+// Reuse: completion-signal sets form a ring; a set is re-armed only after the GEMM that
+// waited on it has completed (its `done` event), by which point all of its pieces landed.
+#include "sptl_stager.h"
+
+#include <hsa/hsa.h>
+#include <hsa/hsa_ext_amd.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <chrono>
+#include <condition_variable>
+#include <deque>
+#include <mutex>
+#include <thread>
+
+namespace sptl {
+
+namespace {
+constexpr int kSets = 4;
+constexpr size_t kMinPiece = 512 * 1024;  // below this, striping costs more than it gains
+
+struct FindAgent {
+    uint32_t bdf;
+    uint32_t domain;
+    hsa_agent_t agent;
+    bool found;
+};
+
+hsa_status_t find_agent(hsa_agent_t a, void *data) {
+    auto *f = static_cast<FindAgent *>(data);
+    hsa_device_type_t t;
+    if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &t) != HSA_STATUS_SUCCESS || t != HSA_DEVICE_TYPE_GPU)
+        return HSA_STATUS_SUCCESS;
+    uint32_t bdf = 0, dom = 0;
+    hsa_agent_get_info(a, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_BDFID, &bdf);
+    hsa_agent_get_info(a, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_DOMAIN, &dom);
+    if ((bdf & ~7u) == (f->bdf & ~7u) && dom == f->domain) {
+        f->agent = a;
+        f->found = true;
+        return HSA_STATUS_INFO_BREAK;
+    }
+    return HSA_STATUS_SUCCESS;
+}
+}  // namespace
+
+struct SignalSet {
+    hsa_signal_t sig[kMaxPlanChunks + 1] = {};
+    int64_t *val[kMaxPlanChunks + 1] = {};
+    hipEvent_t fork = nullptr, done = nullptr;
+    bool used = false;
+};
+
+struct Job {
+    int set;
+    hipEvent_t fork;
+    std::vector<CopyPiece> pieces;
+};
+
+class SdmaStager {
+  public:
+    int device = 0;
+    hsa_agent_t agent{};
+    std::vector<uint32_t> engines;  // hsa_amd_sdma_engine_id_t bits
+    SignalSet sets[kSets];
+    int next_set = 0;
+    std::mutex mu;                  // guards next_set, sets[].used, the queue
+    std::condition_variable cv;
+    std::deque<Job> queue;
+    bool stop = false;
+    std::thread worker;
+    std::atomic<bool> failed{false};
+    unsigned next_engine = 0;       // worker thread only
+    void *scratch = nullptr;        // 8 KB for the engine checks
+
+    // The fork usually completes within microseconds of the call (earlier stream work is
+    // short), and a blocking event wait sleeps ~50 us before noticing: poll first, then block.
+    static bool wait_fork(hipEvent_t fork) {
+        const auto t0 = std::chrono::steady_clock::now();
+        for (;;) {
+            const hipError_t q = hipEventQuery(fork);
+            if (q == hipSuccess) return true;
+            if (q != hipErrorNotReady) return false;
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(200))
+                return hipEventSynchronize(fork) == hipSuccess;
+        }
+    }
+
+    void run() {
+        (void)hipSetDevice(device);
+        for (;;) {
+            Job job;
+            {
+                std::unique_lock<std::mutex> lk(mu);
+                cv.wait(lk, [&] { return stop || !queue.empty(); });
+                if (queue.empty()) return;  // stop requested and nothing left
+                job = std::move(queue.front());
+                queue.pop_front();
+            }
+            SignalSet &ss = sets[job.set];
+            static const bool trace = getenv("SPTL_STAGER_TRACE") != nullptr;
+            const auto tq = std::chrono::steady_clock::now();
+            bool ok = wait_fork(job.fork);
+            const auto tf = std::chrono::steady_clock::now();
+            int last_chunk = -2;
+            for (const CopyPiece &pc : job.pieces) {
+                if (trace && pc.chunk != last_chunk) {
+                    fprintf(stderr, "[stager] chunk %d submit at +%.1f us after fork (fork wait %.1f us)\n", pc.chunk,
+                            std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - tf).count(),
+                            std::chrono::duration<double, std::micro>(tf - tq).count());
+                    last_chunk = pc.chunk;
+                }
+                const uint32_t eng = engines[next_engine++ % engines.size()];
+                if (ok)
+                    ok = hsa_amd_memory_async_copy_on_engine(pc.dst, agent, pc.src, agent, pc.bytes, 0, nullptr,
+                                                             ss.sig[pc.chunk], (hsa_amd_sdma_engine_id_t)eng,
+                                                             true) == HSA_STATUS_SUCCESS;
+                if (!ok) {
+                    // release every waiter of this call; the call's results are invalid and
+                    // the failure is reported through stager_failed
+                    failed = true;
+                    for (int c = 0; c <= kMaxPlanChunks; ++c) hsa_signal_store_screlease(ss.sig[c], 0);
+                    break;
+                }
+            }
+        }
+    }
+};
+
+SdmaStager *stager_create(int device, std::string *err) {
+    if (hsa_init() != HSA_STATUS_SUCCESS) {
+        *err = "hsa_init failed";
+        return nullptr;
+    }
+    int bus = 0, dev = 0, dom = 0;
+    if (hipDeviceGetAttribute(&bus, hipDeviceAttributePciBusId, device) != hipSuccess ||
+        hipDeviceGetAttribute(&dev, hipDeviceAttributePciDeviceId, device) != hipSuccess ||
+        hipDeviceGetAttribute(&dom, hipDeviceAttributePciDomainID, device) != hipSuccess) {
+        *err = "cannot read the device's PCI location";
+        hsa_shut_down();
+        return nullptr;
+    }
+    FindAgent f{(uint32_t)((bus << 8) | (dev << 3)), (uint32_t)dom, {}, false};
+    hsa_iterate_agents(find_agent, &f);
+    if (!f.found) {
+        *err = "no HSA agent matches the HIP device";
+        hsa_shut_down();
+        return nullptr;
+    }
+    // Candidate engines: what the runtime reports free for device-to-device copies; some
+    // runtime versions report none for a same-device copy, then the agent's xGMI-class
+    // engines (else its plain SDMA engines) are the candidates.  Every candidate is checked
+    // with a small copy below, and only engines that complete it are used.
+    uint32_t mask = 0;
+    if (hsa_amd_memory_copy_engine_status(f.agent, f.agent, &mask) != HSA_STATUS_SUCCESS || mask == 0) {
+        uint32_t n_sdma = 0, n_xgmi = 0;
+        hsa_agent_get_info(f.agent, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_NUM_SDMA_ENG, &n_sdma);
+        hsa_agent_get_info(f.agent, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_NUM_SDMA_XGMI_ENG, &n_xgmi);
+        const uint32_t first = n_xgmi ? n_sdma : 0, count = n_xgmi ? n_xgmi : n_sdma;
+        mask = 0;
+        for (uint32_t b = first; b < first + count && b < 16; ++b) mask |= 1u << b;
+    }
+    if (mask == 0) {
+        *err = "the agent reports no SDMA engine";
+        hsa_shut_down();
+        return nullptr;
+    }
+    auto *s = new SdmaStager;
+    s->device = device;
+    s->agent = f.agent;
+    if (hipMalloc(&s->scratch, 8192) != hipSuccess || hipMemset(s->scratch, 0, 8192) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        *err = "cannot allocate the engine-check buffer";
+        (void)hipGetLastError();
+        stager_destroy(s);
+        return nullptr;
+    }
+    {
+        hsa_signal_t probe;
+        if (hsa_signal_create(1, 0, nullptr, &probe) != HSA_STATUS_SUCCESS) {
+            *err = "hsa_signal_create failed";
+            stager_destroy(s);
+            return nullptr;
+        }
+        for (int b = 0; b < 16; ++b) {
+            if (!(mask & (1u << b))) continue;
+            hsa_signal_store_screlease(probe, 1);
+            char *sc = static_cast<char *>(s->scratch);
+            if (hsa_amd_memory_async_copy_on_engine(sc + 4096, f.agent, sc, f.agent, 256, 0, nullptr, probe,
+                                                    (hsa_amd_sdma_engine_id_t)(1u << b), true) != HSA_STATUS_SUCCESS)
+                continue;
+            // bounded wait (200 ms); an engine that does not finish is left out
+            bool done = false;
+            for (int i = 0; i < 200 && !done; ++i)
+                done = hsa_signal_wait_scacquire(probe, HSA_SIGNAL_CONDITION_LT, 1, 1000000, HSA_WAIT_STATE_ACTIVE) < 1;
+            if (done) s->engines.push_back(1u << b);
+            else break;  // a copy may still be pending on `probe`: stop using it
+        }
+        if (hsa_signal_load_scacquire(probe) < 1) hsa_signal_destroy(probe);  // else leak it safely
+    }
+    if (s->engines.empty()) {
+        *err = "no SDMA engine completed a device-to-device check copy";
+        stager_destroy(s);
+        return nullptr;
+    }
+    bool ok = true;
+    std::string why;
+    for (SignalSet &ss : s->sets) {
+        for (int c = 0; c <= kMaxPlanChunks && ok; ++c) {
+            hsa_status_t st = hsa_amd_signal_create(0, 0, nullptr, HSA_AMD_SIGNAL_AMD_GPU_ONLY, &ss.sig[c]);
+            if (st != HSA_STATUS_SUCCESS) {
+                why = "hsa_amd_signal_create(GPU_ONLY) status " + std::to_string((int)st);
+                ok = false;
+                break;
+            }
+            volatile hsa_signal_value_t *vp = nullptr;
+            st = hsa_amd_signal_value_pointer(ss.sig[c], &vp);
+            if (st != HSA_STATUS_SUCCESS || !vp) {
+                why = "hsa_amd_signal_value_pointer status " + std::to_string((int)st);
+                ok = false;
+                break;
+            }
+            // the GEMM polls this word: it must be device memory the kernels can read
+            hipPointerAttribute_t pa;
+            const hipError_t he = hipPointerGetAttributes(&pa, (void *)vp);
+            if (he != hipSuccess || pa.type != hipMemoryTypeDevice) {
+                why = std::string("signal value is not known device memory (") + hipGetErrorString(he) +
+                      ", type " + std::to_string(he == hipSuccess ? (int)pa.type : -1) + ")";
+                ok = false;
+                break;
+            }
+            ss.val[c] = (int64_t *)vp;
+        }
+        if (ok && (hipEventCreate(&ss.fork) != hipSuccess || hipEventCreate(&ss.done) != hipSuccess)) {
+            why = "hipEventCreate failed";
+            ok = false;
+        }
+        if (!ok) break;
+    }
+    (void)hipGetLastError();
+    if (!ok) {
+        *err = "cannot create device-memory completion signals: " + why;
+        stager_destroy(s);
+        return nullptr;
+    }
+    s->worker = std::thread([s] { s->run(); });
+    return s;
+}
+
+void stager_destroy(SdmaStager *s) {
+    if (!s) return;
+    {
+        std::lock_guard<std::mutex> lk(s->mu);
+        s->stop = true;
+    }
+    s->cv.notify_all();
+    if (s->worker.joinable()) s->worker.join();
+    for (SignalSet &ss : s->sets) {
+        if (ss.used && ss.done) (void)hipEventSynchronize(ss.done);
+        for (int c = 0; c <= kMaxPlanChunks; ++c)
+            if (ss.sig[c].handle) hsa_signal_destroy(ss.sig[c]);
+        if (ss.fork) (void)hipEventDestroy(ss.fork);
+        if (ss.done) (void)hipEventDestroy(ss.done);
+    }
+    if (s->scratch) (void)hipFree(s->scratch);
+    delete s;
+    hsa_shut_down();
+}
+
+int stager_engine_count(const SdmaStager *s) { return s ? (int)s->engines.size() : 0; }
+
+bool stager_failed(const SdmaStager *s) { return s && s->failed.load(); }
+
+int stager_wait_idle(SdmaStager *s) {
+    for (SignalSet &ss : s->sets)
+        if (ss.used && hipEventSynchronize(ss.done) != hipSuccess) return -1;
+    return 0;
+}
+
+std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies) {
+    std::vector<CopyPiece> out;
+    const size_t E = s->engines.size();
+    for (const CopyPiece &c : copies) {
+        size_t n = c.bytes / kMinPiece;
+        n = n < 1 ? 1 : n > E ? E : n;
+        // equal pieces rounded to 256 bytes; the last takes the remainder
+        const size_t step = ((c.bytes / n) + 255) & ~(size_t)255;
+        size_t off = 0;
+        while (off < c.bytes) {
+            const size_t b = c.bytes - off < step ? c.bytes - off : step;
+            out.push_back({static_cast<char *>(c.dst) + off, static_cast<const char *>(c.src) + off, b, c.chunk});
+            off += b;
+        }
+    }
+    return out;
+}
+
+int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, StageCall *out, std::string *err) {
+    int set;
+    {
+        std::lock_guard<std::mutex> lk(s->mu);
+        set = s->next_set;
+        s->next_set = (s->next_set + 1) % kSets;
+    }
+    SignalSet &ss = s->sets[set];
+    if (ss.used && hipEventSynchronize(ss.done) != hipSuccess) {
+        *err = "waiting for an earlier staged call failed";
+        return -1;
+    }
+    int64_t count[kMaxPlanChunks + 1] = {};
+    for (const CopyPiece &p : pieces) count[p.chunk]++;
+    for (int c = 0; c <= kMaxPlanChunks; ++c) hsa_signal_store_screlease(ss.sig[c], count[c]);
+    ss.used = true;
+    out->set = set;
+    for (int c = 0; c < kMaxPlanChunks; ++c) out->ready[c] = count[c] ? ss.val[c] : nullptr;
+    out->join = count[kJoinChunk] ? ss.val[kJoinChunk] : nullptr;
+    out->fork = ss.fork;
+    out->done = ss.done;
+    return 0;
+}
+
+int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> pieces, std::string *err) {
+    (void)err;
+    {
+        std::lock_guard<std::mutex> lk(s->mu);
+        s->queue.push_back(Job{call.set, call.fork, std::move(pieces)});
+    }
+    s->cv.notify_one();
+    return 0;
+}
+
+}  // namespace sptl

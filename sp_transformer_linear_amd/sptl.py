@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 BF16, F32 = 0, 1
 STATUS = {0: "SPTL_OK", 1: "SPTL_E_NULL", 2: "SPTL_E_SHAPE", 3: "SPTL_E_DIVISIBILITY",
           4: "SPTL_E_ALIGN", 5: "SPTL_E_DTYPE", 6: "SPTL_E_RANGE", 7: "SPTL_E_HIP",
-          8: "SPTL_E_UNSUPPORTED"}
+          8: "SPTL_E_UNSUPPORTED", 9: "SPTL_E_ASYNC"}
 MAX_PARTIALS, MAX_TP, MAX_CHUNKS = 16, 64, 512
 
 _vp = ctypes.c_void_p
@@ -40,6 +40,8 @@ _SIGS = {
     "sptl_destroy": ([_vp], _int),
     "sptl_last_error": ([], ctypes.c_char_p),
     "sptl_version": ([], _int),
+    "sptl_ctx_check": ([_vp], _int),
+    "sptl_ctx_info": ([_vp], ctypes.c_char_p),
     "agmm_chunked": ([_vp, _i64, _i64, _i64, _int, _int, _int, _ptrs, _vp, _vp, _vp, _int, _vp, _vp,
                       _int], _int),
     "sptl_agmm_timeline": ([_vp, ctypes.POINTER(ctypes.c_double), _int], _int),
@@ -130,6 +132,14 @@ class Context:
             self.close()
         except Exception:
             pass
+
+    def check(self) -> None:
+        """Wait for this context's staged calls and raise SptlError on a recorded async failure."""
+        _check(_lib.sptl_ctx_check(self.handle))
+
+    def info(self) -> str:
+        """How agmm_chunked stages chunks on this context (diagnostic)."""
+        return (_lib.sptl_ctx_info(self.handle) or b"").decode()
 
     def timeline(self, n_chunks: int):
         """Per-chunk [copy start, copy end, GEMM start, GEMM end] (ms) of the last timed call."""

@@ -335,3 +335,86 @@ def test_validation_enqueues_nothing(env):
     assert rc == 1
     torch.cuda.synchronize()
     assert torch.all(y == 7.0) and torch.all(res == 1.0)
+
+
+# ------------------------------------------------------------------------------------------
+# chunk-ordered (SDMA-staged) path
+# ------------------------------------------------------------------------------------------
+
+STAGED_CASES = [
+    # tp, n_chunks, rows per rank, K, N, rank      (rows per chunk a multiple of 128)
+    (4, 4, 256, 512, 384, 1),      # 256-row chunks: 256 x 256 tiles
+    (2, 2, 384, 256, 264, 0),      # 384-row chunks: 128 x 128 tiles, ragged N
+    (8, 16, 256, 200, 520, 5),     # two chunks per rank, ragged K and N
+    (3, 3, 512, 1024, 1024, 2),    # odd TP degree
+]
+
+
+@pytest.mark.parametrize("tp,n_chunks,rows,K,N,rank", STAGED_CASES)
+def test_agmm_staged_parity_and_cross_path_bits(env, tp, n_chunks, rows, K, N, rank):
+    """The staged path matches the oracle and the per-chunk event path bit for bit."""
+    torch, sptl, ctx = env
+    seed = 300 + rows + N
+    shards_b = [gen(seed, (0, q), rows, K) for q in range(tp)]
+    w_b = gen(seed, (1,), K, N, 1.0 / K)
+    M = tp * rows
+    shards = [to_dev(b) for b in shards_b]
+    w = to_dev(w_b)
+    xg = torch.full((M, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    sptl.agmm_chunked(shards, xg, w, y, n_chunks=n_chunks, rank=rank, ctx=ctx)
+    ctx.check()
+    torch.cuda.synchronize()
+    _, y_want = O.agmm(shards_b, w_b)
+    assert np.array_equal(to_bits(xg), np.concatenate(shards_b))
+    assert_within(y.cpu().numpy().astype(np.float64), y_want, fp32_tol(y_want), "staged y")
+    # per-chunk event path (a caller-supplied copy stream selects it)
+    xg2 = torch.full((M, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y)
+    side = torch.cuda.Stream()
+    sptl.agmm_chunked(shards, xg2, w, y2, n_chunks=n_chunks, rank=rank, ctx=ctx, copy=side)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
+def test_agmm_staged_no_stale_data(env):
+    """Gathered rows cached by earlier reads, and a previous call's data, are never used."""
+    torch, sptl, ctx = env
+    tp, rows, K, N = 4, 512, 512, 512
+    M = tp * rows
+    w_b = gen(41, (1,), K, N, 1.0 / K)
+    w = to_dev(w_b)
+    xg = torch.full((M, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    junk = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    sptl.gemm_partial(xg, w, junk, ctx=ctx)  # pulls the poisoned rows through the caches
+    for trial in range(3):
+        shards_b = [gen(42 + trial, (0, q), rows, K) for q in range(tp)]
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        sptl.agmm_chunked([to_dev(b) for b in shards_b], xg, w, y, n_chunks=tp, rank=trial % tp, ctx=ctx)
+        torch.cuda.synchronize()
+        ctx.check()
+        _, y_want = O.agmm(shards_b, w_b)
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all(), f"trial {trial}: stale poisoned rows were read"
+        assert_within(got, y_want, fp32_tol(y_want), f"trial {trial}")
+
+
+def test_agmm_staged_back_to_back_calls(env):
+    """More calls in flight than completion-signal sets: each call still sees its own data."""
+    torch, sptl, ctx = env
+    tp, rows, K, N = 2, 256, 256, 256
+    M = tp * rows
+    w_b = gen(51, (1,), K, N, 1.0 / K)
+    w = to_dev(w_b)
+    outs, wants = [], []
+    for i in range(9):
+        shards_b = [gen(60 + i, (0, q), rows, K) for q in range(tp)]
+        xg = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        sptl.agmm_chunked([to_dev(b) for b in shards_b], xg, w, y, n_chunks=tp, rank=0, ctx=ctx)
+        outs.append(y)
+        wants.append(O.agmm(shards_b, w_b)[1])
+    torch.cuda.synchronize()
+    ctx.check()
+    for i, (y, want) in enumerate(zip(outs, wants)):
+        assert_within(y.cpu().numpy().astype(np.float64), want, fp32_tol(want), f"call {i}")
