@@ -3,19 +3,21 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input, inputs resident
 in HBM:
-  1. agmm_chunked        sequence all-gather (SDMA chunk staging on a side stream) overlapped
-                         with the column-parallel chunk GEMMs (bf16 MFMA, fp32 accumulate);
+  1. agmm_chunked        sequence all-gather staged by the SDMA copy engines (striped over
+                         all engines, released at the call's fork point) overlapped with one
+                         chunk-ordered column-parallel GEMM launch (bf16 MFMA, fp32
+                         accumulate) whose tiles wait for their chunk's completion signal;
   2. gemm_partial        row-parallel GEMM producing this rank's bf16 partial sum
                          (input = the column GEMM's bf16 output, same weight);
   3. reduce_residual_rmsnorm   own partial + the peers' partials + residual, RMSNorm;
   4. dtp_accumulate      delayed-TP update (own partial now, peers' partials of an earlier
                          module), RMSNorm.
-Per-call times come from HIP events on the compute stream; per-chunk copy/GEMM intervals
-from the library's own event timeline (the events sit on the streams the copies and the
-kernels run on).
+Per-call times come from HIP events on the compute stream that every call is issued on.
+Per-chunk landing and tile times come from the library's device timestamps (one
+instrumented call outside the timed region).
 
 Prints ONE JSON line.  `value` is the chunked AG-GEMM throughput in TFLOP/s (2*M*K*N per
-call over the call's wall time, exposed copy included).
+call over the call's event time, exposed copy included).
 """
 from __future__ import annotations
 
@@ -47,6 +49,60 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("sp_transformer_linear_amd/csrc/sptl_gemm.hip", "sp_transformer_linear_amd/csrc/sptl_internal.h")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch from the committed counter runs, or None if absent or stale.
+
+    profiles/traffic.json holds, per kernel and workload, FETCH_SIZE + WRITE_SIZE per launch
+    scaled by the counters' reading for a plain copy kernel of known size, together with
+    the hash of the kernel sources it was measured on; a changed kernel reads as None.
+    """
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            entry = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("source_sha256") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def interval_hidden_fraction(tl):
+    """Share of the staging time during which chunk GEMM tiles were running.
+
+    tl rows are [copy queued, chunk landed, first tile start, last tile end] (ms) per chunk,
+    own chunks with -1 copy times.  The engines take the peers' chunks in landing order, so
+    chunk c is taken to be in flight from the previous peer chunk's landing (0 for the first)
+    to its own.  Returns sum_c |copy_c intersect union_g gemm_g| / sum_c |copy_c|.
+    """
+    gemm = sorted((r[2], r[3]) for r in tl)
+    merged = []
+    for a, b in gemm:
+        if merged and a <= merged[-1][1]:
+            merged[-1][1] = max(merged[-1][1], b)
+        else:
+            merged.append([a, b])
+    landed = sorted(r[1] for r in tl if r[1] >= 0)
+    total = covered = 0.0
+    prev = 0.0
+    for t in landed:
+        total += t - prev
+        covered += sum(max(0.0, min(t, b) - max(prev, a)) for a, b in merged)
+        prev = t
+    return None if total <= 0 else covered / total
 
 
 def cpu_baseline(wl, budget_s):
@@ -213,18 +269,28 @@ def main():
     # the same GEMM on already-gathered rows (no staging)
     y_tmp = torch.empty_like(y_col)
     t_gemm = timed(lambda: sptl.gemm_partial(xg, w_col, y_tmp, stream=cs, ctx=ctx), reps)
-    # the same staging with an 8-column weight: the GEMM is negligible, the copies are identical
+    # Staging alone: the same copies with an 8-column weight.  Its workgroups (one column
+    # tile per row tile) are all resident from the start, so the time the first of them sees
+    # a chunk's completion signal is when that chunk landed; the peers' last landing time,
+    # from the kernel's start, is the staging time.  (The call's own duration is not: each
+    # tile still walks the whole K.)
     w_thin = torch.zeros((K, 8), dtype=torch.bfloat16, device=dev)
     y_thin = torch.empty((M, 8), dtype=torch.bfloat16, device=dev)
-    t_copy = timed(lambda: agmm(w_thin, y_thin), reps)
+    copy_runs = []
+    for _ in range(reps):
+        agmm(w_thin, y_thin, timing=True)
+        copy_runs.append(max(r[1] for r in ctx.timeline(wl.n_chunks)))
+    ctx.check()
+    t_copy = float(np.median(copy_runs))
     t_agmm = float(agmm_ms.mean())
     exposed = max(0.0, t_agmm - t_gemm)
-    hidden_frac = None if t_copy <= 0 else max(0.0, 1.0 - exposed / t_copy)
+    hidden_cross = None if t_copy <= 0 else max(0.0, 1.0 - exposed / t_copy)
     staged_bytes = (wl.tp - 1) * (M // wl.tp) * K * 2
     # per-chunk timeline of one instrumented call
     agmm(w_col, y_col, timing=True)
     tl = ctx.timeline(wl.n_chunks)
     ctx.check()
+    hidden_iv = interval_hidden_fraction(tl)
 
     P = wl.P
     red_bytes = (P + 1) * M * wl.H * 2 + 2 * M * wl.H * 2 + wl.H * 2
@@ -260,7 +326,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(agmm_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(f"agmm_chunk_ordered_gemm/{wl.name}"),
             "launch_flop": agmm_flops,
             "avg_launch_us": round(t_agmm * 1e3, 2),
         },
@@ -269,10 +335,12 @@ def main():
             "ms": round(t_agmm, 4),
             "gemm_prestaged_ms": round(t_gemm, 4),
             "gemm_prestaged_tflops": round(agmm_flops / (t_gemm * 1e-3) / 1e12, 2),
+            "ms_median": round(float(np.median(agmm_ms)), 4), "ms_min": round(float(agmm_ms.min()), 4),
             "copy_alone_ms": round(t_copy, 4),
             "copy_alone_GBps": round(staged_bytes / (t_copy * 1e-3) / 1e9, 1),
             "copy_exposed_ms": round(exposed, 4),
-            "copy_hidden_frac": None if hidden_frac is None else round(hidden_frac, 4),
+            "copy_hidden_frac": None if hidden_iv is None else round(hidden_iv, 4),
+            "copy_hidden_frac_crosscheck": None if hidden_cross is None else round(hidden_cross, 4),
             "chunk_ready_ms": [round(r[1], 4) for r in tl],
             "chunk_gemm_ms": [[round(r[2], 4), round(r[3], 4)] for r in tl],
         },

@@ -66,16 +66,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // Bounded spin until *word <= 0 (an SDMA completion signal counting down copy pieces).  On
 // timeout sets *plan.err and returns, so every wave exits.
+// The polls are relaxed (a coherent load that bypasses the caches, no cache invalidation);
+// one acquire fence follows the last poll, so a waiting workgroup does not invalidate its
+// L2 once per poll while the other workgroups on that XCD are streaming tiles through it.
 __device__ __forceinline__ void wait_ready(const int64_t *word, const ChunkPlan &plan) {
     if (!word) return;
     const uint64_t t0 = wall_clock64();
-    while (__hip_atomic_load(word, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) > 0) {
+    while (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) > 0) {
         if (wall_clock64() - t0 > plan.timeout_ticks) {
             __hip_atomic_store(plan.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            return;
+            break;
         }
         __builtin_amdgcn_s_sleep(32);
     }
+    __atomic_thread_fence(__ATOMIC_ACQUIRE);  // system scope: the copied rows are visible
 }
 
 template <int BM, int BN, int WGM, int WGN>
@@ -345,16 +349,20 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
 }
 
 // Tile configurations.  All share the MFMA instruction and the K order.
-enum Config { k256x256w2x2, k256x256w2x4, k256x256w4x2, k128x128w2x2, kNumConfigs };
+enum Config { k256x256w2x2, k256x256w2x4, k256x256w4x2, k256x128w4x2, k256x128w4x1, k128x128w2x2, kNumConfigs };
 
 const char *config_name(int c) {
     switch (c) {
         case k256x256w2x2: return "256x256w2x2";
         case k256x256w2x4: return "256x256w2x4";
         case k256x256w4x2: return "256x256w4x2";
+        case k256x128w4x2: return "256x128w4x2";
+        case k256x128w4x1: return "256x128w4x1";
         default: return "128x128w2x2";
     }
 }
+
+int config_rows(int c) { return c == k128x128w2x2 ? 128 : 256; }
 
 // SPTL_GEMM_CFG=<name> forces one configuration for every GEMM (measurement aid).
 int forced_config() {
@@ -370,7 +378,7 @@ int forced_config() {
 
 int resolve(const GemmProblem &p, GemmTile t) {
     if (p.plan.chunk_rows) {  // chunk-ordered: the tile height must divide the chunk
-        if (p.plan.chunk_rows % 256 == 0 && forced_config() >= 0 && forced_config() != k128x128w2x2)
+        if (forced_config() >= 0 && p.plan.chunk_rows % config_rows(forced_config()) == 0)
             return forced_config();
         return p.plan.chunk_rows % 256 == 0 ? k256x256w4x2 : k128x128w2x2;
     }
@@ -402,6 +410,8 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile) 
         case k256x256w2x2: return launch_cfg<256, 256, 2, 2>(p, stream);
         case k256x256w2x4: return launch_cfg<256, 256, 2, 4>(p, stream);
         case k256x256w4x2: return launch_cfg<256, 256, 4, 2>(p, stream);
+        case k256x128w4x2: return launch_cfg<256, 128, 4, 2>(p, stream);
+        case k256x128w4x1: return launch_cfg<256, 128, 4, 1>(p, stream);
         default: return launch_cfg<128, 128, 2, 2>(p, stream);
     }
 }

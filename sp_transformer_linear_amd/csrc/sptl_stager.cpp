@@ -214,6 +214,11 @@ SdmaStager *stager_create(int device, std::string *err) {
         }
         if (hsa_signal_load_scacquire(probe) < 1) hsa_signal_destroy(probe);  // else leak it safely
     }
+    // tuning knob: SPTL_SDMA_ENGINES=n keeps only the first n working engines
+    if (const char *e = getenv("SPTL_SDMA_ENGINES")) {
+        const long n = strtol(e, nullptr, 10);
+        if (n > 0 && (size_t)n < s->engines.size()) s->engines.resize((size_t)n);
+    }
     if (s->engines.empty()) {
         *err = "no SDMA engine completed a device-to-device check copy";
         stager_destroy(s);
@@ -247,7 +252,8 @@ SdmaStager *stager_create(int device, std::string *err) {
             }
             ss.val[c] = (int64_t *)vp;
         }
-        if (ok && (hipEventCreate(&ss.fork) != hipSuccess || hipEventCreate(&ss.done) != hipSuccess)) {
+        if (ok && (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+                   hipEventCreateWithFlags(&ss.done, hipEventDisableTiming) != hipSuccess)) {
             why = "hipEventCreate failed";
             ok = false;
         }
@@ -295,9 +301,15 @@ int stager_wait_idle(SdmaStager *s) {
 
 std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies) {
     std::vector<CopyPiece> out;
-    const size_t E = s->engines.size();
+    // tuning knob: SPTL_SDMA_SPLIT=p stripes a chunk into up to p pieces per engine
+    static const size_t split = [] {
+        const char *e = getenv("SPTL_SDMA_SPLIT");
+        const long v = e ? strtol(e, nullptr, 10) : 1;
+        return (size_t)(v >= 1 && v <= 16 ? v : 1);
+    }();
+    const size_t E = s->engines.size() * split;
     for (const CopyPiece &c : copies) {
-        size_t n = c.bytes / kMinPiece;
+        size_t n = c.bytes / (kMinPiece / split);
         n = n < 1 ? 1 : n > E ? E : n;
         // equal pieces rounded to 256 bytes; the last takes the remainder
         const size_t step = ((c.bytes / n) + 255) & ~(size_t)255;
