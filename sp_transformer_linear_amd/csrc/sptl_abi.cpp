@@ -24,6 +24,8 @@ struct sptl_ctx {
     std::string staging_info;           // how agmm_chunked stages chunks, and why
     int *err_dev = nullptr;             // device flag set by a timed-out staging wait
     uint64_t *ts_dev = nullptr;         // [3 * kMaxPlanChunks + 1] chunk timestamps
+    uint64_t *flags_dev = nullptr;      // landed flags, kFlagSetWords per stager set
+    uint64_t epoch[sptl::kStageSets] = {};  // last epoch used per stager set
     int wallclock_khz = 100000;
     int t_mode = 0;                     // 0: event timeline, 1: chunk-ordered timeline
     int t_rank_first = 0, t_rank_count = 0;
@@ -112,7 +114,12 @@ int create_ctx(sptl_ctx **out, int device) {
     if (!rc && hipMalloc(&c->err_dev, 256) != hipSuccess) rc = fail(SPTL_E_HIP, "hipMalloc of the error flag failed");
     if (!rc && hipMalloc(&c->ts_dev, sizeof(uint64_t) * (3 * sptl::kMaxPlanChunks + 8)) != hipSuccess)
         rc = fail(SPTL_E_HIP, "hipMalloc of the timestamp buffer failed");
-    if (!rc && hipMemset(c->err_dev, 0, 256) != hipSuccess) rc = fail(SPTL_E_HIP, "hipMemset failed");
+    if (!rc && hipMalloc(&c->flags_dev, sizeof(uint64_t) * sptl::kFlagSetWords * sptl::kStageSets) != hipSuccess)
+        rc = fail(SPTL_E_HIP, "hipMalloc of the landed flags failed");
+    if (!rc && (hipMemset(c->err_dev, 0, 256) != hipSuccess ||
+                hipMemset(c->flags_dev, 0, sizeof(uint64_t) * sptl::kFlagSetWords * sptl::kStageSets) != hipSuccess ||
+                hipDeviceSynchronize() != hipSuccess))
+        rc = fail(SPTL_E_HIP, "hipMemset failed");
     if (!rc) {
         (void)hipDeviceGetAttribute(&c->wallclock_khz, hipDeviceAttributeWallClockRate, device);
         if (c->wallclock_khz <= 0) c->wallclock_khz = 100000;
@@ -242,6 +249,15 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     plan.own_a = static_cast<const uint16_t *>(shard_src[rank]);
     plan.err = ctx->err_dev;
     plan.timeout_ticks = (uint64_t)ctx->wallclock_khz * 10000u;  // 10 s
+    static const int poll_sleep = [] {
+        const char *e = getenv("SPTL_POLL_SLEEP");
+        const long v = e ? strtol(e, nullptr, 10) : 0;
+        return (int)(v >= 0 && v <= 64 ? v : 0);
+    }();
+    plan.poll_sleep = poll_sleep;
+    if (call.set < 0 || call.set >= sptl::kStageSets) return fail(SPTL_E_HIP, "agmm_chunked: bad stager set");
+    plan.flags = ctx->flags_dev + (size_t)call.set * sptl::kFlagSetWords;
+    plan.epoch = ++ctx->epoch[call.set];
     plan.ts = timing ? ctx->ts_dev : nullptr;
     SPTL_HIP(sptl::launch_gemm(gp, cs));
     SPTL_HIP(hipEventRecord(call.done, cs));
@@ -301,6 +317,7 @@ int sptl_destroy(sptl_ctx *ctx) {
     if (ctx->stager) sptl::stager_destroy(ctx->stager);
     if (ctx->err_dev) (void)hipFree(ctx->err_dev);
     if (ctx->ts_dev) (void)hipFree(ctx->ts_dev);
+    if (ctx->flags_dev) (void)hipFree(ctx->flags_dev);
     if (ctx->copy_stream) {
         (void)hipStreamSynchronize(ctx->copy_stream);
         (void)hipStreamDestroy(ctx->copy_stream);

@@ -65,21 +65,53 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // Bounded spin until *word <= 0 (an SDMA completion signal counting down copy pieces).  On
-// timeout sets *plan.err and returns, so every wave exits.
-// The polls are relaxed (a coherent load that bypasses the caches, no cache invalidation);
-// one acquire fence follows the last poll, so a waiting workgroup does not invalidate its
-// L2 once per poll while the other workgroups on that XCD are streaming tiles through it.
+// timeout sets *plan.err and returns, so every wave exits.  The polls are relaxed (coherent
+// loads that bypass the caches, no cache invalidation); one acquire fence follows the last
+// poll, so a waiting workgroup does not invalidate its L2 while others stream through it.
+__device__ __forceinline__ bool timed_out(uint64_t t0, const ChunkPlan &plan) {
+    if (wall_clock64() - t0 <= plan.timeout_ticks) return false;
+    __hip_atomic_store(plan.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return true;
+}
+
+__device__ __forceinline__ void poll_pause(const ChunkPlan &plan) {
+    __builtin_amdgcn_s_sleep(32);
+    for (int i = 0; i < plan.poll_sleep; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 __device__ __forceinline__ void wait_ready(const int64_t *word, const ChunkPlan &plan) {
     if (!word) return;
     const uint64_t t0 = wall_clock64();
     while (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) > 0) {
-        if (wall_clock64() - t0 > plan.timeout_ticks) {
-            __hip_atomic_store(plan.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(32);
+        if (timed_out(t0, plan)) break;
+        poll_pause(plan);
     }
     __atomic_thread_fence(__ATOMIC_ACQUIRE);  // system scope: the copied rows are visible
+}
+
+// Wait of workgroup `bid` for chunk `chunk` through the replicated landed flags (see
+// ChunkPlan); falls back to wait_ready when the launch has no flags.
+constexpr unsigned kSignalPollEvery = 16;
+
+__device__ __forceinline__ void wait_chunk(const ChunkPlan &plan, int chunk, int bid) {
+    const int64_t *word = plan.ready[chunk];
+    if (!word) return;
+    if (!plan.flags) return wait_ready(word, plan);
+    uint64_t *mine = plan.flags + (size_t)(bid % kFlagReplicas) * kFlagStride + chunk;
+    const uint64_t t0 = wall_clock64();
+    for (unsigned it = (unsigned)bid;; ++it) {
+        if (__hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == plan.epoch) break;
+        if (it % kSignalPollEvery == 0 && __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) <= 0) {
+            __atomic_thread_fence(__ATOMIC_ACQ_REL);  // the flags are set after the landing was seen
+            for (int r = 0; r < kFlagReplicas; ++r)
+                __hip_atomic_store(plan.flags + (size_t)r * kFlagStride + chunk, plan.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+            break;
+        }
+        if (timed_out(t0, plan)) break;
+        poll_pause(plan);
+    }
+    __atomic_thread_fence(__ATOMIC_ACQUIRE);
 }
 
 template <int BM, int BN, int WGM, int WGN>
@@ -144,7 +176,7 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
                      : p.a + m0 * p.lda;
         if (plan.ts && bid == 0 && tid == 0) plan.ts[3 * plan.n_chunks] = wall_clock64();
         if (tid == 0) {
-            wait_ready(plan.ready[chunk], plan);  // this chunk's copy pieces have landed
+            wait_chunk(plan, chunk, bid);  // this chunk's copy pieces have landed
             if (plan.ts) {
                 const unsigned long long now = wall_clock64();
                 atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + chunk), now);

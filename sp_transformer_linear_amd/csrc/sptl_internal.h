@@ -9,6 +9,12 @@ namespace sptl {
 
 constexpr int kMaxPlanChunks = 64;  // chunks of one chunk-ordered GEMM launch
 
+// Landed flags of a chunk-ordered launch: kFlagReplicas copies per chunk, 4 KiB apart so that
+// they fall on different memory channels; replica r of chunk c is word r * kFlagStride + c.
+constexpr int kFlagReplicas = 16;
+constexpr int kFlagStride = 512;                                   // 64-bit words
+constexpr size_t kFlagSetWords = (size_t)kFlagReplicas * kFlagStride;
+
 // Chunk-ordered GEMM over a gathered activation (the column GEMM of the chunked all-gather +
 // matmul).  Row tiles are processed in `order` (own chunks first, then the peers' chunks in
 // arrival order); the workgroups of a tile of chunk c wait, with a bounded spin, until
@@ -25,8 +31,16 @@ struct ChunkPlan {
     const uint16_t *own_a;
     int *err;                                // set to 1 when a wait times out
     uint64_t timeout_ticks;                  // wall-clock ticks of the bounded waits
+    int poll_sleep;                          // extra s_sleep 127 per poll (0: ~1 us between polls)
+    uint64_t *flags;                         // landed flags (kFlagSetWords words), or nullptr
+    uint64_t epoch;                          // value a landed flag holds for this launch
     uint64_t *ts;                            // optional per-chunk timestamps (see below)
 };
+// Waiting: a workgroup of chunk c polls its replica of c's landed flag about every
+// microsecond and, once every 16 polls (phase set by its index), c's completion word itself.
+// The first workgroup to see the word reach zero sets every replica to `epoch`.  Spreading
+// the polls over replicas keeps a few hundred waiting workgroups from hammering the one
+// memory line the copy engines update.
 // ts layout (wall-clock ticks, n = n_chunks): ts[c] = first time a tile of chunk c found it
 // ready (min), ts[n + c] = first tile start of chunk c (min), ts[2 n + c] = last tile end of
 // chunk c (max), ts[3 n] = start of workgroup 0.

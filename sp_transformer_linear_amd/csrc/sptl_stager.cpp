@@ -33,7 +33,7 @@
 namespace sptl {
 
 namespace {
-constexpr int kSets = 4;
+constexpr int kSets = kStageSets;
 constexpr size_t kMinPiece = 512 * 1024;  // below this, striping costs more than it gains
 
 struct FindAgent {

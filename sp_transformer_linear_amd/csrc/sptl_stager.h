@@ -21,11 +21,12 @@ struct CopyPiece {
     int chunk;
 };
 constexpr int kJoinChunk = kMaxPlanChunks;
+constexpr int kStageSets = 4;  // calls that can be in flight on one stager
 
 // Device-side view of one call's completion words: ready[c] reaches <= 0 once every piece of
 // chunk c has landed; join likewise for the kJoinChunk pieces.
 struct StageCall {
-    int set = -1;
+    int set = -1;               // in [0, kStageSets)
     const int64_t *ready[kMaxPlanChunks] = {};
     const int64_t *join = nullptr;
     hipEvent_t fork = nullptr;  // record on the compute stream before the consuming GEMM
