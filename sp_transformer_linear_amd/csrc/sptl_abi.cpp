@@ -25,11 +25,11 @@ struct sptl_ctx {
     int *err_dev = nullptr;             // device flag set by a timed-out staging wait
     uint64_t *ts_dev = nullptr;         // [3 * kMaxPlanChunks + 1] chunk timestamps
     uint64_t *flags_dev = nullptr;      // landed flags, kFlagSetWords per stager set
-    uint64_t epoch[sptl::kStageSets] = {};  // last epoch used per stager set
     int wallclock_khz = 100000;
     int t_mode = 0;                     // 0: event timeline, 1: chunk-ordered timeline
     int t_rank_first = 0, t_rank_count = 0;
-    hipEvent_t t_done = nullptr;        // end of the last timed chunk-ordered call
+    int t_set = -1;                     // stager set and epoch of the last timed chunk-ordered call
+    uint64_t t_epoch = 0;
     hipStream_t copy_stream = nullptr;  // created on first use
     hipEvent_t fork = nullptr;          // compute stream -> copy stream
     hipEvent_t join = nullptr;          // copy stream -> compute stream
@@ -218,17 +218,7 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     if (!own_aliased)
         copies.push_back({xg + (size_t)rank * cpr * chunk_elems, shard_src[rank], chunk_bytes * cpr, sptl::kJoinChunk});
     std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies);
-    sptl::StageCall call;
-    std::string why;
-    if (sptl::stager_begin(ctx->stager, pieces, &call, &why))
-        return fail(SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
-
     const int n = n_chunks;
-    if (timing) {
-        SPTL_HIP(sptl::launch_fill_u64(ctx->ts_dev, 2 * n, ~0ull, cs));
-        SPTL_HIP(sptl::launch_fill_u64(ctx->ts_dev + 2 * n, n + 1, 0ull, cs));
-    }
-    SPTL_HIP(hipEventRecord(call.fork, cs));
     gp.a = xg;
     gp.b = static_cast<const uint16_t *>(w);
     gp.c = y;
@@ -243,9 +233,6 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     plan.n_chunks = n;
     plan.own_first = rank * cpr;
     plan.own_count = cpr;
-    for (int c = 0; c < n; ++c) plan.ready[c] = call.ready[c];
-    for (int s = 0; s < cpr; ++s) plan.ready[rank * cpr + s] = nullptr;  // read from the source
-    plan.join = call.join;
     plan.own_a = static_cast<const uint16_t *>(shard_src[rank]);
     plan.err = ctx->err_dev;
     plan.timeout_ticks = (uint64_t)ctx->wallclock_khz * 10000u;  // 10 s
@@ -255,18 +242,38 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
         return (int)(v >= 0 && v <= 64 ? v : 0);
     }();
     plan.poll_sleep = poll_sleep;
-    if (call.set < 0 || call.set >= sptl::kStageSets) return fail(SPTL_E_HIP, "agmm_chunked: bad stager set");
-    plan.flags = ctx->flags_dev + (size_t)call.set * sptl::kFlagSetWords;
-    plan.epoch = ++ctx->epoch[call.set];
     plan.ts = timing ? ctx->ts_dev : nullptr;
-    SPTL_HIP(sptl::launch_gemm(gp, cs));
-    SPTL_HIP(hipEventRecord(call.done, cs));
+
+    sptl::StageCall call;
+    std::string why;
+    if (sptl::stager_begin(ctx->stager, pieces, sptl::gemm_workgroups(gp), &call, &why))
+        return fail(SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
+    for (int c = 0; c < n; ++c) plan.ready[c] = call.ready[c];
+    for (int s = 0; s < cpr; ++s) plan.ready[rank * cpr + s] = nullptr;  // read from the source
+    plan.join = call.join;
+    plan.flags = ctx->flags_dev + (size_t)call.set * sptl::kFlagSetWords;
+    plan.epoch = call.epoch;
+    plan.finished = call.finished;
+    plan.wg_count = call.wg_count;
+    plan.wg_last = call.wg_last;
+    hipError_t he = hipSuccess;
+    if (timing) {
+        he = sptl::launch_fill_u64(ctx->ts_dev, 2 * n, ~0ull, cs);
+        if (he == hipSuccess) he = sptl::launch_fill_u64(ctx->ts_dev + 2 * n, n + 1, 0ull, cs);
+    }
+    if (he == hipSuccess) he = hipEventRecord(call.fork, cs);
+    if (he == hipSuccess) he = sptl::launch_gemm(gp, cs);
+    if (he != hipSuccess) {
+        sptl::stager_cancel(ctx->stager, call);
+        return hip_fail(he, "agmm_chunked: kernel launch");
+    }
     if (sptl::stager_submit(ctx->stager, call, std::move(pieces), &why))
         return fail(SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
     if (timing) {
         ctx->t_mode = 1;
         ctx->t_chunks = n;
-        ctx->t_done = call.done;
+        ctx->t_set = call.set;
+        ctx->t_epoch = call.epoch;
         ctx->t_rank_first = rank * cpr;
         ctx->t_rank_count = cpr;
     }
@@ -478,7 +485,8 @@ int sptl_agmm_timeline(sptl_ctx *ctx, double *out, int n_chunks) {
         // chunk-ordered call: timestamps taken by the GEMM's workgroups (wall clock)
         const int n = n_chunks;
         std::vector<uint64_t> ts(3 * n + 1);
-        SPTL_HIP(hipEventSynchronize(ctx->t_done));
+        if (!ctx->stager || sptl::stager_wait_call(ctx->stager, ctx->t_set, ctx->t_epoch))
+            return fail(SPTL_E_HIP, "sptl_agmm_timeline: the timed call did not finish");
         SPTL_HIP(hipMemcpy(ts.data(), ctx->ts_dev, ts.size() * sizeof(uint64_t), hipMemcpyDeviceToHost));
         const double per_ms = (double)ctx->wallclock_khz;
         const uint64_t t0 = ts[3 * n];

@@ -350,8 +350,14 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         if (plan.ts)
             atomicMax(reinterpret_cast<unsigned long long *>(plan.ts + 2 * plan.n_chunks + chunk),
                       (unsigned long long)wall_clock64());
-        // the kernel ends only once every copy of the call has landed (own slot included)
-        if (blockIdx.x == gridDim.x - 1) wait_ready(plan.join, plan);
+        // The last workgroup to finish waits for every copy of the call (own slot included),
+        // so the kernel ends only after all of them, then reports the call done.
+        const uint64_t done_before =
+            __hip_atomic_fetch_add(plan.wg_count, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (done_before == plan.wg_last) {
+            wait_ready(plan.join, plan);
+            __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
     }
 #endif
 }
@@ -435,6 +441,12 @@ hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t strea
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n, v);
     return hipGetLastError();
+}
+
+int64_t gemm_workgroups(const GemmProblem &p, GemmTile tile) {
+    const int c = resolve(p, tile);
+    const int64_t bm = config_rows(c), bn = (c == k256x128w4x2 || c == k256x128w4x1 || c == k128x128w2x2) ? 128 : 256;
+    return ((p.m + bm - 1) / bm) * ((p.n + bn - 1) / bn);
 }
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile) {

@@ -27,13 +27,16 @@ struct ChunkPlan {
     int own_first, own_count;
     int order[kMaxPlanChunks];               // processing position -> chunk
     const int64_t *ready[kMaxPlanChunks];    // per chunk; nullptr: no wait
-    const int64_t *join;                     // waited for by the last workgroup before it exits
+    const int64_t *join;                     // waited for by the last workgroup to finish
     const uint16_t *own_a;
     int *err;                                // set to 1 when a wait times out
     uint64_t timeout_ticks;                  // wall-clock ticks of the bounded waits
     int poll_sleep;                          // extra s_sleep 127 per poll (0: ~1 us between polls)
     uint64_t *flags;                         // landed flags (kFlagSetWords words), or nullptr
     uint64_t epoch;                          // value a landed flag holds for this launch
+    uint64_t *finished;                      // pinned host word: epoch once the launch is done
+    uint64_t *wg_count;                      // finished-workgroup counter of the signal set
+    uint64_t wg_last;                        // counter value seen by this launch's last workgroup
     uint64_t *ts;                            // optional per-chunk timestamps (see below)
 };
 // Waiting: a workgroup of chunk c polls its replica of c's landed flag about every
@@ -41,6 +44,8 @@ struct ChunkPlan {
 // The first workgroup to see the word reach zero sets every replica to `epoch`.  Spreading
 // the polls over replicas keeps a few hundred waiting workgroups from hammering the one
 // memory line the copy engines update.
+// End: every workgroup counts itself in *wg_count when done, and the one that sees wg_last
+// waits for the join, then stores epoch to *finished.
 // ts layout (wall-clock ticks, n = n_chunks): ts[c] = first time a tile of chunk c found it
 // ready (min), ts[n + c] = first tile start of chunk c (min), ts[2 n + c] = last tile end of
 // chunk c (max), ts[3 n] = start of workgroup 0.
@@ -64,6 +69,9 @@ enum class GemmTile { T256x256, T128x128, Auto };
 // Picks a tile shape for the problem (Auto) and launches.  Returns the HIP error of the
 // launch.
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile = GemmTile::Auto);
+
+// Workgroups launch_gemm(p, stream, tile) launches.
+int64_t gemm_workgroups(const GemmProblem &p, GemmTile tile = GemmTile::Auto);
 
 // Tile height a chunk-ordered launch of `p` would use (0: chunk_rows fits no tile height).
 int chunk_tile_rows(int64_t chunk_rows);

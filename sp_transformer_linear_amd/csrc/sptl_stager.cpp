@@ -9,13 +9,17 @@
 // polls them.
 //
 // Ordering: copies must not overwrite the gathered buffer while earlier work on the compute
-// stream still reads it.  A HIP event recorded at the call's fork point is waited for by a
-// worker thread (interrupt-driven), which then submits the pieces with no HSA dependencies.
-// (A dependency on a signal written by a kernel is resolved by the runtime's host thread
-// with millisecond latency, because a kernel store raises no interrupt.)
+// stream still reads it.  A HIP event recorded at the call's fork point (right before the
+// consuming kernel) is waited for by a worker thread, which then submits the pieces with no
+// HSA dependencies.  The event's completion is signalled by the command processor, so the
+// copies start while the kernel is being dispatched; a store from the kernel itself would
+// queue behind the kernel's own memory traffic.  (A dependency on a signal written by a
+// kernel is resolved by the runtime's host thread with millisecond latency, because a
+// kernel store raises no interrupt.)
 //
-// Reuse: completion-signal sets form a ring; a set is re-armed only after the GEMM that
-// waited on it has completed (its `done` event), by which point all of its pieces landed.
+// Reuse: completion-signal sets form a ring; a set is re-armed only after the kernel that
+// waited on it has reported its end through a pinned host word (by then all of the set's
+// pieces have landed).  No marker follows the kernel on the stream.
 #include "sptl_stager.h"
 
 #include <hsa/hsa.h>
@@ -60,11 +64,18 @@ hsa_status_t find_agent(hsa_agent_t a, void *data) {
 }
 }  // namespace
 
+// Pinned host words: set s finished at word 16 * s (one 128-byte line each).  Device
+// counters: finished workgroups of set s at word 32 * s.
+constexpr int kHostWords = 16 * kStageSets;
+constexpr int kCountWords = 32 * kStageSets;
+constexpr double kReuseWaitSeconds = 30.0;  // longest a call waits for a set to come free
+
 struct SignalSet {
     hsa_signal_t sig[kMaxPlanChunks + 1] = {};
     int64_t *val[kMaxPlanChunks + 1] = {};
-    hipEvent_t fork = nullptr, done = nullptr;
-    bool used = false;
+    hipEvent_t fork = nullptr;
+    uint64_t epoch = 0;       // of the last call begun on the set (0: never used)
+    uint64_t wg_total = 0;    // workgroups of all calls begun on the set
 };
 
 struct Job {
@@ -73,6 +84,19 @@ struct Job {
     std::vector<CopyPiece> pieces;
 };
 
+// Spins (with pauses, yielding now and then) until *word == value; false after `seconds`.
+bool spin_until(const volatile uint64_t *word, uint64_t value, double seconds) {
+    const auto t0 = std::chrono::steady_clock::now();
+    for (unsigned i = 1;; ++i) {
+        if (__atomic_load_n(word, __ATOMIC_ACQUIRE) == value) return true;
+        __builtin_ia32_pause();
+        if ((i & 1023) == 0) {
+            if (std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count() > seconds) return false;
+            std::this_thread::yield();
+        }
+    }
+}
+
 class SdmaStager {
   public:
     int device = 0;
@@ -80,7 +104,7 @@ class SdmaStager {
     std::vector<uint32_t> engines;  // hsa_amd_sdma_engine_id_t bits
     SignalSet sets[kSets];
     int next_set = 0;
-    std::mutex mu;                  // guards next_set, sets[].used, the queue
+    std::mutex mu;                  // guards next_set and the queue
     std::condition_variable cv;
     std::deque<Job> queue;
     bool stop = false;
@@ -88,6 +112,10 @@ class SdmaStager {
     std::atomic<bool> failed{false};
     unsigned next_engine = 0;       // worker thread only
     void *scratch = nullptr;        // 8 KB for the engine checks
+    uint64_t *host_words = nullptr; // pinned, kHostWords
+    uint64_t *counts = nullptr;     // device, kCountWords
+
+    volatile uint64_t *finished(int set) const { return host_words + 16 * set; }
 
     // The fork usually completes within microseconds of the call (earlier stream work is
     // short), and a blocking event wait sleeps ~50 us before noticing: poll first, then block.
@@ -185,8 +213,12 @@ SdmaStager *stager_create(int device, std::string *err) {
     s->device = device;
     s->agent = f.agent;
     if (hipMalloc(&s->scratch, 8192) != hipSuccess || hipMemset(s->scratch, 0, 8192) != hipSuccess ||
+        hipMalloc(&s->counts, kCountWords * sizeof(uint64_t)) != hipSuccess ||
+        hipMemset(s->counts, 0, kCountWords * sizeof(uint64_t)) != hipSuccess ||
+        hipHostMalloc(&s->host_words, kHostWords * sizeof(uint64_t), hipHostMallocMapped | hipHostMallocCoherent) !=
+            hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
-        *err = "cannot allocate the engine-check buffer";
+        *err = "cannot allocate the engine-check buffer, counters or pinned progress words";
         (void)hipGetLastError();
         stager_destroy(s);
         return nullptr;
@@ -226,6 +258,17 @@ SdmaStager *stager_create(int device, std::string *err) {
     }
     bool ok = true;
     std::string why;
+    for (int i = 0; i < kHostWords; ++i) s->host_words[i] = 0;
+    {
+        // the kernels write these words through the device address of the pinned block
+        void *dp = nullptr;
+        if (hipHostGetDevicePointer(&dp, s->host_words, 0) != hipSuccess || dp != (void *)s->host_words) {
+            *err = "pinned progress words have no identical device address";
+            (void)hipGetLastError();
+            stager_destroy(s);
+            return nullptr;
+        }
+    }
     for (SignalSet &ss : s->sets) {
         for (int c = 0; c <= kMaxPlanChunks && ok; ++c) {
             hsa_status_t st = hsa_amd_signal_create(0, 0, nullptr, HSA_AMD_SIGNAL_AMD_GPU_ONLY, &ss.sig[c]);
@@ -252,8 +295,7 @@ SdmaStager *stager_create(int device, std::string *err) {
             }
             ss.val[c] = (int64_t *)vp;
         }
-        if (ok && (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-                   hipEventCreateWithFlags(&ss.done, hipEventDisableTiming) != hipSuccess)) {
+        if (ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) {
             why = "hipEventCreate failed";
             ok = false;
         }
@@ -277,14 +319,16 @@ void stager_destroy(SdmaStager *s) {
     }
     s->cv.notify_all();
     if (s->worker.joinable()) s->worker.join();
-    for (SignalSet &ss : s->sets) {
-        if (ss.used && ss.done) (void)hipEventSynchronize(ss.done);
+    for (int set = 0; set < kSets; ++set) {
+        SignalSet &ss = s->sets[set];
+        if (ss.epoch && s->host_words) (void)spin_until(s->finished(set), ss.epoch, kReuseWaitSeconds);
         for (int c = 0; c <= kMaxPlanChunks; ++c)
             if (ss.sig[c].handle) hsa_signal_destroy(ss.sig[c]);
         if (ss.fork) (void)hipEventDestroy(ss.fork);
-        if (ss.done) (void)hipEventDestroy(ss.done);
     }
     if (s->scratch) (void)hipFree(s->scratch);
+    if (s->counts) (void)hipFree(s->counts);
+    if (s->host_words) (void)hipHostFree(s->host_words);
     delete s;
     hsa_shut_down();
 }
@@ -293,9 +337,14 @@ int stager_engine_count(const SdmaStager *s) { return s ? (int)s->engines.size()
 
 bool stager_failed(const SdmaStager *s) { return s && s->failed.load(); }
 
+int stager_wait_call(SdmaStager *s, int set, uint64_t epoch) {
+    if (set < 0 || set >= kSets) return -1;
+    return spin_until(s->finished(set), epoch, kReuseWaitSeconds) ? 0 : -1;
+}
+
 int stager_wait_idle(SdmaStager *s) {
-    for (SignalSet &ss : s->sets)
-        if (ss.used && hipEventSynchronize(ss.done) != hipSuccess) return -1;
+    for (int set = 0; set < kSets; ++set)
+        if (s->sets[set].epoch && !spin_until(s->finished(set), s->sets[set].epoch, kReuseWaitSeconds)) return -1;
     return 0;
 }
 
@@ -323,7 +372,8 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
     return out;
 }
 
-int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, StageCall *out, std::string *err) {
+int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t workgroups, StageCall *out,
+                 std::string *err) {
     int set;
     {
         std::lock_guard<std::mutex> lk(s->mu);
@@ -331,19 +381,23 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, StageCall 
         s->next_set = (s->next_set + 1) % kSets;
     }
     SignalSet &ss = s->sets[set];
-    if (ss.used && hipEventSynchronize(ss.done) != hipSuccess) {
-        *err = "waiting for an earlier staged call failed";
+    if (ss.epoch && !spin_until(s->finished(set), ss.epoch, kReuseWaitSeconds)) {
+        *err = "an earlier staged call did not finish";
         return -1;
     }
     int64_t count[kMaxPlanChunks + 1] = {};
     for (const CopyPiece &p : pieces) count[p.chunk]++;
     for (int c = 0; c <= kMaxPlanChunks; ++c) hsa_signal_store_screlease(ss.sig[c], count[c]);
-    ss.used = true;
     out->set = set;
     for (int c = 0; c < kMaxPlanChunks; ++c) out->ready[c] = count[c] ? ss.val[c] : nullptr;
     out->join = count[kJoinChunk] ? ss.val[kJoinChunk] : nullptr;
+    out->epoch = ++ss.epoch;
     out->fork = ss.fork;
-    out->done = ss.done;
+    out->finished = const_cast<uint64_t *>(s->finished(set));
+    out->wg_count = s->counts + 32 * set;
+    out->wg_first = ss.wg_total;
+    out->wg_last = ss.wg_total + (uint64_t)workgroups - 1;
+    ss.wg_total += (uint64_t)workgroups;
     return 0;
 }
 
@@ -355,6 +409,12 @@ int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> p
     }
     s->cv.notify_one();
     return 0;
+}
+
+void stager_cancel(SdmaStager *s, const StageCall &call) {
+    // nothing ran on the set: mark the call finished and take back its workgroup count
+    s->sets[call.set].wg_total = call.wg_first;
+    __atomic_store_n(s->host_words + 16 * call.set, call.epoch, __ATOMIC_RELEASE);
 }
 
 }  // namespace sptl

@@ -23,14 +23,24 @@ struct CopyPiece {
 constexpr int kJoinChunk = kMaxPlanChunks;
 constexpr int kStageSets = 4;  // calls that can be in flight on one stager
 
-// Device-side view of one call's completion words: ready[c] reaches <= 0 once every piece of
-// chunk c has landed; join likewise for the kJoinChunk pieces.
+// One call's view of its completion-signal set.  ready[c] reaches <= 0 once every piece of
+// chunk c has landed; join likewise for the kJoinChunk pieces.  `fork` is recorded on the
+// compute stream right before the consuming kernel: once it completes, every earlier
+// operation on the stream has, so the copies may overwrite the gathered buffer.  The kernel
+// reports its own end through a word of pinned host memory: *wg_count counts finished
+// workgroups of all calls on the set, and the workgroup that raises it to wg_last + 1 waits
+// for the join and then stores `epoch` to *finished.  (No marker follows the kernel on the
+// stream: each marker costs several microseconds of GPU time.)
 struct StageCall {
     int set = -1;               // in [0, kStageSets)
     const int64_t *ready[kMaxPlanChunks] = {};
     const int64_t *join = nullptr;
-    hipEvent_t fork = nullptr;  // record on the compute stream before the consuming GEMM
-    hipEvent_t done = nullptr;  // record on the compute stream after it
+    hipEvent_t fork = nullptr;
+    uint64_t epoch = 0;
+    uint64_t *finished = nullptr;
+    uint64_t *wg_count = nullptr;
+    uint64_t wg_first = 0;
+    uint64_t wg_last = 0;
 };
 
 class SdmaStager;
@@ -45,16 +55,24 @@ int stager_engine_count(const SdmaStager *s);
 // stager_submit expects.
 std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies);
 
-// Reserves a completion-signal set for one call and arms it with the number of pieces per
-// chunk.  Blocks while the set's previous call is still running.
-int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, StageCall *out, std::string *err);
+// Reserves a completion-signal set for one call whose consuming kernel has `workgroups`
+// workgroups, and arms it with the number of pieces per chunk.  Blocks (bounded) while the
+// set's previous call is still running.
+int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t workgroups, StageCall *out,
+                 std::string *err);
 
 // Queues the pieces; a worker thread submits them to the engines as soon as `call.fork`
-// has completed (so the copies never overwrite data that earlier stream work still reads).
+// has completed.
 int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> pieces, std::string *err);
+
+// Gives back a set reserved by stager_begin whose kernel was never launched.
+void stager_cancel(SdmaStager *s, const StageCall &call);
 
 // True once a submission failed; the stager is then not used again.
 bool stager_failed(const SdmaStager *s);
+
+// Blocks (bounded) until the kernel of the call (set, epoch) has finished.
+int stager_wait_call(SdmaStager *s, int set, uint64_t epoch);
 
 // Blocks until every call begun on the stager has completed on the GPU.
 int stager_wait_idle(SdmaStager *s);
