@@ -19,8 +19,12 @@
  *     device pointers; the library reads them during the call only.
  *   - Streams are hipStream_t values passed as void*; NULL means the null stream.
  *   - Ownership: the caller owns every buffer and stream.  The library never allocates,
- *     frees or retains caller memory.  A context owns only HIP events and, lazily, one
- *     copy stream.  Inputs must stay valid until the stream work of the call completes.
+ *     frees or retains caller memory.  A context owns its own resources only: HIP events,
+ *     a few small device buffers (an error word, chunk timestamps, 256 KiB of landed
+ *     flags), and, from its first agmm_chunked call, a copy stream or an SDMA stager (HSA
+ *     completion signals, 4 KiB of counters, one page of pinned host memory and one worker
+ *     thread).  These are created on first use, never on later calls.  Inputs must stay
+ *     valid until the stream work of the call completes.
  *   - Every call is asynchronous (stream-ordered) and returns an sptl_status.  All
  *     arguments are validated BEFORE anything is enqueued: on any non-OK status nothing
  *     was enqueued and sptl_last_error() holds a message.  HIP failures after validation
@@ -64,13 +68,15 @@ typedef enum {
 #define SPTL_MAX_TP 64         /* TP degree of agmm_chunked and dtp_accumulate           */
 #define SPTL_MAX_CHUNKS 512    /* chunk count of agmm_chunked                            */
 
-/* Create a context on HIP device `device` (events are created now; the copy stream
- * lazily).  *out receives the context.  Returns SPTL_E_NULL if out is NULL,
- * SPTL_E_RANGE for a bad device, SPTL_E_HIP on runtime failure. */
+/* Create a context on HIP device `device` (events and small device buffers are created
+ * now; the copy stream or SDMA stager on the first agmm_chunked call).  *out receives the
+ * context.  Returns SPTL_E_NULL if out is NULL, SPTL_E_RANGE for a bad device, SPTL_E_HIP on
+ * runtime failure. */
 int sptl_create(sptl_ctx **out, int device);
 
-/* Destroy a context created by sptl_create: synchronises its copy stream, then releases
- * its events and stream.  NULL is accepted and ignored. */
+/* Destroy a context created by sptl_create: waits (bounded) for its staged calls and its copy
+ * stream, stops its worker thread, then releases everything it owns.  NULL is accepted and
+ * ignored. */
 int sptl_destroy(sptl_ctx *ctx);
 
 /* Text describing the last non-OK status returned on the calling thread ("" if none).
@@ -80,15 +86,16 @@ const char *sptl_last_error(void);
 /* ABI version (major * 100 + minor). */
 int sptl_version(void);
 
-/* Waits until every agmm_chunked call made on ctx has completed on the GPU, then reports
- * asynchronous failures recorded since the last check: SPTL_E_ASYNC if a staging wait timed
- * out (the affected call's y is invalid) or a staging copy could not be submitted (the
- * staged path is then disabled for ctx); SPTL_OK otherwise.  Clears the recorded state. */
+/* Waits (bounded, 30 s per call) until every staged agmm_chunked call made on ctx has
+ * completed on the GPU, then reports asynchronous failures recorded since the last check:
+ * SPTL_E_ASYNC if a staging wait timed out (the affected call's y is invalid; a chunk wait
+ * gives up after 10 s) or a staging copy could not be submitted (the staged path is then
+ * disabled for ctx); SPTL_OK otherwise.  Clears the recorded state. */
 int sptl_ctx_check(sptl_ctx *ctx);
 
-/* Short text naming how agmm_chunked stages chunks on ctx (copy engines driven directly with
- * a chunk-ordered GEMM, or one copy and one GEMM launch per chunk) and, for the latter, why.
- * Owned by ctx; valid until ctx is destroyed.  Diagnostic only. */
+/* Short text naming how agmm_chunked stages chunks on ctx with copy == NULL (copy engines
+ * driven directly with a chunk-ordered GEMM, or one copy and one GEMM launch per chunk) and,
+ * for the latter, why.  Owned by ctx; valid until ctx is destroyed.  Diagnostic only. */
 const char *sptl_ctx_info(sptl_ctx *ctx);
 
 /*
@@ -120,12 +127,28 @@ const char *sptl_ctx_info(sptl_ctx *ctx);
  *            fp32 accumulation in a fixed order, so every chunking gives identical bits.
  *   compute  stream that runs the GEMMs; the call is ordered after earlier work on it,
  *            and later work on it sees x_gathered and y complete.
- *   copy     stream for the staging copies; NULL = the context's own copy stream.
- *   timing   0: no timing; 1: record per-chunk copy/GEMM timestamps, read afterwards with
- *            sptl_agmm_timeline().
- * Copies: chunks of ranks rank+1, ..., rank+tp-1 (mod tp) in that order, then this rank's
- * own slot if shard_src[rank] does not alias it.  GEMMs: this rank's chunks first (read
- * straight from shard_src[rank]), then each other chunk after its copy's event.
+ *   copy     NULL: staged path (below).  Otherwise a stream for the per-chunk path.
+ *   timing   0: no timing; 1: record per-chunk landing and GEMM timestamps, read
+ *            afterwards with sptl_agmm_timeline().
+ * Staged path (copy == NULL, the default; used when the device's SDMA engines can be driven
+ * through HSA, seq_len / n_chunks is a multiple of 128 and n_chunks <= 64; else the
+ * per-chunk path runs on the context's own copy stream):
+ *   - Every peer chunk is split into pieces striped over all SDMA copy engines.  The pieces
+ *     are submitted by the context's worker thread as soon as an event recorded on
+ *     `compute` at the call's position has completed, so the copies never overwrite
+ *     x_gathered while earlier work on `compute` still reads it.  Copy order: chunks of
+ *     ranks rank+1, ..., rank+tp-1 (mod tp), then this rank's own slot unless
+ *     shard_src[rank] aliases it.
+ *   - ONE GEMM launch on `compute` processes row tiles in chunk order: this rank's chunks
+ *     first (read straight from shard_src[rank]), then the peers' chunks in copy order;
+ *     each tile waits on the GPU for its own chunk's pieces to land.  The launch ends only
+ *     after every copy of the call (own slot included) has landed.
+ *   - Up to 4 staged calls per context may be in flight; a fifth blocks the calling thread
+ *     until the oldest has finished on the GPU.
+ * Per-chunk path (copy != NULL): for each peer chunk, one SDMA-class hipMemcpyAsync on
+ * `copy` (forked from `compute`) and an event; then one GEMM launch per chunk on `compute`
+ * after that chunk's event, own chunks first; `compute` joins `copy` at the end.
+ * Both paths give bit-identical x_gathered and y.
  */
 int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
                  int tp, int n_chunks, int rank,
@@ -133,10 +156,14 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
                  void *y, int y_dtype, void *compute, void *copy, int timing);
 
 /* Per-chunk timeline of the last agmm_chunked call on ctx that had timing = 1.  Blocks
- * until that call's work is done.  out (host) receives n_chunks rows of 4 doubles, in
- * milliseconds from the call's fork point: copy start, copy end, GEMM start, GEMM end.
- * Chunks with no copy have copy start = copy end = -1.  Returns SPTL_E_RANGE if n_chunks
- * differs from the recorded call or no timed call was made. */
+ * until that call's work is done.  out (host) receives n_chunks rows of 4 doubles in
+ * milliseconds: copy start, copy end, GEMM start, GEMM end.  Staged path: times from the
+ * start of the GEMM launch's first workgroup (device wall clock); copy start is 0 (all
+ * copies are queued at the fork), copy end is when the first tile of the chunk saw it
+ * landed, GEMM start/end are the chunk's first tile start and last tile end.  Per-chunk path:
+ * event times from the call's fork point.  Chunks with no copy have copy start = copy end =
+ * -1.  Returns SPTL_E_RANGE if n_chunks differs from the recorded call or no timed call was
+ * made. */
 int sptl_agmm_timeline(sptl_ctx *ctx, double *out, int n_chunks);
 
 /*
