@@ -54,6 +54,7 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 constexpr int kBK = 64;                   // K depth of one LDS stage
 constexpr int kRsrcFlags = 0x00020000;    // raw buffer, 32-bit data format
 constexpr int kOutOfRange = 0x7ffffff0;   // an offset past any num_records used here
+constexpr int kBand = 4;                  // tile rows per band of the plain tile order
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -150,22 +151,42 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     const ChunkPlan &plan = p.plan;
     int chunk = -1;
     if constexpr (!CHUNKED) {
-        // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes a contiguous run.
+        // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes a contiguous run
+        // of a banded order (bands of kBand tile rows, column-major inside a band), so the
+        // workgroups an XCD runs at once cover a few rows by several columns and share A
+        // and B panels in its L2.
         const int nt = tiles_m * tiles_n;
         const int per = nt >> 3, rem = nt & 7;
         const int xcd = bid & 7, slot = bid >> 3;
         const int t = xcd * per + (xcd < rem ? xcd : rem) + slot;
-        const int tm = t / tiles_n, tn = t - tm * tiles_n;
+        const int band = t / (kBand * tiles_n), in_band = t - band * (kBand * tiles_n);
+        const int band_rows = tiles_m - band * kBand < kBand ? tiles_m - band * kBand : kBand;
+        const int tm = band * kBand + in_band % band_rows, tn = in_band / band_rows;
         m0 = (int64_t)tm * BM;
         n0 = (int64_t)tn * BN;
         a_tile = p.a + m0 * p.lda;
         rows_valid = (int)((p.m - m0) < BM ? (p.m - m0) : BM);
     } else {
         // Chunk-ordered: workgroups are dispatched in index order, so tiles of the chunks
-        // that land first come first.  A chunk is a whole number of tile rows.
-        const int lt = bid / tiles_n, tn = bid - lt * tiles_n;
+        // that land first come first.  A chunk is a whole number of tile rows.  Inside a
+        // chunk, when its tiles split evenly into 8 blocks, the tiles of XCD x (local
+        // index = x mod 8) form block x, so the XCD shares one A panel set and the same B
+        // columns across the chunks in flight.
         const int tpc = plan.chunk_rows / BM;
-        const int pos = lt / tpc, sub = lt - pos * tpc;
+        const int per_chunk = tpc * tiles_n;
+        const int pos = bid / per_chunk, local = bid - pos * per_chunk;
+        int sub, tn;
+        const int rg = tpc < 8 ? tpc : 8;  // row groups
+        const int cg = 8 / rg;             // column groups
+        if ((8 % rg) == 0 && (tpc % rg) == 0 && (tiles_n % cg) == 0) {
+            const int x = local & 7, slot = local >> 3;
+            const int brows = tpc / rg, bcols = tiles_n / cg;
+            sub = (x / cg) * brows + slot % brows;
+            tn = (x % cg) * bcols + slot / brows;
+        } else {
+            sub = local / tiles_n;
+            tn = local - sub * tiles_n;
+        }
         chunk = plan.order[pos];
         m0 = (int64_t)chunk * plan.chunk_rows + (int64_t)sub * BM;
         n0 = (int64_t)tn * BN;

@@ -117,15 +117,18 @@ class SdmaStager {
 
     volatile uint64_t *finished(int set) const { return host_words + 16 * set; }
 
-    // The fork usually completes within microseconds of the call (earlier stream work is
-    // short), and a blocking event wait sleeps ~50 us before noticing: poll first, then block.
+    // The copies should start the moment the fork completes: a blocking event wait wakes
+    // up tens of microseconds late, which delays every chunk by as much.  So the worker
+    // polls while a call is pending (the host usually runs ahead of the GPU by a few
+    // calls, i.e. up to a few milliseconds), and only blocks after kForkSpin.
+    static constexpr auto kForkSpin = std::chrono::milliseconds(50);
     static bool wait_fork(hipEvent_t fork) {
         const auto t0 = std::chrono::steady_clock::now();
-        for (;;) {
+        for (unsigned i = 1;; ++i) {
             const hipError_t q = hipEventQuery(fork);
             if (q == hipSuccess) return true;
             if (q != hipErrorNotReady) return false;
-            if (std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(200))
+            if ((i & 255) == 0 && std::chrono::steady_clock::now() - t0 > kForkSpin)
                 return hipEventSynchronize(fork) == hipSuccess;
         }
     }
