@@ -50,6 +50,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBK = 64;                   // K depth of one LDS stage
 constexpr int kRsrcFlags = 0x00020000;    // raw buffer, 32-bit data format
@@ -115,41 +116,23 @@ __device__ __forceinline__ void wait_chunk(const ChunkPlan &plan, int chunk, int
     __atomic_thread_fence(__ATOMIC_ACQUIRE);
 }
 
-template <int BM, int BN, int WGM, int WGN>
-struct Cfg {
-    static constexpr int THREADS = 64 * WGM * WGN;
-    static constexpr int WM = BM / WGM, WN = BN / WGN;      // one wave's block
-    static constexpr int TM = WM / 32, TN = WN / 32;        // 32 x 32 MFMA blocks per wave
-    static constexpr int A_STAGE = BM * 128;                // bytes
-    static constexpr int B_STAGE = BN * 128;
-    static constexpr int STAGE = A_STAGE + B_STAGE;
-    static constexpr int B_ROW = BN * 2;                    // bytes per B row in LDS
-    static constexpr int A_VEC = BM * kBK / 8 / THREADS;    // 16-byte A vectors per thread
-    static constexpr int B_VEC = BN * kBK / 8 / THREADS;
-    static_assert(TM >= 1 && TN >= 1 && A_VEC >= 1 && B_VEC >= 1, "tile shape");
-    static_assert(BN >= 128, "B swizzle needs at least 8 units of 32 bytes per row");
-};
-
-template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED>
-__global__ void __launch_bounds__(64 * WGM * WGN)
-gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
-#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
-    using T = Cfg<BM, BN, WGM, WGN>;
-    constexpr int A_VEC = T::A_VEC, B_VEC = T::B_VEC;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm0 = (wave / WGN) * T::WM;
-    const int wn0 = (wave % WGN) * T::WN;
-
-    const int bid = blockIdx.x;
+// Output tile of this workgroup and, for a chunk-ordered launch, the wait for its chunk.
+struct TileOrigin {
     int64_t m0, n0;          // output tile origin
     const uint16_t *a_tile;  // first row of this tile's A rows
     int rows_valid;
+    int chunk;               // chunk-ordered launches: the tile's chunk, else -1
+};
+
+template <int BM, int BN, bool CHUNKED>
+__device__ __forceinline__ void tile_begin(const GemmProblem &p, int tiles_m, int tiles_n, TileOrigin &o) {
+    const int bid = blockIdx.x, tid = threadIdx.x;
     const ChunkPlan &plan = p.plan;
-    int chunk = -1;
+    int64_t &m0 = o.m0, &n0 = o.n0;
+    const uint16_t *&a_tile = o.a_tile;
+    int &rows_valid = o.rows_valid;
+    int &chunk = o.chunk;
+    chunk = -1;
     if constexpr (!CHUNKED) {
         // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes a contiguous run
         // of a banded order (bands of kBand tile rows, column-major inside a band), so the
@@ -206,6 +189,88 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         }
         __syncthreads();
     }
+}
+
+// Stores the tile's accumulators and, for a chunk-ordered launch, records the tile's end and
+// completes the call when this is its last workgroup.
+template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED>
+__device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin &o,
+                                         const f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+    constexpr int TM = BM / WGM / 32, TN = BN / WGN / 32;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm0 = (wave / WGN) * (BM / WGM), wn0 = (wave % WGN) * (BN / WGN);
+    const int64_t m0 = o.m0, n0 = o.n0;
+    // 32 x 32 MFMA result layout: lane l holds column l % 32; register r holds row
+    // 8 (r / 4) + 4 (l / 32) + r % 4.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = n0 + wn0 + j * 32 + (lane & 31);
+            if (col >= p.n) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (row < p.m) {
+                    if constexpr (OUT_F32)
+                        static_cast<float *>(p.c)[row * p.ldc + col] = acc[i][j][r];
+                    else
+                        static_cast<uint16_t *>(p.c)[row * p.ldc + col] = f32_to_bf16(acc[i][j][r]);
+                }
+            }
+        }
+    }
+    if (CHUNKED && threadIdx.x == 0) {
+        const ChunkPlan &plan = p.plan;
+        const int chunk = o.chunk;
+        if (plan.ts)
+            atomicMax(reinterpret_cast<unsigned long long *>(plan.ts + 2 * plan.n_chunks + chunk),
+                      (unsigned long long)wall_clock64());
+        // The last workgroup to finish waits for every copy of the call (own slot included),
+        // so the kernel ends only after all of them, then reports the call done.
+        const uint64_t done_before =
+            __hip_atomic_fetch_add(plan.wg_count, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (done_before == plan.wg_last) {
+            wait_ready(plan.join, plan);
+            __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN>
+struct Cfg {
+    static constexpr int THREADS = 64 * WGM * WGN;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;      // one wave's block
+    static constexpr int TM = WM / 32, TN = WN / 32;        // 32 x 32 MFMA blocks per wave
+    static constexpr int A_STAGE = BM * 128;                // bytes
+    static constexpr int B_STAGE = BN * 128;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int B_ROW = BN * 2;                    // bytes per B row in LDS
+    static constexpr int A_VEC = BM * kBK / 8 / THREADS;    // 16-byte A vectors per thread
+    static constexpr int B_VEC = BN * kBK / 8 / THREADS;
+    static_assert(TM >= 1 && TN >= 1 && A_VEC >= 1 && B_VEC >= 1, "tile shape");
+    static_assert(BN >= 128, "B swizzle needs at least 8 units of 32 bytes per row");
+};
+
+template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
+    using T = Cfg<BM, BN, WGM, WGN>;
+    constexpr int A_VEC = T::A_VEC, B_VEC = T::B_VEC;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm0 = (wave / WGN) * T::WM;
+    const int wn0 = (wave % WGN) * T::WN;
+
+    TileOrigin o;
+    tile_begin<BM, BN, CHUNKED>(p, tiles_m, tiles_n, o);
+    const int64_t m0 = o.m0, n0 = o.n0;
+    const uint16_t *a_tile = o.a_tile;
+    const int rows_valid = o.rows_valid;
 
     // Global -> register staging.  Thread t loads A vectors q = t + THREADS i (row q / 8,
     // 16-byte chunk q % 8) and B vectors q = t + THREADS i (row q / (BN / 8), columns
@@ -347,39 +412,180 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         __syncthreads();
     }
 
-    // 32 x 32 MFMA result layout: lane l holds column l % 32; register r holds row
-    // 8 (r / 4) + 4 (l / 32) + r % 4.
+    tile_end<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc);
+#endif
+}
+
+// Direct-to-LDS variant of the 256 x 256 tile (8 waves, 4 x 2, each 64 x 128).  K is walked
+// in stages of 32 held in a ring of four LDS slots; the buffer loads write LDS directly
+// (64 lanes x 16 bytes = 1 KB per instruction, lane l at byte 16 l), so no register staging
+// and no LDS store instructions are needed, and three stages (96 of K) are in flight while
+// one is consumed.  The per-lane global addresses apply the LDS swizzles in reverse:
+//   A slot: 256 rows of 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
+//           (a ds_read_b128 by 16 lanes then covers all 16 bank groups once);
+//   B slot: 32 rows (k) of 512 bytes, the same unit swizzle as the register-staged kernel.
+// Same MFMA instruction and K order as every other configuration.
+// A raw buffer descriptor (V#) for `bytes` bytes from `base`: 32-bit data format, no
+// stride, so out-of-range lane offsets read zero.
+__device__ __forceinline__ u32x4_t buffer_desc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4_t d;
+    d.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    d.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    d.z = __builtin_amdgcn_readfirstlane(bytes);
+    d.w = (uint32_t)kRsrcFlags;
+    return d;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p);
+}
+
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes land at LDS byte lds + 16 l.  Written as
+// inline assembly so that the compiler, which cannot tell which ring slot a load writes,
+// does not wait for every load before each LDS read; the kernel waits explicitly.
+__device__ __forceinline__ void load_to_lds(u32x4_t desc, uint32_t lds, int voffset) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(desc), "{m0}"(lds) : "memory");
+}
+
+constexpr int kDmaBK = 32;
+constexpr int kDmaSlotBytes = 256 * kDmaBK * 2;  // 16 KB per operand per stage
+constexpr int kDmaSlots = 4;                     // ring depth; the wait counts assume 4
+
+template <bool OUT_F32, bool CHUNKED>
+__global__ void __launch_bounds__(512)
+gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int BM = 256, BN = 256, WGM = 4, WGN = 2, TM = 2, TN = 4;
+    constexpr int B_ROW = BN * 2;
+    constexpr int SLOT = 2 * kDmaSlotBytes;  // ring slot: A (16 KB) then B (16 KB)
+    __shared__ __attribute__((aligned(1024))) char smem[kDmaSlots * SLOT];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm0 = (wave / WGN) * (BM / WGM);
+    const int wn0 = (wave % WGN) * (BN / WGN);
+
+    TileOrigin o;
+    tile_begin<BM, BN, CHUNKED>(p, tiles_m, tiles_n, o);
+    const int64_t n0 = o.n0;
+    const uint16_t *a_tile = o.a_tile;
+    const int rows_valid = o.rows_valid;
+
+    // Per-lane source offsets of this wave's two A blocks (16 rows each) and two B blocks
+    // (2 k-rows each) of a stage.
+    int a_off[2], a_kc[2], b_off[2];
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-            const int64_t col = n0 + wn0 + j * 32 + (lane & 31);
-            if (col >= p.n) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (row < p.m) {
-                    if constexpr (OUT_F32)
-                        static_cast<float *>(p.c)[row * p.ldc + col] = acc[i][j][r];
-                    else
-                        static_cast<uint16_t *>(p.c)[row * p.ldc + col] = f32_to_bf16(acc[i][j][r]);
-                }
-            }
-        }
+    for (int t = 0; t < 2; ++t) {
+        const int blk = wave * 2 + t;
+        const int row = blk * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        a_kc[t] = c * 8;
+        a_off[t] = (int)((row * p.lda + c * 8) * 2);
+        const int krow = blk * 2 + (lane >> 5);
+        const int q = lane & 31;
+        const int u = (q >> 1) ^ ((krow & 3) << 1);
+        const int64_t n = n0 + u * 16 + (q & 1) * 8;
+        b_off[t] = n < p.n ? (int)((krow * p.ldb + n) * 2) : kOutOfRange;
     }
-    if (CHUNKED && tid == 0) {
-        if (plan.ts)
-            atomicMax(reinterpret_cast<unsigned long long *>(plan.ts + 2 * plan.n_chunks + chunk),
-                      (unsigned long long)wall_clock64());
-        // The last workgroup to finish waits for every copy of the call (own slot included),
-        // so the kernel ends only after all of them, then reports the call done.
-        const uint64_t done_before =
-            __hip_atomic_fetch_add(plan.wg_count, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (done_before == plan.wg_last) {
-            wait_ready(plan.join, plan);
-            __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int nk = (int)((p.k + kDmaBK - 1) / kDmaBK);
+    const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 2) * 1024;  // this wave's first block
+
+    // Stage kt into ring slot `slot`.  Stages past the end read an empty range (zeros), so
+    // every stage issues exactly four loads per wave and the wait counts below stay fixed.
+    auto issue = [&](int kt, int slot) {
+        const bool live = kt < nk;
+        const int64_t k0 = live ? (int64_t)kt * kDmaBK : 0;
+        const int64_t a_bytes = live ? ((int64_t)rows_valid * p.lda - k0) * 2 : 0;
+        const u32x4_t ar = buffer_desc(a_tile + k0, (uint32_t)a_bytes);
+        const bool k_tail = k0 + kDmaBK > p.k;
+        const int64_t k_rows = !live ? 0 : (p.k - k0) < kDmaBK ? (p.k - k0) : kDmaBK;
+        const u32x4_t br = buffer_desc(p.b + k0 * p.ldb, (uint32_t)(k_rows * p.ldb * 2));
+        const uint32_t la = lds0 + (uint32_t)(slot * SLOT), lb = la + kDmaSlotBytes;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int off = (k_tail && k0 + a_kc[t] >= p.k) ? kOutOfRange : a_off[t];
+            load_to_lds(ar, la + t * 1024, off);
         }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) load_to_lds(br, lb + t * 1024, b_off[t]);
+    };
+
+    // fragment read addresses (within a slot); step s of a stage adds 16 k
+    int a_addr[2][TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm0 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) a_addr[st][i] = r * (kDmaBK * 2) + (((2 * st + (lane >> 5)) ^ ((r >> 2) & 3)) << 4);
     }
+    const int rr = lane & 15;
+    const int b_k0 = 8 * (lane >> 5) + (rr >> 2);
+    int b_addr[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int n = wn0 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (rr & 3);
+        b_addr[j] = kDmaSlotBytes + b_k0 * B_ROW + (((n >> 4) ^ ((b_k0 & 3) << 1)) << 5) + (n & 15) * 2;
+    }
+
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto load_frags = [&](const char *slot, int st, bf16x8_t *af, bf16x8_t *bfr) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(slot + a_addr[st][i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const char *base = slot + b_addr[j] + st * 16 * B_ROW;
+            bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
+            bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * B_ROW));
+            bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    auto compute = [&](const char *slot) {
+        bf16x8_t af[2][TM], bfr[2][TN];
+        load_frags(slot, 0, af[0], bfr[0]);
+        load_frags(slot, 1, af[1], bfr[1]);
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[st][i], bfr[st][j], acc[i][j], 0, 0, 0);
+        // order: step 0's fragment reads, then each MFMA of step 0 with one fragment read of
+        // step 1, then step 1's MFMAs
+        constexpr int kDs = TM + 2 * TN, kMf = TM * TN;
+        __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);
+#pragma unroll
+        for (int m = 0; m < kMf; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m < kDs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
+    };
+    // One stage: wait for this wave's loads of stage kt (the two later stages may stay in
+    // flight), make every wave's loads visible and retire the slot the previous stage read,
+    // start stage kt + 3 into it, then compute stage kt.
+    auto step = [&](int kt, int slot) {
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        __syncthreads();
+        issue(kt + kDmaSlots - 1, (slot + kDmaSlots - 1) % kDmaSlots);
+        compute(smem + slot * SLOT);
+    };
+
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    for (int kt = 0; kt < nk; ++kt) step(kt, kt & (kDmaSlots - 1));
+    // no load may still be writing this workgroup's LDS when it exits
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    tile_end<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc);
 #endif
 }
 
@@ -407,8 +613,27 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+hipError_t launch_dma(const GemmProblem &p, hipStream_t stream) {
+    const int64_t tm = (p.m + 255) / 256, tn = (p.n + 255) / 256;
+    const int64_t nt = tm * tn;
+    if (nt == 0) return hipSuccess;
+    if (nt > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)nt), block(512);
+    const bool chunked = p.plan.chunk_rows != 0;
+    if (p.c_f32 && chunked)
+        hipLaunchKernelGGL((gemm_dma_kernel<true, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
+    else if (p.c_f32)
+        hipLaunchKernelGGL((gemm_dma_kernel<true, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
+    else if (chunked)
+        hipLaunchKernelGGL((gemm_dma_kernel<false, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
+    else
+        hipLaunchKernelGGL((gemm_dma_kernel<false, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
+    return hipGetLastError();
+}
+
 // Tile configurations.  All share the MFMA instruction and the K order.
-enum Config { k256x256w2x2, k256x256w2x4, k256x256w4x2, k256x128w4x2, k256x128w4x1, k128x128w2x2, kNumConfigs };
+enum Config { k256x256w2x2, k256x256w2x4, k256x256w4x2, k256x128w4x2, k256x128w4x1, k128x128w2x2, k256x256dma,
+              kNumConfigs };
 
 const char *config_name(int c) {
     switch (c) {
@@ -417,6 +642,7 @@ const char *config_name(int c) {
         case k256x256w4x2: return "256x256w4x2";
         case k256x128w4x2: return "256x128w4x2";
         case k256x128w4x1: return "256x128w4x1";
+        case k256x256dma: return "256x256dma";
         default: return "128x128w2x2";
     }
 }
@@ -477,6 +703,7 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile) 
         case k256x256w4x2: return launch_cfg<256, 256, 4, 2>(p, stream);
         case k256x128w4x2: return launch_cfg<256, 128, 4, 2>(p, stream);
         case k256x128w4x1: return launch_cfg<256, 128, 4, 1>(p, stream);
+        case k256x256dma: return launch_dma(p, stream);
         default: return launch_cfg<128, 128, 2, 2>(p, stream);
     }
 }
