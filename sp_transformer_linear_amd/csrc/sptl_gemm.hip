@@ -416,15 +416,6 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #endif
 }
 
-// Direct-to-LDS variant of the 256 x 256 tile (8 waves, 4 x 2, each 64 x 128).  K is walked
-// in stages of 32 held in a ring of four LDS slots; the buffer loads write LDS directly
-// (64 lanes x 16 bytes = 1 KB per instruction, lane l at byte 16 l), so no register staging
-// and no LDS store instructions are needed, and three stages (96 of K) are in flight while
-// one is consumed.  The per-lane global addresses apply the LDS swizzles in reverse:
-//   A slot: 256 rows of 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
-//           (a ds_read_b128 by 16 lanes then covers all 16 bank groups once);
-//   B slot: 32 rows (k) of 512 bytes, the same unit swizzle as the register-staged kernel.
-// Same MFMA instruction and K order as every other configuration.
 // A raw buffer descriptor (V#) for `bytes` bytes from `base`: 32-bit data format, no
 // stride, so out-of-range lane offsets read zero.
 __device__ __forceinline__ u32x4_t buffer_desc(const void *base, uint32_t bytes) {
@@ -450,16 +441,33 @@ __device__ __forceinline__ void load_to_lds(u32x4_t desc, uint32_t lds, int voff
 
 constexpr int kDmaBK = 32;
 constexpr int kDmaSlotBytes = 256 * kDmaBK * 2;  // 16 KB per operand per stage
-constexpr int kDmaSlots = 4;                     // ring depth; the wait counts assume 4
 
-template <bool OUT_F32, bool CHUNKED>
-__global__ void __launch_bounds__(512)
+// s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Direct-to-LDS variant of the 256 x 256 tile (WGM x WGN waves).  K is walked in stages of
+// 32 held in a ring of SLOTS LDS slots; the buffer loads write LDS directly (64 lanes x 16
+// bytes = 1 KB per instruction, lane l at byte 16 l), so no register staging and no LDS
+// store instructions are needed, and SLOTS - 1 stages are in flight while one is consumed.
+// The per-lane global addresses apply the LDS swizzles in reverse:
+//   A slot: 256 rows of 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
+//           (a ds_read_b128 by 16 lanes then covers all 16 bank groups once);
+//   B slot: 32 rows (k) of 512 bytes, the same unit swizzle as the register-staged kernel.
+// Same MFMA instruction and K order as every other configuration.
+template <int WGM, int WGN, int SLOTS, bool OUT_F32, bool CHUNKED>
+__global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int BM = 256, BN = 256, WGM = 4, WGN = 2, TM = 2, TN = 4;
+    constexpr int BM = 256, BN = 256, TM = BM / WGM / 32, TN = BN / WGN / 32;
+    constexpr int NBLK = 16 / (WGM * WGN);   // 1 KB blocks per operand per wave per stage
+    static_assert(NBLK * WGM * WGN == 16 && SLOTS >= 3 && SLOTS * 2 * kDmaSlotBytes <= 160 * 1024, "shape");
     constexpr int B_ROW = BN * 2;
     constexpr int SLOT = 2 * kDmaSlotBytes;  // ring slot: A (16 KB) then B (16 KB)
-    __shared__ __attribute__((aligned(1024))) char smem[kDmaSlots * SLOT];
+    __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -474,10 +482,10 @@ gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 
     // Per-lane source offsets of this wave's two A blocks (16 rows each) and two B blocks
     // (2 k-rows each) of a stage.
-    int a_off[2], a_kc[2], b_off[2];
+    int a_off[NBLK], a_kc[NBLK], b_off[NBLK];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int blk = wave * 2 + t;
+    for (int t = 0; t < NBLK; ++t) {
+        const int blk = wave * NBLK + t;
         const int row = blk * 16 + (lane >> 2);
         const int c = (lane & 3) ^ ((row >> 2) & 3);
         a_kc[t] = c * 8;
@@ -489,7 +497,7 @@ gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         b_off[t] = n < p.n ? (int)((krow * p.ldb + n) * 2) : kOutOfRange;
     }
     const int nk = (int)((p.k + kDmaBK - 1) / kDmaBK);
-    const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 2) * 1024;  // this wave's first block
+    const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * NBLK) * 1024;  // this wave's first block
 
     // Stage kt into ring slot `slot`.  Stages past the end read an empty range (zeros), so
     // every stage issues exactly four loads per wave and the wait counts below stay fixed.
@@ -503,12 +511,12 @@ gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         const u32x4_t br = buffer_desc(p.b + k0 * p.ldb, (uint32_t)(k_rows * p.ldb * 2));
         const uint32_t la = lds0 + (uint32_t)(slot * SLOT), lb = la + kDmaSlotBytes;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NBLK; ++t) {
             const int off = (k_tail && k0 + a_kc[t] >= p.k) ? kOutOfRange : a_off[t];
             load_to_lds(ar, la + t * 1024, off);
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) load_to_lds(br, lb + t * 1024, b_off[t]);
+        for (int t = 0; t < NBLK; ++t) load_to_lds(br, lb + t * 1024, b_off[t]);
     };
 
     // fragment read addresses (within a slot); step s of a stage adds 16 k
@@ -573,18 +581,17 @@ gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     // flight), make every wave's loads visible and retire the slot the previous stage read,
     // start stage kt + 3 into it, then compute stage kt.
     auto step = [&](int kt, int slot) {
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        wait_vmcnt<2 * NBLK * (SLOTS - 2)>();  // 2 NBLK loads per stage, SLOTS - 2 stages after kt
         __syncthreads();
-        issue(kt + kDmaSlots - 1, (slot + kDmaSlots - 1) % kDmaSlots);
+        issue(kt + SLOTS - 1, slot == 0 ? SLOTS - 1 : slot - 1);
         compute(smem + slot * SLOT);
     };
 
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    for (int kt = 0; kt < nk; ++kt) step(kt, kt & (kDmaSlots - 1));
+#pragma unroll
+    for (int st = 0; st < SLOTS - 1; ++st) issue(st, st);
+    for (int kt = 0, slot = 0; kt < nk; ++kt, slot = slot + 1 == SLOTS ? 0 : slot + 1) step(kt, slot);
     // no load may still be writing this workgroup's LDS when it exits
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt<0>();
     tile_end<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc);
 #endif
 }
@@ -613,21 +620,22 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int WGM, int WGN, int SLOTS>
 hipError_t launch_dma(const GemmProblem &p, hipStream_t stream) {
     const int64_t tm = (p.m + 255) / 256, tn = (p.n + 255) / 256;
     const int64_t nt = tm * tn;
     if (nt == 0) return hipSuccess;
     if (nt > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)nt), block(512);
+    const dim3 grid((unsigned)nt), block(64 * WGM * WGN);
     const bool chunked = p.plan.chunk_rows != 0;
     if (p.c_f32 && chunked)
-        hipLaunchKernelGGL((gemm_dma_kernel<true, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_dma_kernel<WGM, WGN, SLOTS, true, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else if (p.c_f32)
-        hipLaunchKernelGGL((gemm_dma_kernel<true, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_dma_kernel<WGM, WGN, SLOTS, true, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else if (chunked)
-        hipLaunchKernelGGL((gemm_dma_kernel<false, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_dma_kernel<WGM, WGN, SLOTS, false, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else
-        hipLaunchKernelGGL((gemm_dma_kernel<false, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_dma_kernel<WGM, WGN, SLOTS, false, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
     return hipGetLastError();
 }
 
@@ -703,7 +711,7 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile) 
         case k256x256w4x2: return launch_cfg<256, 256, 4, 2>(p, stream);
         case k256x128w4x2: return launch_cfg<256, 128, 4, 2>(p, stream);
         case k256x128w4x1: return launch_cfg<256, 128, 4, 1>(p, stream);
-        case k256x256dma: return launch_dma(p, stream);
+        case k256x256dma: return launch_dma<4, 2, 4>(p, stream);
         default: return launch_cfg<128, 128, 2, 2>(p, stream);
     }
 }
