@@ -151,25 +151,14 @@ __device__ __forceinline__ void tile_begin(const GemmProblem &p, int tiles_m, in
         rows_valid = (int)((p.m - m0) < BM ? (p.m - m0) : BM);
     } else {
         // Chunk-ordered: workgroups are dispatched in index order, so tiles of the chunks
-        // that land first come first.  A chunk is a whole number of tile rows.  Inside a
-        // chunk, when its tiles split evenly into 8 blocks, the tiles of XCD x (local
-        // index = x mod 8) form block x, so the XCD shares one A panel set and the same B
-        // columns across the chunks in flight.
+        // that land first come first.  A chunk is a whole number of tile rows, walked row by
+        // row: with 16 column tiles, XCD x (workgroups x mod 8) takes columns x and x + 8 of
+        // every row tile, so its workgroups of one chunk share 4 A and 2 B panels in its L2
+        // (the fewest for 8 tiles of one chunk).
         const int tpc = plan.chunk_rows / BM;
         const int per_chunk = tpc * tiles_n;
         const int pos = bid / per_chunk, local = bid - pos * per_chunk;
-        int sub, tn;
-        const int rg = tpc < 8 ? tpc : 8;  // row groups
-        const int cg = 8 / rg;             // column groups
-        if ((8 % rg) == 0 && (tpc % rg) == 0 && (tiles_n % cg) == 0) {
-            const int x = local & 7, slot = local >> 3;
-            const int brows = tpc / rg, bcols = tiles_n / cg;
-            sub = (x / cg) * brows + slot % brows;
-            tn = (x % cg) * bcols + slot / brows;
-        } else {
-            sub = local / tiles_n;
-            tn = local - sub * tiles_n;
-        }
+        const int sub = local / tiles_n, tn = local - sub * tiles_n;
         chunk = plan.order[pos];
         m0 = (int64_t)chunk * plan.chunk_rows + (int64_t)sub * BM;
         n0 = (int64_t)tn * BN;
