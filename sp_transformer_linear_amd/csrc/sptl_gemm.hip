@@ -150,15 +150,35 @@ __device__ __forceinline__ void tile_begin(const GemmProblem &p, int tiles_m, in
         a_tile = p.a + m0 * p.lda;
         rows_valid = (int)((p.m - m0) < BM ? (p.m - m0) : BM);
     } else {
-        // Chunk-ordered: workgroups are dispatched in index order, so tiles of the chunks
-        // that land first come first.  A chunk is a whole number of tile rows, walked row by
-        // row: with 16 column tiles, XCD x (workgroups x mod 8) takes columns x and x + 8 of
-        // every row tile, so its workgroups of one chunk share 4 A and 2 B panels in its L2
-        // (the fewest for 8 tiles of one chunk).
+        // Chunk-ordered: each XCD (workgroups x mod 8) runs its workgroups in index order, so
+        // on every XCD the tiles of chunks that land first come first.  A chunk is a whole
+        // number of tile rows.  When the chunks divide evenly, a chunk's tiles go to a group
+        // of g XCDs (the fewest that keeps each XCD's share at 32 tiles or less, one per CU),
+        // 8 / g chunks run side by side, and each XCD's share of a chunk is a contiguous run
+        // of the chunk's banded order (4 tile rows, column-major), so the workgroups an XCD
+        // runs at once share a few A and B panels in its L2.
         const int tpc = plan.chunk_rows / BM;
         const int per_chunk = tpc * tiles_n;
-        const int pos = bid / per_chunk, local = bid - pos * per_chunk;
-        const int sub = local / tiles_n, tn = local - sub * tiles_n;
+        int g = 0;
+        for (int c = 1; c <= 8 && !g; c *= 2)
+            if (per_chunk % c == 0 && plan.n_chunks % (8 / c) == 0 && per_chunk / c <= 32) g = c;
+        for (int c = 8; c >= 1 && !g; c /= 2)
+            if (per_chunk % c == 0 && plan.n_chunks % (8 / c) == 0) g = c;
+        int pos, sub, tn;
+        if (g) {
+            const int x = bid & 7, slot = bid >> 3, share = per_chunk / g;
+            pos = (slot / share) * (8 / g) + x / g;
+            const int t = (x % g) * share + slot % share;
+            const int band = t / (kBand * tiles_n), in_band = t - band * (kBand * tiles_n);
+            const int band_rows = tpc - band * kBand < kBand ? tpc - band * kBand : kBand;
+            sub = band * kBand + in_band % band_rows;
+            tn = in_band / band_rows;
+        } else {
+            pos = bid / per_chunk;
+            const int local = bid - pos * per_chunk;
+            sub = local / tiles_n;
+            tn = local - sub * tiles_n;
+        }
         chunk = plan.order[pos];
         m0 = (int64_t)chunk * plan.chunk_rows + (int64_t)sub * BM;
         n0 = (int64_t)tn * BN;
@@ -226,26 +246,33 @@ __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin 
     }
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int BK>
 struct Cfg {
     static constexpr int THREADS = 64 * WGM * WGN;
     static constexpr int WM = BM / WGM, WN = BN / WGN;      // one wave's block
     static constexpr int TM = WM / 32, TN = WN / 32;        // 32 x 32 MFMA blocks per wave
-    static constexpr int A_STAGE = BM * 128;                // bytes
-    static constexpr int B_STAGE = BN * 128;
+    static constexpr int A_ROW = BK * 2;                    // bytes per A row in LDS
+    static constexpr int CPR = BK / 8;                      // 16-byte chunks per A row
+    static constexpr int A_STAGE = BM * A_ROW;              // bytes
+    static constexpr int B_STAGE = BN * 2 * BK;
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int B_ROW = BN * 2;                    // bytes per B row in LDS
-    static constexpr int A_VEC = BM * kBK / 8 / THREADS;    // 16-byte A vectors per thread
-    static constexpr int B_VEC = BN * kBK / 8 / THREADS;
+    static constexpr int A_VEC = BM * BK / 8 / THREADS;     // 16-byte A vectors per thread
+    static constexpr int B_VEC = BN * BK / 8 / THREADS;
+    static_assert(BK == 64 || BK == 32, "stage depth");
     static_assert(TM >= 1 && TN >= 1 && A_VEC >= 1 && B_VEC >= 1, "tile shape");
     static_assert(BN >= 128, "B swizzle needs at least 8 units of 32 bytes per row");
+    // A chunk swizzle: 64-k rows (8 chunks) use c ^ ((r ^ r >> 3) & 7); 32-k rows (4 chunks)
+    // use c ^ ((r >> 2) & 3).  Either way 16 lanes reading one chunk of 16 consecutive rows
+    // hit 16 distinct 16-byte bank groups.
+    static __device__ __forceinline__ int aswz(int r) { return BK == 64 ? swz(r) : (r >> 2) & 3; }
 };
 
-template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED>
-__global__ void __launch_bounds__(64 * WGM * WGN)
+template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED, int BK = kBK, int WPE = 1>
+__global__ void __launch_bounds__(64 * WGM * WGN, WPE)
 gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
-    using T = Cfg<BM, BN, WGM, WGN>;
+    using T = Cfg<BM, BN, WGM, WGN, BK>;
     constexpr int A_VEC = T::A_VEC, B_VEC = T::B_VEC;
     __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
@@ -261,17 +288,17 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     const uint16_t *a_tile = o.a_tile;
     const int rows_valid = o.rows_valid;
 
-    // Global -> register staging.  Thread t loads A vectors q = t + THREADS i (row q / 8,
-    // 16-byte chunk q % 8) and B vectors q = t + THREADS i (row q / (BN / 8), columns
+    // Global -> register staging.  Thread t loads A vectors q = t + THREADS i (row q / CPR,
+    // 16-byte chunk q % CPR) and B vectors q = t + THREADS i (row q / (BN / 8), columns
     // 8 (q % (BN / 8)) ..).
     int a_voff[A_VEC], a_kc[A_VEC], a_lds[A_VEC];
 #pragma unroll
     for (int i = 0; i < A_VEC; ++i) {
         const int q = tid + i * T::THREADS;
-        const int row = q >> 3, c = q & 7;
+        const int row = q / T::CPR, c = q % T::CPR;
         a_kc[i] = c * 8;
         a_voff[i] = (int)((row * p.lda + c * 8) * 2);
-        a_lds[i] = row * 128 + ((c ^ swz(row)) << 4);
+        a_lds[i] = row * T::A_ROW + ((c ^ T::aswz(row)) << 4);
     }
     int b_voff[B_VEC], b_lds[B_VEC];
 #pragma unroll
@@ -284,22 +311,22 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     }
     u32x4_t ra[A_VEC], rb[B_VEC];
 
-    const int nk = (int)((p.k + kBK - 1) / kBK);
+    const int nk = (int)((p.k + BK - 1) / BK);
     // Loads stage kt into registers.  Stages past the end (kt >= nk) get an empty buffer
     // range and read zeros, which keeps the loop free of branches.
     auto load_stage = [&](int kt) {
         const bool live = kt < nk;
-        const int64_t k0 = live ? (int64_t)kt * kBK : 0;
+        const int64_t k0 = live ? (int64_t)kt * BK : 0;
         const int64_t a_bytes = live ? ((int64_t)rows_valid * p.lda - k0) * 2 : 0;
         __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(a_tile + k0), (short)0, (int)a_bytes, kRsrcFlags);
-        const bool k_tail = k0 + kBK > p.k;
+        const bool k_tail = k0 + BK > p.k;
 #pragma unroll
         for (int i = 0; i < A_VEC; ++i) {
             const int off = (k_tail && k0 + a_kc[i] >= p.k) ? kOutOfRange : a_voff[i];
             ra[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0));
         }
-        const int64_t k_rows = !live ? 0 : (p.k - k0) < kBK ? (p.k - k0) : kBK;
+        const int64_t k_rows = !live ? 0 : (p.k - k0) < BK ? (p.k - k0) : BK;
         __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(p.b + k0 * p.ldb), (short)0, (int)(k_rows * p.ldb * 2), kRsrcFlags);
 #pragma unroll
@@ -319,8 +346,8 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
         const int r = wm0 + i * 32 + (lane & 31);
-        a_row_off[i] = r * 128;
-        a_swz[i] = swz(r);
+        a_row_off[i] = r * T::A_ROW;
+        a_swz[i] = T::aswz(r);
     }
     const int rr = lane & 15;
     const int b_k0 = 8 * (lane >> 5) + (rr >> 2);  // k within a 16-k step, first half
@@ -361,8 +388,8 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         bf16x8_t af[2][T::TM], bfr[2][T::TN];
         load_frags(as, bs, 0, af[0], bfr[0]);
 #pragma unroll
-        for (int s = 0; s < kBK / 16; ++s) {
-            if (s + 1 < kBK / 16) load_frags(as, bs, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+        for (int s = 0; s < BK / 16; ++s) {
+            if (s + 1 < BK / 16) load_frags(as, bs, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
 #pragma unroll
@@ -375,7 +402,7 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     auto pin_schedule = [&]() {
         constexpr int kDsPerStep = T::TM + 2 * T::TN;
         constexpr int kMfmaPerStep = T::TM * T::TN;
-        constexpr int kSteps = kBK / 16;
+        constexpr int kSteps = BK / 16;
         __builtin_amdgcn_sched_group_barrier(0x020, A_VEC + B_VEC, 0);  // global loads first
         __builtin_amdgcn_sched_group_barrier(0x100, kDsPerStep, 0);
 #pragma unroll
@@ -590,7 +617,7 @@ __global__ void fill_u64_kernel(uint64_t *p, int64_t n, uint64_t v) {
     if (i < n) p[i] = v;
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int BK = kBK, int WPE = 1>
 hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
     const int64_t tm = (p.m + BM - 1) / BM, tn = (p.n + BN - 1) / BN;
     const int64_t nt = tm * tn;
@@ -599,13 +626,13 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
     const dim3 grid((unsigned)nt), block(64 * WGM * WGN);
     const bool chunked = p.plan.chunk_rows != 0;
     if (p.c_f32 && chunked)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, true, BK, WPE>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else if (p.c_f32)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, false, BK, WPE>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else if (chunked)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, true, BK, WPE>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, false, BK, WPE>), grid, block, 0, stream, p, (int)tm, (int)tn);
     return hipGetLastError();
 }
 
@@ -630,7 +657,7 @@ hipError_t launch_dma(const GemmProblem &p, hipStream_t stream) {
 
 // Tile configurations.  All share the MFMA instruction and the K order.
 enum Config { k256x256w2x2, k256x256w2x4, k256x256w4x2, k256x128w4x2, k256x128w4x1, k128x128w2x2, k256x256dma,
-              kNumConfigs };
+              k128x256w2x2k32, k256x256w4x2k32, kNumConfigs };
 
 const char *config_name(int c) {
     switch (c) {
@@ -640,11 +667,13 @@ const char *config_name(int c) {
         case k256x128w4x2: return "256x128w4x2";
         case k256x128w4x1: return "256x128w4x1";
         case k256x256dma: return "256x256dma";
+        case k128x256w2x2k32: return "128x256w2x2k32";
+        case k256x256w4x2k32: return "256x256w4x2k32";
         default: return "128x128w2x2";
     }
 }
 
-int config_rows(int c) { return c == k128x128w2x2 ? 128 : 256; }
+int config_rows(int c) { return c == k128x128w2x2 || c == k128x256w2x2k32 ? 128 : 256; }
 
 // SPTL_GEMM_CFG=<name> forces one configuration for every GEMM (measurement aid).
 int forced_config() {
@@ -701,6 +730,8 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile) 
         case k256x128w4x2: return launch_cfg<256, 128, 4, 2>(p, stream);
         case k256x128w4x1: return launch_cfg<256, 128, 4, 1>(p, stream);
         case k256x256dma: return launch_dma<4, 2, 4>(p, stream);
+        case k128x256w2x2k32: return launch_cfg<128, 256, 2, 2, 32, 2>(p, stream);
+        case k256x256w4x2k32: return launch_cfg<256, 256, 4, 2, 32>(p, stream);
         default: return launch_cfg<128, 128, 2, 2>(p, stream);
     }
 }
