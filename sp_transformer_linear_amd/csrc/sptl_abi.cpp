@@ -26,6 +26,7 @@ struct sptl_ctx {
     uint64_t *ts_dev = nullptr;         // [3 * kMaxPlanChunks + 1] chunk timestamps
     uint64_t *flags_dev = nullptr;      // landed flags, kFlagSetWords per stager set
     int wallclock_khz = 100000;
+    uint64_t wait_timeout_us = 10000000;  // bound on one chunk wait inside the GEMM (10 s)
     int t_mode = 0;                     // 0: event timeline, 1: chunk-ordered timeline
     int t_rank_first = 0, t_rank_count = 0;
     int t_set = -1;                     // stager set and epoch of the last timed chunk-ordered call
@@ -125,6 +126,11 @@ int create_ctx(sptl_ctx **out, int device) {
         if (c->wallclock_khz <= 0) c->wallclock_khz = 100000;
         const char *e = getenv("SPTL_STAGING");
         c->events_only = e && !strcmp(e, "events");
+        // SPTL_WAIT_TIMEOUT_US shortens the bound on a chunk wait (failure-path tests)
+        if (const char *t = getenv("SPTL_WAIT_TIMEOUT_US")) {
+            const long long us = strtoll(t, nullptr, 10);
+            if (us >= 1 && us <= 10000000) c->wait_timeout_us = (uint64_t)us;
+        }
     }
     if (rc) {
         sptl_destroy(c);
@@ -235,7 +241,7 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     plan.own_count = cpr;
     plan.own_a = static_cast<const uint16_t *>(shard_src[rank]);
     plan.err = ctx->err_dev;
-    plan.timeout_ticks = (uint64_t)ctx->wallclock_khz * 10000u;  // 10 s
+    plan.timeout_ticks = (uint64_t)ctx->wallclock_khz * ctx->wait_timeout_us / 1000u;
     static const int poll_sleep = [] {
         const char *e = getenv("SPTL_POLL_SLEEP");
         const long v = e ? strtol(e, nullptr, 10) : 0;

@@ -418,3 +418,41 @@ def test_agmm_staged_back_to_back_calls(env):
     ctx.check()
     for i, (y, want) in enumerate(zip(outs, wants)):
         assert_within(y.cpu().numpy().astype(np.float64), want, fp32_tol(want), f"call {i}")
+
+
+def test_agmm_staged_wait_timeout_is_reported(env):
+    """A chunk wait that runs out of time is reported by sptl_ctx_check as SPTL_E_ASYNC.
+
+    The bound on a chunk wait is set to 1 us for one context (from the host, through the
+    context's configuration), so the GEMM's workgroups give up long before 8 MiB chunks land;
+    every wave still exits normally.  The result is invalid; the report is what is checked.
+    """
+    import os
+    import time
+    torch, sptl, ctx = env
+    os.environ["SPTL_WAIT_TIMEOUT_US"] = "1"
+    try:
+        short = sptl.Context(0)
+    finally:
+        del os.environ["SPTL_WAIT_TIMEOUT_US"]
+    tp, rows, K, N = 8, 1024, 4096, 256
+    shards = [torch.ones((rows, K), dtype=torch.bfloat16, device="cuda") for _ in range(tp)]
+    xg = torch.empty((tp * rows, K), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones((K, N), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((tp * rows, N), dtype=torch.bfloat16, device="cuda")
+    try:
+        sptl.agmm_chunked(shards, xg, w, y, n_chunks=tp, rank=0, ctx=short)
+        torch.cuda.synchronize()
+        with pytest.raises(sptl.SptlError) as err:
+            short.check()
+        assert err.value.status == 9, str(err.value)
+        short.check()  # the report was cleared
+        time.sleep(0.05)  # the copies of the abandoned call land before its signals go away
+        torch.cuda.synchronize()
+    finally:
+        short.close()
+    # the shared context is unaffected
+    sptl.agmm_chunked(shards, xg, w, y, n_chunks=tp, rank=0, ctx=ctx)
+    torch.cuda.synchronize()
+    ctx.check()
+    assert torch.all(y == float(K))
