@@ -71,7 +71,8 @@ typedef enum {
 /* Create a context on HIP device `device` (events and small device buffers are created
  * now; the copy stream or SDMA stager on the first agmm_chunked call).  *out receives the
  * context.  Returns SPTL_E_NULL if out is NULL, SPTL_E_RANGE for a bad device, SPTL_E_HIP on
- * runtime failure. */
+ * runtime failure.  Environment read here: SPTL_STAGING=events forces the per-chunk path;
+ * SPTL_WAIT_TIMEOUT_US=1..10000000 sets the bound on one chunk wait (default 10 s). */
 int sptl_create(sptl_ctx **out, int device);
 
 /* Destroy a context created by sptl_create: waits (bounded) for its staged calls and its copy
