@@ -261,7 +261,8 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     plan.epoch = call.epoch;
     plan.finished = call.finished;
     plan.wg_count = call.wg_count;
-    plan.wg_last = call.wg_last;
+    for (int g = 0; g < sptl::kEndGroups; ++g) plan.grp_last[g] = call.grp_last[g];
+    plan.all_last = call.all_last;
     hipError_t he = hipSuccess;
     if (timing) {
         he = sptl::launch_fill_u64(ctx->ts_dev, 2 * n, ~0ull, cs);

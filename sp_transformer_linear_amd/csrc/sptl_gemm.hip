@@ -236,10 +236,16 @@ __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin 
             atomicMax(reinterpret_cast<unsigned long long *>(plan.ts + 2 * plan.n_chunks + chunk),
                       (unsigned long long)wall_clock64());
         // The last workgroup to finish waits for every copy of the call (own slot included),
-        // so the kernel ends only after all of them, then reports the call done.
-        const uint64_t done_before =
-            __hip_atomic_fetch_add(plan.wg_count, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (done_before == plan.wg_last) {
+        // so the kernel ends only after all of them, then reports the call done.  The counts
+        // are relaxed: a workgroup counts itself after its chunk wait has returned, so a full
+        // count means that no workgroup of the call still reads the set's signals or flags,
+        // which is all the report promises (the outputs are ordered by the kernel's end).  A
+        // release or acquire per workgroup would write back or invalidate its L2 each time.
+        const int g = blockIdx.x % kEndGroups;
+        if (__hip_atomic_fetch_add(plan.wg_count + g * kEndLine, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                plan.grp_last[g] &&
+            __hip_atomic_fetch_add(plan.wg_count + kEndGroups * kEndLine, 1ull, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) == plan.all_last) {
             wait_ready(plan.join, plan);
             __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
         }

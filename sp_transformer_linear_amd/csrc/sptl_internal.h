@@ -8,6 +8,9 @@
 namespace sptl {
 
 constexpr int kMaxPlanChunks = 64;  // chunks of one chunk-ordered GEMM launch
+constexpr int kEndGroups = 8;       // end-counter groups (workgroup index mod 8)
+constexpr int kEndLine = 32;        // 64-bit words between end counters (256 bytes)
+constexpr int kEndCounters = kEndGroups + 1;
 
 // Landed flags of a chunk-ordered launch: kFlagReplicas copies per chunk, 4 KiB apart so that
 // they fall on different memory channels; replica r of chunk c is word r * kFlagStride + c.
@@ -35,8 +38,9 @@ struct ChunkPlan {
     uint64_t *flags;                         // landed flags (kFlagSetWords words), or nullptr
     uint64_t epoch;                          // value a landed flag holds for this launch
     uint64_t *finished;                      // pinned host word: epoch once the launch is done
-    uint64_t *wg_count;                      // finished-workgroup counter of the signal set
-    uint64_t wg_last;                        // counter value seen by this launch's last workgroup
+    uint64_t *wg_count;                      // end counters of the signal set (kEndCounters lines)
+    uint64_t grp_last[kEndGroups];           // group counter value seen by a group's last workgroup
+    uint64_t all_last;                       // final counter value seen by the last group
     uint64_t *ts;                            // optional per-chunk timestamps (see below)
 };
 // Waiting: a workgroup of chunk c polls its replica of c's landed flag about every
@@ -44,8 +48,12 @@ struct ChunkPlan {
 // The first workgroup to see the word reach zero sets every replica to `epoch`.  Spreading
 // the polls over replicas keeps a few hundred waiting workgroups from hammering the one
 // memory line the copy engines update.
-// End: every workgroup counts itself in *wg_count when done, and the one that sees wg_last
-// waits for the join, then stores epoch to *finished.
+// End: workgroup b counts itself in group counter b % kEndGroups (line g of wg_count, 256
+// bytes apart) when done; the last of a group (it sees grp_last[g]) counts the group in the
+// final counter (line kEndGroups), and the last group's workgroup (it sees all_last) waits for
+// the join, then stores epoch to *finished.  Spreading the counting keeps the last round's
+// workgroups from queueing on one atomic (one counter cost about 15 us per launch).  Every
+// counter is cumulative over the launches of a set; groups with no workgroup are skipped.
 // ts layout (wall-clock ticks, n = n_chunks): ts[c] = first time a tile of chunk c found it
 // ready (min), ts[n + c] = first tile start of chunk c (min), ts[2 n + c] = last tile end of
 // chunk c (max), ts[3 n] = start of workgroup 0.

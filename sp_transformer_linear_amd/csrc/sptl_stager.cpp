@@ -65,9 +65,10 @@ hsa_status_t find_agent(hsa_agent_t a, void *data) {
 }  // namespace
 
 // Pinned host words: set s finished at word 16 * s (one 128-byte line each).  Device
-// counters: finished workgroups of set s at word 32 * s.
+// counters: set s's kEndCounters end counters from word kSetCountWords * s, kEndLine apart.
 constexpr int kHostWords = 16 * kStageSets;
-constexpr int kCountWords = 32 * kStageSets;
+constexpr int kSetCountWords = kEndCounters * kEndLine;
+constexpr int kCountWords = kSetCountWords * kStageSets;
 constexpr double kReuseWaitSeconds = 30.0;  // longest a call waits for a set to come free
 
 struct SignalSet {
@@ -75,7 +76,8 @@ struct SignalSet {
     int64_t *val[kMaxPlanChunks + 1] = {};
     hipEvent_t fork = nullptr;
     uint64_t epoch = 0;       // of the last call begun on the set (0: never used)
-    uint64_t wg_total = 0;    // workgroups of all calls begun on the set
+    uint64_t grp_total[kEndGroups] = {};  // workgroups counted per group, all calls on the set
+    uint64_t all_total = 0;               // groups counted, all calls on the set
 };
 
 struct Job {
@@ -397,10 +399,18 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
     out->epoch = ++ss.epoch;
     out->fork = ss.fork;
     out->finished = const_cast<uint64_t *>(s->finished(set));
-    out->wg_count = s->counts + 32 * set;
-    out->wg_first = ss.wg_total;
-    out->wg_last = ss.wg_total + (uint64_t)workgroups - 1;
-    ss.wg_total += (uint64_t)workgroups;
+    out->wg_count = s->counts + (size_t)kSetCountWords * set;
+    int groups = 0;
+    for (int g = 0; g < kEndGroups; ++g) {
+        const int64_t n = workgroups > g ? (workgroups - g + kEndGroups - 1) / kEndGroups : 0;
+        out->grp_first[g] = ss.grp_total[g];
+        out->grp_last[g] = n ? ss.grp_total[g] + (uint64_t)n - 1 : ~0ull;
+        ss.grp_total[g] += (uint64_t)n;
+        groups += n ? 1 : 0;
+    }
+    out->all_first = ss.all_total;
+    out->all_last = ss.all_total + (uint64_t)groups - 1;
+    ss.all_total += (uint64_t)groups;
     return 0;
 }
 
@@ -416,7 +426,9 @@ int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> p
 
 void stager_cancel(SdmaStager *s, const StageCall &call) {
     // nothing ran on the set: mark the call finished and take back its workgroup count
-    s->sets[call.set].wg_total = call.wg_first;
+    SignalSet &ss = s->sets[call.set];
+    for (int g = 0; g < kEndGroups; ++g) ss.grp_total[g] = call.grp_first[g];
+    ss.all_total = call.all_first;
     __atomic_store_n(s->host_words + 16 * call.set, call.epoch, __ATOMIC_RELEASE);
 }
 

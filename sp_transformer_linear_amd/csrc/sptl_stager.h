@@ -27,10 +27,10 @@ constexpr int kStageSets = 4;  // calls that can be in flight on one stager
 // chunk c has landed; join likewise for the kJoinChunk pieces.  `fork` is recorded on the
 // compute stream right before the consuming kernel: once it completes, every earlier
 // operation on the stream has, so the copies may overwrite the gathered buffer.  The kernel
-// reports its own end through a word of pinned host memory: *wg_count counts finished
-// workgroups of all calls on the set, and the workgroup that raises it to wg_last + 1 waits
-// for the join and then stores `epoch` to *finished.  (No marker follows the kernel on the
-// stream: each marker costs several microseconds of GPU time.)
+// reports its own end through a word of pinned host memory: the end counters at wg_count
+// count finished workgroups in groups (see ChunkPlan), and the workgroup that completes the
+// count waits for the join and then stores `epoch` to *finished.  (No marker follows the
+// kernel on the stream: each marker costs several microseconds of GPU time.)
 struct StageCall {
     int set = -1;               // in [0, kStageSets)
     const int64_t *ready[kMaxPlanChunks] = {};
@@ -39,8 +39,10 @@ struct StageCall {
     uint64_t epoch = 0;
     uint64_t *finished = nullptr;
     uint64_t *wg_count = nullptr;
-    uint64_t wg_first = 0;
-    uint64_t wg_last = 0;
+    uint64_t grp_last[kEndGroups] = {};
+    uint64_t all_last = 0;
+    uint64_t grp_first[kEndGroups] = {};  // the set's totals before this call (for a cancel)
+    uint64_t all_first = 0;
 };
 
 class SdmaStager;
