@@ -110,6 +110,9 @@ class SdmaStager {
     std::condition_variable cv;
     std::deque<Job> queue;
     bool stop = false;
+    std::atomic<int> queued{0};        // jobs in the queue (polled without the lock)
+    std::atomic<bool> stop_flag{false};
+    static constexpr auto kIdleSpin = std::chrono::milliseconds(2);
     std::thread worker;
     std::atomic<bool> failed{false};
     unsigned next_engine = 0;       // worker thread only
@@ -139,12 +142,21 @@ class SdmaStager {
         (void)hipSetDevice(device);
         for (;;) {
             Job job;
+            // A call usually follows the last one within a millisecond; waking a blocked
+            // thread takes tens of microseconds, which would delay every chunk of that call.
+            // So poll for a while before blocking.
+            const auto idle0 = std::chrono::steady_clock::now();
+            for (unsigned i = 1; queued.load(std::memory_order_acquire) == 0 && !stop_flag.load(); ++i) {
+                __builtin_ia32_pause();
+                if ((i & 1023) == 0 && std::chrono::steady_clock::now() - idle0 > kIdleSpin) break;
+            }
             {
                 std::unique_lock<std::mutex> lk(mu);
                 cv.wait(lk, [&] { return stop || !queue.empty(); });
                 if (queue.empty()) return;  // stop requested and nothing left
                 job = std::move(queue.front());
                 queue.pop_front();
+                queued.fetch_sub(1, std::memory_order_relaxed);
             }
             SignalSet &ss = sets[job.set];
             static const bool trace = getenv("SPTL_STAGER_TRACE") != nullptr;
@@ -321,6 +333,7 @@ void stager_destroy(SdmaStager *s) {
     {
         std::lock_guard<std::mutex> lk(s->mu);
         s->stop = true;
+        s->stop_flag.store(true);
     }
     s->cv.notify_all();
     if (s->worker.joinable()) s->worker.join();
@@ -419,6 +432,7 @@ int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> p
     {
         std::lock_guard<std::mutex> lk(s->mu);
         s->queue.push_back(Job{call.set, call.fork, std::move(pieces)});
+        s->queued.fetch_add(1, std::memory_order_release);
     }
     s->cv.notify_one();
     return 0;
