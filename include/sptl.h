@@ -33,6 +33,8 @@
  *     device, created on first use.  Argument validation happens before that, so a call
  *     with invalid arguments makes no HIP call at all.
  *   - Sizes are element counts.  Empty work (seq_len == 0) is valid and enqueues nothing.
+ *   - A context serves one host thread at a time; different contexts (and the default
+ *     contexts of different devices) may be used from different threads concurrently.
  */
 #ifndef SPTL_H
 #define SPTL_H
@@ -67,6 +69,8 @@ typedef enum {
 #define SPTL_MAX_PARTIALS 16   /* partial sums per reduce call (tp)                      */
 #define SPTL_MAX_TP 64         /* TP degree of agmm_chunked and dtp_accumulate           */
 #define SPTL_MAX_CHUNKS 512    /* chunk count of agmm_chunked                            */
+#define SPTL_MAX_K 2097152     /* GEMM reduction size (hidden of agmm_chunked, k_local)  */
+#define SPTL_MAX_N 8388608     /* GEMM output width (n_local, hidden of gemm_partial)    */
 
 /* Create a context on HIP device `device` (events and small device buffers are created
  * now; the copy stream or SDMA stager on the first agmm_chunked call).  *out receives the

@@ -172,6 +172,10 @@ int check_gemm_dims(int64_t m, int64_t k, int64_t n) {
     if (k % 8 || n % 8)
         return fail(SPTL_E_DIVISIBILITY, "k=%lld and n=%lld must be multiples of 8", (long long)k,
                     (long long)n);
+    // the kernels address a tile's A rows and B rows with 32-bit byte offsets
+    if (k > SPTL_MAX_K || n > SPTL_MAX_N)
+        return fail(SPTL_E_SHAPE, "k=%lld or n=%lld above the limits %d and %d", (long long)k, (long long)n,
+                    SPTL_MAX_K, SPTL_MAX_N);
     // grid of 128 x 128 tiles must fit a 32-bit dimension
     if (((m + 127) / 128) * ((n + 127) / 128) > 0x7fffffffLL)
         return fail(SPTL_E_SHAPE, "GEMM too large for one launch");
@@ -340,8 +344,11 @@ int sptl_destroy(sptl_ctx *ctx) {
         if (e) (void)hipEventDestroy(e);
     for (auto *v : {&ctx->ready, &ctx->t_copy_start, &ctx->t_gemm_start, &ctx->t_gemm_end})
         for (hipEvent_t e : *v) (void)hipEventDestroy(e);
-    for (int d = 0; d < kMaxDevices; ++d)
-        if (g_default[d] == ctx) g_default[d] = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_default_mu);
+        for (int d = 0; d < kMaxDevices; ++d)
+            if (g_default[d] == ctx) g_default[d] = nullptr;
+    }
     delete ctx;
     return SPTL_OK;
 }

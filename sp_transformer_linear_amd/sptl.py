@@ -29,6 +29,7 @@ STATUS = {0: "SPTL_OK", 1: "SPTL_E_NULL", 2: "SPTL_E_SHAPE", 3: "SPTL_E_DIVISIBI
           4: "SPTL_E_ALIGN", 5: "SPTL_E_DTYPE", 6: "SPTL_E_RANGE", 7: "SPTL_E_HIP",
           8: "SPTL_E_UNSUPPORTED", 9: "SPTL_E_ASYNC"}
 MAX_PARTIALS, MAX_TP, MAX_CHUNKS = 16, 64, 512
+MAX_K, MAX_N = 2097152, 8388608
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64

@@ -62,6 +62,7 @@ def agmm_args(**kw):
     (dict(n_chunks=3), 3), (dict(seq_len=255), 3), (dict(hidden=252), 3), (dict(n_local=500), 3),
     (dict(y_dtype=2), 5), (dict(y_dtype=-1), 5), (dict(timing=2), 6),
     (dict(x_gathered=A + 8), 4), (dict(w=A + 2), 4), (dict(y=A + 4), 4), (dict(shard_src=[A, A + 8]), 4),
+    (dict(hidden=2097152 + 8), 2), (dict(n_local=8388608 + 8), 2),
 ])
 def test_agmm_validation(sptl, kw, status):
     rc = sptl.raw_agmm_chunked(**agmm_args(**kw))
@@ -73,6 +74,7 @@ def test_agmm_validation(sptl, kw, status):
     (dict(a=None), 1), (dict(w=None), 1), (dict(partial=None), 1),
     (dict(seq_len=-1), 2), (dict(k_local=0), 2), (dict(hidden=0), 2),
     (dict(k_local=12), 3), (dict(hidden=20), 3), (dict(out_dtype=7), 5), (dict(a=A + 2), 4),
+    (dict(k_local=2097152 + 8), 2), (dict(hidden=8388608 + 8), 2),
 ])
 def test_gemm_partial_validation(sptl, kw, status):
     d = dict(ctx=None, seq_len=64, k_local=64, hidden=64, a=A, w=A, partial=A, out_dtype=0, stream=None)
