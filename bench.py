@@ -156,7 +156,7 @@ def cpu_baseline(wl, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: runs on one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU path is not built.", file=sys.stderr)
         return 2
 

@@ -61,7 +61,7 @@ typedef enum {
     SPTL_E_RANGE = 6,        /* rank, tp, delta or module index out of range, or a pointer
                                 given/omitted against the delayed-TP schedule            */
     SPTL_E_HIP = 7,          /* a HIP runtime call failed                                 */
-    SPTL_E_UNSUPPORTED = 8,  /* valid request this build does not handle                  */
+    SPTL_E_UNSUPPORTED = 8,  /* valid request the library does not handle                */
     SPTL_E_ASYNC = 9         /* an asynchronous failure was recorded (see sptl_ctx_check)  */
 } sptl_status;
 
