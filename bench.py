@@ -105,6 +105,30 @@ def interval_hidden_fraction(tl):
     return None if total <= 0 else covered / total
 
 
+def max_sclk_mhz(device: int):
+    """Peak shader clock the HIP runtime reports for `device` (hipDeviceAttributeClockRate, kHz)."""
+    try:
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so.7")  # by soname: the runtime already loaded
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, device) == 0 and v.value > 0:
+            return round(v.value / 1000)
+    except OSError:
+        pass
+    return None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(wl, budget_s):
     """Time the float64 oracle on a bounded sample of the workload (1024-row blocks)."""
     import oracle.sptl_oracle as O
@@ -149,7 +173,7 @@ def cpu_baseline(wl, budget_s):
         "sample": f"float64 oracle gather-matmul, {done_rows} gathered rows in {passes} pass(es) over "
                   f"the {wl.M}-row workload ({blocks} blocks of <=1024 rows) x W[{wl.K},{wl.N}], "
                   f"{t_total:.1f} s; "
-                  f"host {platform.processor() or platform.machine()}",
+                  f"host {cpu_model()}",
     }
 
 
@@ -314,6 +338,20 @@ def main():
                                                    module_idx=delta, stream=cs, ctx=ctx), reps)
     del flush
 
+    # Staging check: with x_gathered poisoned (bf16 NaN everywhere, outside the timed region),
+    # one more call must land every chunk before its tiles read it, so y comes out bit for bit
+    # as in the timed region and no NaN is left in x_gathered.
+    y_ref = y_col.clone()
+    xg.fill_(float("nan"))
+    torch.cuda.synchronize()
+    agmm(w_col, y_col)
+    torch.cuda.synchronize()
+    ctx.check()
+    staging_check = {"x_gathered_poisoned_with": "NaN",
+                     "y_bitwise_equal": bool(torch.equal(y_col.view(torch.int16), y_ref.view(torch.int16))),
+                     "x_gathered_nan_free": not bool(torch.isnan(xg).any())}
+    del y_ref
+
     P = wl.P
     red_bytes = (P + 1) * M * wl.H * 2 + 2 * M * wl.H * 2 + wl.H * 2
     dtp_bytes = (1 + 1 + (wl.tp - 1)) * M * wl.H * 2 + 2 * M * wl.H * 2 + wl.H * 2
@@ -365,6 +403,7 @@ def main():
             "copy_hidden_frac_crosscheck": None if hidden_cross is None else round(hidden_cross, 4),
             "chunk_ready_ms": [round(r[1], 4) for r in tl],
             "chunk_gemm_ms": [[round(r[2], 4), round(r[3], 4)] for r in tl],
+            "staging_check": staging_check,
         },
         "gemm_partial": {"tflops": round(gemmp_tflops, 2), "frac_peak": round(gemmp_tflops / PEAK_BF16_TFLOPS, 4),
                          "ms": round(float(gemmp_ms.mean()), 4), "ms_median": round(float(np.median(gemmp_ms)), 4)},
@@ -379,7 +418,7 @@ def main():
                            "frac_hbm_cold": round(dtp_bytes / (dtp_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                            "bytes": dtp_bytes},
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
+                   "arch": getattr(props, "gcnArchName", ""), "max_sclk_mhz": max_sclk_mhz(0)},
         "input_gen_s": round(t_gen, 2),
     }
     if args.cpu_budget > 0:

@@ -21,9 +21,9 @@
  *   - Ownership: the caller owns every buffer and stream.  The library never allocates,
  *     frees or retains caller memory.  A context owns its own resources only: HIP events,
  *     a few small device buffers (an error word, chunk timestamps, 256 KiB of landed
- *     flags), and, from its first agmm_chunked call, a copy stream or an SDMA stager (HSA
- *     completion signals, 4 KiB of counters, one page of pinned host memory and one worker
- *     thread).  These are created on first use, never on later calls.  Inputs must stay
+ *     flags), and, from its first agmm_chunked call, a copy stream or an SDMA stager (4160
+ *     HSA completion signals, about 40 KiB of device counters and tables, one page of pinned
+ *     host memory and one worker thread).  These are created on first use, never on later calls.  Inputs must stay
  *     valid until the stream work of the call completes.
  *   - Every call is asynchronous (stream-ordered) and returns an sptl_status.  All
  *     arguments are validated BEFORE anything is enqueued: on any non-OK status nothing

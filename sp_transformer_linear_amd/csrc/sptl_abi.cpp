@@ -258,9 +258,13 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     std::string why;
     if (sptl::stager_begin(ctx->stager, pieces, sptl::gemm_workgroups(gp), &call, &why))
         return fail(SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
-    for (int c = 0; c < n; ++c) plan.ready[c] = call.ready[c];
+    for (int c = 0; c < n; ++c) {
+        plan.ready[c] = call.ready[c];
+        plan.ready_n[c] = call.ready_n[c];
+    }
     for (int s = 0; s < cpr; ++s) plan.ready[rank * cpr + s] = nullptr;  // read from the source
     plan.join = call.join;
+    plan.join_n = call.join_n;
     plan.flags = ctx->flags_dev + (size_t)call.set * sptl::kFlagSetWords;
     plan.epoch = call.epoch;
     plan.finished = call.finished;

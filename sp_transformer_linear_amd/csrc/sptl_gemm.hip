@@ -66,10 +66,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Bounded spin until *word <= 0 (an SDMA completion signal counting down copy pieces).  On
-// timeout sets *plan.err and returns, so every wave exits.  The polls are relaxed (coherent
-// loads that bypass the caches, no cache invalidation); one acquire fence follows the last
-// poll, so a waiting workgroup does not invalidate its L2 while others stream through it.
+// Bounded spins on SDMA completion signals: `words` lists the value words of one chunk's copy
+// pieces (n <= 64), each 1 until its piece lands and then <= 0.  The waits are run by one whole
+// wave, lane l watching piece l, so one vector load checks every piece.  On timeout a wait sets
+// *plan.err and returns, so every wave exits.  The polls are relaxed (coherent loads that bypass
+// the caches, no cache invalidation); one acquire fence follows the last poll, so a waiting
+// workgroup does not invalidate its L2 while others stream through it.
 __device__ __forceinline__ bool timed_out(uint64_t t0, const ChunkPlan &plan) {
     if (wall_clock64() - t0 <= plan.timeout_ticks) return false;
     __hip_atomic_store(plan.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -81,10 +83,18 @@ __device__ __forceinline__ void poll_pause(const ChunkPlan &plan) {
     for (int i = 0; i < plan.poll_sleep; ++i) __builtin_amdgcn_s_sleep(127);
 }
 
-__device__ __forceinline__ void wait_ready(const int64_t *word, const ChunkPlan &plan) {
-    if (!word) return;
+// Whether every piece has landed; the same answer in every lane of the calling wave.
+__device__ __forceinline__ bool pieces_landed(const int64_t *const *words, int n) {
+    const int lane = threadIdx.x & 63;
+    const bool mine = lane >= n || __hip_atomic_load(words[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) <= 0;
+    return __all(mine);
+}
+
+// Called by a whole wave.
+__device__ __forceinline__ void wait_ready(const int64_t *const *words, int n, const ChunkPlan &plan) {
+    if (!words) return;
     const uint64_t t0 = wall_clock64();
-    while (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) > 0) {
+    while (!pieces_landed(words, n)) {
         if (timed_out(t0, plan)) break;
         poll_pause(plan);
     }
@@ -92,21 +102,25 @@ __device__ __forceinline__ void wait_ready(const int64_t *word, const ChunkPlan 
 }
 
 // Wait of workgroup `bid` for chunk `chunk` through the replicated landed flags (see
-// ChunkPlan); falls back to wait_ready when the launch has no flags.
+// ChunkPlan), run by the workgroup's first wave; falls back to wait_ready when the launch has
+// no flags.
 constexpr unsigned kSignalPollEvery = 16;
+static_assert(kFlagReplicas <= 64, "one lane per flag replica");
 
 __device__ __forceinline__ void wait_chunk(const ChunkPlan &plan, int chunk, int bid) {
-    const int64_t *word = plan.ready[chunk];
-    if (!word) return;
-    if (!plan.flags) return wait_ready(word, plan);
+    const int64_t *const *words = plan.ready[chunk];
+    if (!words) return;
+    const int n = plan.ready_n[chunk];
+    if (!plan.flags) return wait_ready(words, n, plan);
+    const int lane = threadIdx.x & 63;
     uint64_t *mine = plan.flags + (size_t)(bid % kFlagReplicas) * kFlagStride + chunk;
     const uint64_t t0 = wall_clock64();
     for (unsigned it = (unsigned)bid;; ++it) {
         if (__hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == plan.epoch) break;
-        if (it % kSignalPollEvery == 0 && __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) <= 0) {
+        if (it % kSignalPollEvery == 0 && pieces_landed(words, n)) {
             __atomic_thread_fence(__ATOMIC_ACQ_REL);  // the flags are set after the landing was seen
-            for (int r = 0; r < kFlagReplicas; ++r)
-                __hip_atomic_store(plan.flags + (size_t)r * kFlagStride + chunk, plan.epoch, __ATOMIC_RELAXED,
+            if (lane < kFlagReplicas)
+                __hip_atomic_store(plan.flags + (size_t)lane * kFlagStride + chunk, plan.epoch, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_SYSTEM);
             break;
         }
@@ -188,9 +202,9 @@ __device__ __forceinline__ void tile_begin(const GemmProblem &p, int tiles_m, in
                      ? plan.own_a + ((int64_t)own_idx * plan.chunk_rows + (int64_t)sub * BM) * p.lda
                      : p.a + m0 * p.lda;
         if (plan.ts && bid == 0 && tid == 0) plan.ts[3 * plan.n_chunks] = wall_clock64();
-        if (tid == 0) {
+        if (tid < 64) {
             wait_chunk(plan, chunk, bid);  // this chunk's copy pieces have landed
-            if (plan.ts) {
+            if (plan.ts && tid == 0) {
                 const unsigned long long now = wall_clock64();
                 atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + chunk), now);
                 atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + plan.n_chunks + chunk), now);
@@ -229,25 +243,31 @@ __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin 
             }
         }
     }
-    if (CHUNKED && threadIdx.x == 0) {
+    if (CHUNKED && threadIdx.x < 64) {
         const ChunkPlan &plan = p.plan;
         const int chunk = o.chunk;
-        if (plan.ts)
-            atomicMax(reinterpret_cast<unsigned long long *>(plan.ts + 2 * plan.n_chunks + chunk),
-                      (unsigned long long)wall_clock64());
         // The last workgroup to finish waits for every copy of the call (own slot included),
         // so the kernel ends only after all of them, then reports the call done.  The counts
         // are relaxed: a workgroup counts itself after its chunk wait has returned, so a full
         // count means that no workgroup of the call still reads the set's signals or flags,
         // which is all the report promises (the outputs are ordered by the kernel's end).  A
         // release or acquire per workgroup would write back or invalidate its L2 each time.
-        const int g = blockIdx.x % kEndGroups;
-        if (__hip_atomic_fetch_add(plan.wg_count + g * kEndLine, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                plan.grp_last[g] &&
-            __hip_atomic_fetch_add(plan.wg_count + kEndGroups * kEndLine, 1ull, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT) == plan.all_last) {
-            wait_ready(plan.join, plan);
-            __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        // Lane 0 counts; the first wave then waits for the join together.
+        int last = 0;
+        if (threadIdx.x == 0) {
+            if (plan.ts)
+                atomicMax(reinterpret_cast<unsigned long long *>(plan.ts + 2 * plan.n_chunks + chunk),
+                          (unsigned long long)wall_clock64());
+            const int g = blockIdx.x % kEndGroups;
+            last = __hip_atomic_fetch_add(plan.wg_count + g * kEndLine, 1ull, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == plan.grp_last[g] &&
+                   __hip_atomic_fetch_add(plan.wg_count + kEndGroups * kEndLine, 1ull, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == plan.all_last;
+        }
+        if (__shfl(last, 0, 64)) {
+            wait_ready(plan.join, plan.join_n, plan);
+            if (threadIdx.x == 0)
+                __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
 }

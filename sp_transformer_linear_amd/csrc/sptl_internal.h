@@ -20,17 +20,19 @@ constexpr size_t kFlagSetWords = (size_t)kFlagReplicas * kFlagStride;
 
 // Chunk-ordered GEMM over a gathered activation (the column GEMM of the chunked all-gather +
 // matmul).  Row tiles are processed in `order` (own chunks first, then the peers' chunks in
-// arrival order); the workgroups of a tile of chunk c wait, with a bounded spin, until
-// *ready[c] <= 0 (an SDMA completion signal counting down the chunk's copy pieces) before
-// reading its rows.  Rows of chunks [own_first, own_first + own_count) are read from own_a
+// arrival order); the workgroups of a tile of chunk c wait, with a bounded spin, until every
+// word of ready[c][0 .. ready_n[c]) is <= 0 (the SDMA completion signals of the chunk's copy
+// pieces, one per piece) before reading its rows.  Rows of chunks [own_first, own_first + own_count) are read from own_a
 // (this rank's shard), all others from GemmProblem::a (the gathered buffer).
 struct ChunkPlan {
     int chunk_rows;                          // rows per chunk, a multiple of the tile height
     int n_chunks;                            // <= kMaxPlanChunks
     int own_first, own_count;
     int order[kMaxPlanChunks];               // processing position -> chunk
-    const int64_t *ready[kMaxPlanChunks];    // per chunk; nullptr: no wait
-    const int64_t *join;                     // waited for by the last workgroup to finish
+    const int64_t *const *ready[kMaxPlanChunks];  // per chunk: piece signal words; nullptr: no wait
+    int ready_n[kMaxPlanChunks];
+    const int64_t *const *join;              // waited for by the last workgroup to finish
+    int join_n;
     const uint16_t *own_a;
     int *err;                                // set to 1 when a wait times out
     uint64_t timeout_ticks;                  // wall-clock ticks of the bounded waits
@@ -44,8 +46,8 @@ struct ChunkPlan {
     uint64_t *ts;                            // optional per-chunk timestamps (see below)
 };
 // Waiting: a workgroup of chunk c polls its replica of c's landed flag about every
-// microsecond and, once every 16 polls (phase set by its index), c's completion word itself.
-// The first workgroup to see the word reach zero sets every replica to `epoch`.  Spreading
+// microsecond and, once every 16 polls (phase set by its index), c's completion words
+// themselves.  The first workgroup to see them all reach zero sets every replica to `epoch`.  Spreading
 // the polls over replicas keeps a few hundred waiting workgroups from hammering the one
 // memory line the copy engines update.
 // End: workgroup b counts itself in group counter b % kEndGroups (line g of wg_count, 256

@@ -4,9 +4,8 @@
 // request #5513, "Observations" and "Recommendations": only the copy-engine gather helped).
 // On MI355X one SDMA engine moves ~57 GB/s device to device and a HIP copy stream uses one
 // engine at a time, so a chunk is striped over all available engines (14 on MI355X), driven
-// through HSA, each piece decrementing the chunk's completion signal.  The signals are
-// GPU-only HSA signals, whose values live in device memory where the chunk-ordered GEMM
-// polls them.
+// through HSA, each piece completing a signal of its own.  The signals are GPU-only HSA
+// signals, whose values live in device memory where the chunk-ordered GEMM polls them.
 //
 // Ordering: copies must not overwrite the gathered buffer while earlier work on the compute
 // stream still reads it.  A HIP event recorded at the call's fork point (right before the
@@ -71,9 +70,11 @@ constexpr int kSetCountWords = kEndCounters * kEndLine;
 constexpr int kCountWords = kSetCountWords * kStageSets;
 constexpr double kReuseWaitSeconds = 30.0;  // longest a call waits for a set to come free
 
+constexpr int kSetSignals = (kMaxPlanChunks + 1) * kMaxPieces;
+
 struct SignalSet {
-    hsa_signal_t sig[kMaxPlanChunks + 1] = {};
-    int64_t *val[kMaxPlanChunks + 1] = {};
+    hsa_signal_t sig[kMaxPlanChunks + 1][kMaxPieces] = {};
+    int64_t **words = nullptr;  // device: value word of sig[c][p] at words[c * kMaxPieces + p]
     hipEvent_t fork = nullptr;
     uint64_t epoch = 0;       // of the last call begun on the set (0: never used)
     uint64_t grp_total[kEndGroups] = {};  // workgroups counted per group, all calls on the set
@@ -174,13 +175,14 @@ class SdmaStager {
                 const uint32_t eng = engines[next_engine++ % engines.size()];
                 if (ok)
                     ok = hsa_amd_memory_async_copy_on_engine(pc.dst, agent, pc.src, agent, pc.bytes, 0, nullptr,
-                                                             ss.sig[pc.chunk], (hsa_amd_sdma_engine_id_t)eng,
-                                                             true) == HSA_STATUS_SUCCESS;
+                                                             ss.sig[pc.chunk][pc.piece],
+                                                             (hsa_amd_sdma_engine_id_t)eng, true) == HSA_STATUS_SUCCESS;
                 if (!ok) {
                     // release every waiter of this call; the call's results are invalid and
                     // the failure is reported through stager_failed
                     failed = true;
-                    for (int c = 0; c <= kMaxPlanChunks; ++c) hsa_signal_store_screlease(ss.sig[c], 0);
+                    for (int c = 0; c <= kMaxPlanChunks; ++c)
+                        for (int q = 0; q < kMaxPieces; ++q) hsa_signal_store_screlease(ss.sig[c][q], 0);
                     break;
                 }
             }
@@ -287,15 +289,17 @@ SdmaStager *stager_create(int device, std::string *err) {
         }
     }
     for (SignalSet &ss : s->sets) {
-        for (int c = 0; c <= kMaxPlanChunks && ok; ++c) {
-            hsa_status_t st = hsa_amd_signal_create(0, 0, nullptr, HSA_AMD_SIGNAL_AMD_GPU_ONLY, &ss.sig[c]);
+        int64_t *host_words[kSetSignals];
+        for (int i = 0; i < kSetSignals && ok; ++i) {
+            hsa_signal_t &sg = ss.sig[i / kMaxPieces][i % kMaxPieces];
+            hsa_status_t st = hsa_amd_signal_create(0, 0, nullptr, HSA_AMD_SIGNAL_AMD_GPU_ONLY, &sg);
             if (st != HSA_STATUS_SUCCESS) {
                 why = "hsa_amd_signal_create(GPU_ONLY) status " + std::to_string((int)st);
                 ok = false;
                 break;
             }
             volatile hsa_signal_value_t *vp = nullptr;
-            st = hsa_amd_signal_value_pointer(ss.sig[c], &vp);
+            st = hsa_amd_signal_value_pointer(sg, &vp);
             if (st != HSA_STATUS_SUCCESS || !vp) {
                 why = "hsa_amd_signal_value_pointer status " + std::to_string((int)st);
                 ok = false;
@@ -310,7 +314,12 @@ SdmaStager *stager_create(int device, std::string *err) {
                 ok = false;
                 break;
             }
-            ss.val[c] = (int64_t *)vp;
+            host_words[i] = (int64_t *)vp;
+        }
+        if (ok && (hipMalloc(&ss.words, sizeof host_words) != hipSuccess ||
+                   hipMemcpy(ss.words, host_words, sizeof host_words, hipMemcpyHostToDevice) != hipSuccess)) {
+            why = "cannot store the signal word table";
+            ok = false;
         }
         if (ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) {
             why = "hipEventCreate failed";
@@ -341,7 +350,9 @@ void stager_destroy(SdmaStager *s) {
         SignalSet &ss = s->sets[set];
         if (ss.epoch && s->host_words) (void)spin_until(s->finished(set), ss.epoch, kReuseWaitSeconds);
         for (int c = 0; c <= kMaxPlanChunks; ++c)
-            if (ss.sig[c].handle) hsa_signal_destroy(ss.sig[c]);
+            for (int q = 0; q < kMaxPieces; ++q)
+                if (ss.sig[c][q].handle) hsa_signal_destroy(ss.sig[c][q]);
+        if (ss.words) (void)hipFree(ss.words);
         if (ss.fork) (void)hipEventDestroy(ss.fork);
     }
     if (s->scratch) (void)hipFree(s->scratch);
@@ -374,16 +385,18 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
         const long v = e ? strtol(e, nullptr, 10) : 1;
         return (size_t)(v >= 1 && v <= 16 ? v : 1);
     }();
-    const size_t E = s->engines.size() * split;
+    size_t E = s->engines.size() * split;
+    if (E > (size_t)kMaxPieces) E = kMaxPieces;
     for (const CopyPiece &c : copies) {
         size_t n = c.bytes / (kMinPiece / split);
         n = n < 1 ? 1 : n > E ? E : n;
-        // equal pieces rounded to 256 bytes; the last takes the remainder
+        // equal pieces rounded to 256 bytes; the last takes the remainder (so at most n pieces)
         const size_t step = ((c.bytes / n) + 255) & ~(size_t)255;
         size_t off = 0;
+        int piece = 0;
         while (off < c.bytes) {
             const size_t b = c.bytes - off < step ? c.bytes - off : step;
-            out.push_back({static_cast<char *>(c.dst) + off, static_cast<const char *>(c.src) + off, b, c.chunk});
+            out.push_back({static_cast<char *>(c.dst) + off, static_cast<const char *>(c.src) + off, b, c.chunk, piece++});
             off += b;
         }
     }
@@ -392,6 +405,14 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
 
 int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t workgroups, StageCall *out,
                  std::string *err) {
+    int count[kMaxPlanChunks + 1] = {};
+    for (const CopyPiece &p : pieces) {
+        if (p.chunk < 0 || p.chunk > kMaxPlanChunks || p.piece != count[p.chunk] || p.piece >= kMaxPieces) {
+            *err = "copy pieces out of order or too many per chunk";
+            return -1;
+        }
+        count[p.chunk]++;
+    }
     int set;
     {
         std::lock_guard<std::mutex> lk(s->mu);
@@ -403,12 +424,15 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
         *err = "an earlier staged call did not finish";
         return -1;
     }
-    int64_t count[kMaxPlanChunks + 1] = {};
-    for (const CopyPiece &p : pieces) count[p.chunk]++;
-    for (int c = 0; c <= kMaxPlanChunks; ++c) hsa_signal_store_screlease(ss.sig[c], count[c]);
+    for (int c = 0; c <= kMaxPlanChunks; ++c)
+        for (int q = 0; q < count[c]; ++q) hsa_signal_store_screlease(ss.sig[c][q], 1);
     out->set = set;
-    for (int c = 0; c < kMaxPlanChunks; ++c) out->ready[c] = count[c] ? ss.val[c] : nullptr;
-    out->join = count[kJoinChunk] ? ss.val[kJoinChunk] : nullptr;
+    for (int c = 0; c < kMaxPlanChunks; ++c) {
+        out->ready[c] = count[c] ? ss.words + (size_t)c * kMaxPieces : nullptr;
+        out->ready_n[c] = count[c];
+    }
+    out->join = count[kJoinChunk] ? ss.words + (size_t)kJoinChunk * kMaxPieces : nullptr;
+    out->join_n = count[kJoinChunk];
     out->epoch = ++ss.epoch;
     out->fork = ss.fork;
     out->finished = const_cast<uint64_t *>(s->finished(set));

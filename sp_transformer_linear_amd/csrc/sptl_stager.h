@@ -12,19 +12,26 @@
 
 namespace sptl {
 
-// One staging copy: `bytes` from src to dst, counted against chunk `chunk` (kJoinChunk for
+// One staging copy: `bytes` from src to dst, piece `piece` of chunk `chunk` (kJoinChunk for
 // copies that only the end of the call waits for).
 struct CopyPiece {
     void *dst;
     const void *src;
     size_t bytes;
     int chunk;
+    int piece;
 };
 constexpr int kJoinChunk = kMaxPlanChunks;
-constexpr int kStageSets = 4;  // calls that can be in flight on one stager
+constexpr int kStageSets = 4;   // calls that can be in flight on one stager
+constexpr int kMaxPieces = 16;  // copy pieces per chunk, each with a completion signal of its own
+static_assert(kMaxPieces <= 64, "the GEMM watches a chunk's pieces with one lane each");
 
-// One call's view of its completion-signal set.  ready[c] reaches <= 0 once every piece of
-// chunk c has landed; join likewise for the kJoinChunk pieces.  `fork` is recorded on the
+// One call's view of its completion-signal set.  ready[c] is a device array of the value
+// words of chunk c's ready_n[c] piece signals (null: chunk c has no piece); each word goes from
+// 1 to <= 0 when its piece has landed.  join / join_n likewise for the kJoinChunk pieces.  One
+// signal per copy, not one signal per chunk counted down by its pieces: under a tool that
+// intercepts the copies (rocprofv3 --memory-copy-trace), a signal shared by several copies
+// read as complete before all of them had landed, while a signal of one copy stays exact.  `fork` is recorded on the
 // compute stream right before the consuming kernel: once it completes, every earlier
 // operation on the stream has, so the copies may overwrite the gathered buffer.  The kernel
 // reports its own end through a word of pinned host memory: the end counters at wg_count
@@ -33,8 +40,10 @@ constexpr int kStageSets = 4;  // calls that can be in flight on one stager
 // kernel on the stream: each marker costs several microseconds of GPU time.)
 struct StageCall {
     int set = -1;               // in [0, kStageSets)
-    const int64_t *ready[kMaxPlanChunks] = {};
-    const int64_t *join = nullptr;
+    const int64_t *const *ready[kMaxPlanChunks] = {};
+    int ready_n[kMaxPlanChunks] = {};
+    const int64_t *const *join = nullptr;
+    int join_n = 0;
     hipEvent_t fork = nullptr;
     uint64_t epoch = 0;
     uint64_t *finished = nullptr;
@@ -52,9 +61,9 @@ SdmaStager *stager_create(int device, std::string *err);
 void stager_destroy(SdmaStager *s);
 int stager_engine_count(const SdmaStager *s);
 
-// Splits every chunk copy into pieces striped over the engines (`chunk_bytes` per chunk in
-// submission order) and returns them with their chunk ids; the result is what
-// stager_submit expects.
+// Splits every chunk copy into at most kMaxPieces pieces striped over the engines and returns
+// them in submission order with their chunk and piece ids; the result is what stager_begin and
+// stager_submit expect.
 std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies);
 
 // Reserves a completion-signal set for one call whose consuming kernel has `workgroups`
