@@ -112,6 +112,7 @@ class SdmaStager {
     std::deque<Job> queue;
     bool stop = false;
     std::atomic<int> queued{0};        // jobs in the queue (polled without the lock)
+    bool wake = false;                 // a call has begun: leave the blocking wait (guarded by mu)
     std::atomic<bool> stop_flag{false};
     static constexpr auto kIdleSpin = std::chrono::milliseconds(2);
     std::thread worker;
@@ -153,8 +154,12 @@ class SdmaStager {
             }
             {
                 std::unique_lock<std::mutex> lk(mu);
-                cv.wait(lk, [&] { return stop || !queue.empty(); });
-                if (queue.empty()) return;  // stop requested and nothing left
+                cv.wait(lk, [&] { return stop || !queue.empty() || wake; });
+                wake = false;
+                if (queue.empty()) {
+                    if (stop) return;  // stop requested and nothing left
+                    continue;          // woken ahead of a call: poll for its job
+                }
                 job = std::move(queue.front());
                 queue.pop_front();
                 queued.fetch_sub(1, std::memory_order_relaxed);
@@ -418,7 +423,11 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
         std::lock_guard<std::mutex> lk(s->mu);
         set = s->next_set;
         s->next_set = (s->next_set + 1) % kSets;
+        s->wake = true;
     }
+    // A blocked worker takes tens of microseconds to wake up: wake it now, so that it is
+    // polling by the time this call's job is queued (after the kernel launch).
+    s->cv.notify_one();
     SignalSet &ss = s->sets[set];
     if (ss.epoch && !spin_until(s->finished(set), ss.epoch, kReuseWaitSeconds)) {
         *err = "an earlier staged call did not finish";
