@@ -46,6 +46,7 @@ namespace sptl {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -58,13 +59,6 @@ constexpr int kOutOfRange = 0x7ffffff0;   // an offset past any num_records used
 constexpr int kBand = 4;                  // tile rows per band of the plain tile order
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
 
 // Bounded spins on SDMA completion signals: `words` lists the value words of one chunk's copy
 // pieces (n <= 64), each 1 until its piece lands and then <= 0.  The waits are run by one whole
@@ -225,20 +219,45 @@ __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin 
     const int64_t m0 = o.m0, n0 = o.n0;
     // 32 x 32 MFMA result layout: lane l holds column l % 32; register r holds row
     // 8 (r / 4) + 4 (l / 32) + r % 4.
+    if constexpr (OUT_F32) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t col = n0 + wn0 + j * 32 + (lane & 31);
-            if (col >= p.n) continue;
+            for (int j = 0; j < TN; ++j) {
+                const int64_t col = n0 + wn0 + j * 32 + (lane & 31);
+                if (col >= p.n) continue;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (row < p.m) {
-                    if constexpr (OUT_F32)
-                        static_cast<float *>(p.c)[row * p.ldc + col] = acc[i][j][r];
-                    else
-                        static_cast<uint16_t *>(p.c)[row * p.ldc + col] = f32_to_bf16(acc[i][j][r]);
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t row = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    if (row < p.m) static_cast<float *>(p.c)[row * p.ldc + col] = acc[i][j][r];
+                }
+            }
+        }
+    } else {
+        // bf16: lanes 2 q and 2 q + 1 hold adjacent columns.  One DPP swap per pair of values
+        // gives the even lane both columns of rows r = 0..7 and the odd lane both columns of
+        // rows r = 8..15, so every store writes two columns (4 bytes; N is a multiple of 8, so
+        // the pair is whole).  The conversion is the native nearest-even one, two values at a
+        // time.
+        const bool odd = lane & 1;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t col = n0 + wn0 + j * 32 + (lane & 31 & ~1);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float send = odd ? acc[i][j][k] : acc[i][j][k + 8];
+                    const float recv = __builtin_bit_cast(
+                        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+                    const float mine = odd ? acc[i][j][k + 8] : acc[i][j][k];
+                    const int r = odd ? k + 8 : k;
+                    const int64_t row = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    bf16x2_t v;
+                    v[0] = (__bf16)(odd ? recv : mine);
+                    v[1] = (__bf16)(odd ? mine : recv);
+                    if (row < p.m && col < p.n)
+                        *reinterpret_cast<bf16x2_t *>(static_cast<uint16_t *>(p.c) + row * p.ldc + col) = v;
                 }
             }
         }
@@ -285,6 +304,9 @@ struct Cfg {
     static constexpr int B_ROW = BN * 2;                    // bytes per B row in LDS
     static constexpr int A_VEC = BM * BK / 8 / THREADS;     // 16-byte A vectors per thread
     static constexpr int B_VEC = BN * BK / 8 / THREADS;
+    // transposed-B staging: one thread per 8 k x 8 n block of B, the other threads A only
+    static constexpr int BT_B_THREADS = (BK / 8) * (BN / 8);
+    static constexpr int BT_VEC = 8;                          // 16-byte loads per thread
     static_assert(BK == 64 || BK == 32, "stage depth");
     static_assert(TM >= 1 && TN >= 1 && A_VEC >= 1 && B_VEC >= 1, "tile shape");
     static_assert(BN >= 128, "B swizzle needs at least 8 units of 32 bytes per row");
@@ -294,17 +316,29 @@ struct Cfg {
     static __device__ __forceinline__ int aswz(int r) { return BK == 64 ? swz(r) : (r >> 2) & 3; }
 };
 
-template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED, int BK = kBK, int WPE = 1>
+// BT: B is transposed on its way into LDS (see load_stage), so that B fragments, like A
+// fragments, are single ds_read_b128s of 8 consecutive k.  On gfx950 the LDS issues about one
+// instruction per 4-5 clocks per CU whatever its width, so this cuts the LDS instructions per
+// MFMA from 1.5 to 1.0.  The fragments, the MFMA instruction and the K order are unchanged,
+// so the result bits are the same.
+// LSPREAD: 0 issues a stage's global loads before its first MFMA; n > 0 issues one load after
+// every n-th MFMA instead, so that the CU's vector-memory queue sees a steady stream rather
+// than every wave's loads at once.
+template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED, int BK = kBK, int WPE = 1, bool BT = false,
+          int LSPREAD = 0>
 __global__ void __launch_bounds__(64 * WGM * WGN, WPE)
 gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
     using T = Cfg<BM, BN, WGM, WGN, BK>;
-    constexpr int A_VEC = T::A_VEC, B_VEC = T::B_VEC;
+    constexpr int A_VEC = BT ? T::BT_VEC : T::A_VEC, B_VEC = BT ? 0 : T::B_VEC;
+    static_assert(!BT || (T::THREADS == 2 * T::BT_B_THREADS && BK == 64), "transposed-B thread split");
     __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    // BT: the first half of the waves stage B blocks, the second half A rows (wave-uniform)
+    const bool b_role = BT && __builtin_amdgcn_readfirstlane(wave) < T::BT_B_THREADS / 64;
     const int wm0 = (wave / WGN) * T::WM;
     const int wn0 = (wave % WGN) * T::WN;
 
@@ -317,16 +351,41 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     // Global -> register staging.  Thread t loads A vectors q = t + THREADS i (row q / CPR,
     // 16-byte chunk q % CPR) and B vectors q = t + THREADS i (row q / (BN / 8), columns
     // 8 (q % (BN / 8)) ..).
-    int a_voff[A_VEC], a_kc[A_VEC], a_lds[A_VEC];
+    //
+    // BT: thread t < BT_B_THREADS owns the 8 x 8 block of k rows 8 (t / (BN / 8)) .. + 7 and
+    // columns 8 (t % (BN / 8)) .. + 7: it loads the block's 8 rows (A_VEC loads of 16 bytes),
+    // transposes it in registers and writes 8 columns of 8 consecutive k.  LDS then holds B
+    // as BN rows (n) of BK k, with the A layout and swizzle.  The other threads load A
+    // vectors q = (t - BT_B_THREADS) + (THREADS - BT_B_THREADS) i.
+    //   Offsets are kept per role as one base plus a stride: load i of a B thread reads k row
+    //   8 rg + i (stride ldb), load i of an A thread reads row r0 + 32 i (stride 32 lda); the
+    //   LDS address of B column cb 8 + j is (bt_lds ^ (j << 4)) + 128 j (the swizzle of column
+    //   8 cb + j is rg ^ cb ^ j), of A row r0 + 32 i is bt_lds + 4096 i with the row's swizzle,
+    //   which alternates with i.
+    int a_voff[BT ? 1 : A_VEC], a_kc[BT ? 1 : A_VEC], a_lds[BT ? 2 : A_VEC];
+    int bt_stride = 0;
+    if constexpr (BT) {
+        const int cb = tid % (BN / 8), rg = (tid / (BN / 8)) & 7;
+        const int bq = (tid - T::BT_B_THREADS) & (T::THREADS - T::BT_B_THREADS - 1);
+        const int r0 = bq / T::CPR, c = bq % T::CPR;  // A: rows r0 + 32 i, chunk c
+        const int64_t n = n0 + cb * 8;
+        bt_stride = b_role ? (int)(p.ldb * 2) : (int)(32 * p.lda * 2);
+        a_kc[0] = c * 8;
+        a_voff[0] = b_role ? (n < p.n ? (int)((rg * 8 * p.ldb + n) * 2) : kOutOfRange) : (int)((r0 * p.lda + c * 8) * 2);
+        a_lds[0] = b_role ? T::A_STAGE + cb * 8 * T::A_ROW + (((rg ^ cb) & 7) << 4)
+                          : r0 * T::A_ROW + ((c ^ T::aswz(r0)) << 4);
+        a_lds[1] = r0 * T::A_ROW + ((c ^ T::aswz(r0 + 32)) << 4);  // A rows r0 + 32 (odd i)
+    } else {
 #pragma unroll
-    for (int i = 0; i < A_VEC; ++i) {
-        const int q = tid + i * T::THREADS;
-        const int row = q / T::CPR, c = q % T::CPR;
-        a_kc[i] = c * 8;
-        a_voff[i] = (int)((row * p.lda + c * 8) * 2);
-        a_lds[i] = row * T::A_ROW + ((c ^ T::aswz(row)) << 4);
+        for (int i = 0; i < A_VEC; ++i) {
+            const int q = tid + i * T::THREADS;
+            const int row = q / T::CPR, c = q % T::CPR;
+            a_kc[i] = c * 8;
+            a_voff[i] = (int)((row * p.lda + c * 8) * 2);
+            a_lds[i] = row * T::A_ROW + ((c ^ T::aswz(row)) << 4);
+        }
     }
-    int b_voff[B_VEC], b_lds[B_VEC];
+    int b_voff[B_VEC > 0 ? B_VEC : 1], b_lds[B_VEC > 0 ? B_VEC : 1];
 #pragma unroll
     for (int i = 0; i < B_VEC; ++i) {
         const int q = tid + i * T::THREADS;
@@ -335,7 +394,7 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         b_voff[i] = n < p.n ? (int)((row * p.ldb + n) * 2) : kOutOfRange;
         b_lds[i] = row * T::B_ROW + (((piece >> 1) ^ ((row & 3) << 1)) << 5) + ((piece & 1) << 4);
     }
-    u32x4_t ra[A_VEC], rb[B_VEC];
+    u32x4_t ra[A_VEC], rb[B_VEC > 0 ? B_VEC : 1];
 
     const int nk = (int)((p.k + BK - 1) / BK);
     // Loads stage kt into registers.  Stages past the end (kt >= nk) get an empty buffer
@@ -347,19 +406,52 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(a_tile + k0), (short)0, (int)a_bytes, kRsrcFlags);
         const bool k_tail = k0 + BK > p.k;
-#pragma unroll
-        for (int i = 0; i < A_VEC; ++i) {
-            const int off = (k_tail && k0 + a_kc[i] >= p.k) ? kOutOfRange : a_voff[i];
-            ra[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0));
-        }
         const int64_t k_rows = !live ? 0 : (p.k - k0) < BK ? (p.k - k0) : BK;
         __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(p.b + k0 * p.ldb), (short)0, (int)(k_rows * p.ldb * 2), kRsrcFlags);
+        if constexpr (BT) {
+            // one descriptor per wave: B rows past K lie beyond br's range and read zero
+            const __amdgpu_buffer_rsrc_t r = b_role ? br : ar;
+            // A chunk past K, or B columns past N: every load of the thread reads zero
+            // (kOutOfRange + 7 strides stays below 2^32, so it stays out of range)
+            const int base = !b_role && k_tail && k0 + a_kc[0] >= p.k ? kOutOfRange : a_voff[0];
 #pragma unroll
-        for (int i = 0; i < B_VEC; ++i)
-            rb[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(br, b_voff[i], 0, 0));
+            for (int i = 0; i < A_VEC; ++i)
+                ra[i] = __builtin_bit_cast(u32x4_t,
+                                           __builtin_amdgcn_raw_buffer_load_b128(r, base + i * bt_stride, 0, 0));
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_VEC; ++i) {
+                const int off = (k_tail && k0 + a_kc[i] >= p.k) ? kOutOfRange : a_voff[i];
+                ra[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0));
+            }
+#pragma unroll
+            for (int i = 0; i < B_VEC; ++i)
+                rb[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(br, b_voff[i], 0, 0));
+        }
     };
     auto store_stage = [&](char *dst) {
+        if constexpr (BT) {
+            if (b_role) {
+                // 8 x 8 transpose of 16-bit elements: ra[i] holds k row i (columns 0..7, two per
+                // word); column j's word w takes element j of rows 2 w and 2 w + 1.  Each column
+                // is stored as soon as it is formed.
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    u32x4_t t;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        t[w] = __builtin_amdgcn_perm(ra[2 * w + 1][j >> 1], ra[2 * w][j >> 1],
+                                                     (j & 1) ? 0x07060302u : 0x05040100u);
+                    *reinterpret_cast<u32x4_t *>(dst + ((a_lds[0] ^ (j << 4)) + j * T::A_ROW)) = t;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < A_VEC; ++i)
+                    *reinterpret_cast<u32x4_t *>(dst + a_lds[i & 1] + i * 32 * T::A_ROW) = ra[i];
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < A_VEC; ++i) *reinterpret_cast<u32x4_t *>(dst + a_lds[i]) = ra[i];
 #pragma unroll
@@ -377,11 +469,14 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     }
     const int rr = lane & 15;
     const int b_k0 = 8 * (lane >> 5) + (rr >> 2);  // k within a 16-k step, first half
-    int b_col_off[T::TN];
+    int b_col_off[T::TN], bt_row_off[T::TN], bt_swz[T::TN];
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) {
         const int n = wn0 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (rr & 3);
         b_col_off[j] = (((n >> 4) ^ ((b_k0 & 3) << 1)) << 5) + (n & 15) * 2;
+        const int nt = wn0 + j * 32 + (lane & 31);  // BT: lane l reads column l % 32
+        bt_row_off[j] = nt * T::A_ROW;
+        bt_swz[j] = T::aswz(nt);
     }
 
     f32x16_t acc[T::TM][T::TN];
@@ -400,10 +495,15 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         }
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
-            const char *base = bs + (s * 16 + b_k0) * T::B_ROW + b_col_off[j];
-            bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
-            bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * T::B_ROW));
-            bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (BT) {
+                const int ch = (2 * s + a_hi) ^ bt_swz[j];
+                bfr[j] = *reinterpret_cast<const bf16x8_t *>(bs + bt_row_off[j] + ch * 16);
+            } else {
+                const char *base = bs + (s * 16 + b_k0) * T::B_ROW + b_col_off[j];
+                bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
+                bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * T::B_ROW));
+                bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
         }
     };
 
@@ -426,10 +526,11 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     };
     // Instruction order of a stage (see the file comment).
     auto pin_schedule = [&]() {
-        constexpr int kDsPerStep = T::TM + 2 * T::TN;
+        constexpr int kDsPerStep = T::TM + (BT ? 1 : 2) * T::TN;
         constexpr int kMfmaPerStep = T::TM * T::TN;
         constexpr int kSteps = BK / 16;
-        __builtin_amdgcn_sched_group_barrier(0x020, A_VEC + B_VEC, 0);  // global loads first
+        constexpr int kLoads = A_VEC + B_VEC;
+        if (LSPREAD == 0) __builtin_amdgcn_sched_group_barrier(0x020, kLoads, 0);  // global loads first
         __builtin_amdgcn_sched_group_barrier(0x100, kDsPerStep, 0);
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
@@ -437,6 +538,9 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
             for (int m = 0; m < kMfmaPerStep; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 if (s + 1 < kSteps && m < kDsPerStep) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                const int q = s * kMfmaPerStep + m;
+                if (LSPREAD > 0 && q % (LSPREAD > 0 ? LSPREAD : 1) == 0 && q / (LSPREAD > 0 ? LSPREAD : 1) < kLoads)
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         }
     };
@@ -643,7 +747,7 @@ __global__ void fill_u64_kernel(uint64_t *p, int64_t n, uint64_t v) {
     if (i < n) p[i] = v;
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK = kBK, int WPE = 1>
+template <int BM, int BN, int WGM, int WGN, int BK = kBK, int WPE = 1, bool BT = false, int LSPREAD = 0>
 hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
     const int64_t tm = (p.m + BM - 1) / BM, tn = (p.n + BN - 1) / BN;
     const int64_t nt = tm * tn;
@@ -652,13 +756,13 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
     const dim3 grid((unsigned)nt), block(64 * WGM * WGN);
     const bool chunked = p.plan.chunk_rows != 0;
     if (p.c_f32 && chunked)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, true, BK, WPE>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, true, BK, WPE, BT, LSPREAD>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else if (p.c_f32)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, false, BK, WPE>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, false, BK, WPE, BT, LSPREAD>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else if (chunked)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, true, BK, WPE>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, true, BK, WPE, BT, LSPREAD>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, false, BK, WPE>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, false, BK, WPE, BT, LSPREAD>), grid, block, 0, stream, p, (int)tm, (int)tn);
     return hipGetLastError();
 }
 
@@ -683,7 +787,7 @@ hipError_t launch_dma(const GemmProblem &p, hipStream_t stream) {
 
 // Tile configurations.  All share the MFMA instruction and the K order.
 enum Config { k256x256w2x2, k256x256w2x4, k256x256w4x2, k256x128w4x2, k256x128w4x1, k128x128w2x2, k256x256dma,
-              k128x256w2x2k32, k256x256w4x2k32, kNumConfigs };
+              k128x256w2x2k32, k256x256w4x2k32, k256x256bt, k256x256il2, k256x256il4, k256x256btil2, kNumConfigs };
 
 const char *config_name(int c) {
     switch (c) {
@@ -695,6 +799,10 @@ const char *config_name(int c) {
         case k256x256dma: return "256x256dma";
         case k128x256w2x2k32: return "128x256w2x2k32";
         case k256x256w4x2k32: return "256x256w4x2k32";
+        case k256x256bt: return "256x256bt";
+        case k256x256il2: return "256x256il2";
+        case k256x256il4: return "256x256il4";
+        case k256x256btil2: return "256x256btil2";
         default: return "128x128w2x2";
     }
 }
@@ -758,6 +866,10 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile) 
         case k256x256dma: return launch_dma<4, 2, 4>(p, stream);
         case k128x256w2x2k32: return launch_cfg<128, 256, 2, 2, 32, 2>(p, stream);
         case k256x256w4x2k32: return launch_cfg<256, 256, 4, 2, 32>(p, stream);
+        case k256x256bt: return launch_cfg<256, 256, 4, 2, kBK, 1, true>(p, stream);
+        case k256x256il2: return launch_cfg<256, 256, 4, 2, kBK, 1, false, 2>(p, stream);
+        case k256x256il4: return launch_cfg<256, 256, 4, 2, kBK, 1, false, 4>(p, stream);
+        case k256x256btil2: return launch_cfg<256, 256, 4, 2, kBK, 1, true, 2>(p, stream);
         default: return launch_cfg<128, 128, 2, 2>(p, stream);
     }
 }
