@@ -394,7 +394,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_bf16_kernel, chunk-ordered launch of agmm_chunked (one per call)",
+            "kernel": "gemm_ring_kernel, chunk-ordered launch of agmm_chunked (one per call)",
             "achieved": round(agmm_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -595,10 +595,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Direct-to-LDS variant of the 256 x 256 tile (WGM x WGN waves).  K is walked in stages of
-// 32 held in a ring of SLOTS LDS slots; the buffer loads write LDS directly (64 lanes x 16
-// bytes = 1 KB per instruction, lane l at byte 16 l), so no register staging and no LDS
-// store instructions are needed, and SLOTS - 1 stages are in flight while one is consumed.
+// Ring kernel: the 256 x 256 tile with WGM x WGN waves, K walked in 32-deep stages held in a
+// ring of SLOTS LDS slots that direct-to-LDS buffer loads fill (64 lanes x 16 bytes = 1 KB per
+// instruction, lane l at byte 16 l), so no register staging and no LDS store instructions are
+// needed.  Stage kt + 1 is made visible (own loads waited for, then a barrier) at the top of
+// stage kt, and both of its fragment steps are read during stage kt: every fragment is read
+// two MFMA steps before its use, which covers the LDS latency of a CU whose 8 waves all read
+// at once.  Three fragment register sets rotate, so the loop is unrolled three times.
 // The per-lane global addresses apply the LDS swizzles in reverse:
 //   A slot: 256 rows of 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
 //           (a ds_read_b128 by 16 lanes then covers all 16 bank groups once);
@@ -606,11 +609,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Same MFMA instruction and K order as every other configuration.
 template <int WGM, int WGN, int SLOTS, bool OUT_F32, bool CHUNKED>
 __global__ void __launch_bounds__(64 * WGM * WGN)
-gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
+gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BM = 256, BN = 256, TM = BM / WGM / 32, TN = BN / WGN / 32;
     constexpr int NBLK = 16 / (WGM * WGN);   // 1 KB blocks per operand per wave per stage
-    static_assert(NBLK * WGM * WGN == 16 && SLOTS >= 3 && SLOTS * 2 * kDmaSlotBytes <= 160 * 1024, "shape");
+    static_assert(NBLK * WGM * WGN == 16 && SLOTS >= 4 && SLOTS * 2 * kDmaSlotBytes <= 160 * 1024, "shape");
     constexpr int B_ROW = BN * 2;
     constexpr int SLOT = 2 * kDmaSlotBytes;  // ring slot: A (16 KB) then B (16 KB)
     __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT];
@@ -626,7 +629,7 @@ gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     const uint16_t *a_tile = o.a_tile;
     const int rows_valid = o.rows_valid;
 
-    // Per-lane source offsets of this wave's two A blocks (16 rows each) and two B blocks
+    // Per-lane source offsets of this wave's NBLK A blocks (16 rows each) and NBLK B blocks
     // (2 k-rows each) of a stage.
     int a_off[NBLK], a_kc[NBLK], b_off[NBLK];
 #pragma unroll
@@ -645,8 +648,9 @@ gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     const int nk = (int)((p.k + kDmaBK - 1) / kDmaBK);
     const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * NBLK) * 1024;  // this wave's first block
 
-    // Stage kt into ring slot `slot`.  Stages past the end read an empty range (zeros), so
-    // every stage issues exactly four loads per wave and the wait counts below stay fixed.
+    // Stage kt into ring slot `slot`.  Stages past the end (kt >= nk) read an empty range
+    // (zeros), so every stage issues exactly 2 NBLK loads per wave and the wait counts stay
+    // fixed.
     auto issue = [&](int kt, int slot) {
         const bool live = kt < nk;
         const int64_t k0 = live ? (int64_t)kt * kDmaBK : 0;
@@ -665,7 +669,7 @@ gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         for (int t = 0; t < NBLK; ++t) load_to_lds(br, lb + t * 1024, b_off[t]);
     };
 
-    // fragment read addresses (within a slot); step s of a stage adds 16 k
+    // fragment read addresses (within a slot); step st of a stage adds 16 k
     int a_addr[2][TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -701,41 +705,71 @@ gemm_dma_kernel(GemmProblem p, int tiles_m, int tiles_n) {
             bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    auto compute = [&](const char *slot) {
-        bf16x8_t af[2][TM], bfr[2][TN];
-        load_frags(slot, 0, af[0], bfr[0]);
-        load_frags(slot, 1, af[1], bfr[1]);
+    constexpr int kDs = TM + 2 * TN, kMf = TM * TN;
+    auto mfmas = [&](const bf16x8_t *af, const bf16x8_t *bfr) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[st][i], bfr[st][j], acc[i][j], 0, 0, 0);
-        // order: step 0's fragment reads, then each MFMA of step 0 with one fragment read of
-        // step 1, then step 1's MFMAs
-        constexpr int kDs = TM + 2 * TN, kMf = TM * TN;
-        __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+    // Each MFMA of a step is followed by one fragment read; with_loads also places one of the
+    // stage's global loads after every other MFMA.
+    auto pin = [&](bool with_loads) {
 #pragma unroll
         for (int m = 0; m < kMf; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (m < kDs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (with_loads && (m & 1) && m / 2 < 2 * NBLK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
-    };
-    // One stage: wait for this wave's loads of stage kt (the two later stages may stay in
-    // flight), make every wave's loads visible and retire the slot the previous stage read,
-    // start stage kt + 3 into it, then compute stage kt.
-    auto step = [&](int kt, int slot) {
-        wait_vmcnt<2 * NBLK * (SLOTS - 2)>();  // 2 NBLK loads per stage, SLOTS - 2 stages after kt
-        __syncthreads();
-        issue(kt + SLOTS - 1, slot == 0 ? SLOTS - 1 : slot - 1);
-        compute(smem + slot * SLOT);
     };
 
+    bf16x8_t fa[3][TM], fb[3][TN];
 #pragma unroll
     for (int st = 0; st < SLOTS - 1; ++st) issue(st, st);
-    for (int kt = 0, slot = 0; kt < nk; ++kt, slot = slot + 1 == SLOTS ? 0 : slot + 1) step(kt, slot);
+    wait_vmcnt<2 * NBLK * (SLOTS - 2)>();  // stage 0 landed (stages 1 .. SLOTS - 2 may be in flight)
+    __syncthreads();
+    load_frags(smem, 0, fa[0], fb[0]);
+    load_frags(smem, 1, fa[1], fb[1]);
+    // Stage kt: fragment sets S0 = (kt, step 0) and S1 = (kt, step 1) are loaded.  Wait for
+    // this wave's loads of stage kt + 1 and make every wave's visible (the barrier also
+    // retires the slot of stage kt - 1, whose fragments were read during stage kt - 2); start
+    // stage kt + SLOTS - 1 into that slot; read (kt + 1, 0) into S2 during step 0 and
+    // (kt + 1, 1) into S0 during step 1.
+    auto stage = [&](int kt, int slot, int S0, int S1, int S2) {
+        const int nslot = slot + 1 == SLOTS ? 0 : slot + 1;
+        const int fslot = slot == 0 ? SLOTS - 1 : slot - 1;
+        wait_vmcnt<2 * NBLK * (SLOTS - 3)>();  // SLOTS - 3 later stages may stay in flight
+        __syncthreads();
+        issue(kt + SLOTS - 1, fslot);
+        load_frags(smem + nslot * SLOT, 0, fa[S2], fb[S2]);
+        mfmas(fa[S0], fb[S0]);
+        pin(true);
+        load_frags(smem + nslot * SLOT, 1, fa[S0], fb[S0]);
+        mfmas(fa[S1], fb[S1]);
+        pin(false);
+    };
+    int kt = 0, slot = 0;
+    auto advance = [&]() {
+        ++kt;
+        slot = slot + 1 == SLOTS ? 0 : slot + 1;
+    };
+    while (kt + 3 <= nk) {
+        stage(kt, slot, 0, 1, 2);
+        advance();
+        stage(kt, slot, 2, 0, 1);
+        advance();
+        stage(kt, slot, 1, 2, 0);
+        advance();
+    }
+    if (kt < nk) {
+        stage(kt, slot, 0, 1, 2);
+        advance();
+    }
+    if (kt < nk) {
+        stage(kt, slot, 2, 0, 1);
+        advance();
+    }
     // no load may still be writing this workgroup's LDS when it exits
     wait_vmcnt<0>();
     tile_end<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc);
@@ -767,7 +801,7 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
 }
 
 template <int WGM, int WGN, int SLOTS>
-hipError_t launch_dma(const GemmProblem &p, hipStream_t stream) {
+hipError_t launch_ring(const GemmProblem &p, hipStream_t stream) {
     const int64_t tm = (p.m + 255) / 256, tn = (p.n + 255) / 256;
     const int64_t nt = tm * tn;
     if (nt == 0) return hipSuccess;
@@ -775,18 +809,18 @@ hipError_t launch_dma(const GemmProblem &p, hipStream_t stream) {
     const dim3 grid((unsigned)nt), block(64 * WGM * WGN);
     const bool chunked = p.plan.chunk_rows != 0;
     if (p.c_f32 && chunked)
-        hipLaunchKernelGGL((gemm_dma_kernel<WGM, WGN, SLOTS, true, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_ring_kernel<WGM, WGN, SLOTS, true, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else if (p.c_f32)
-        hipLaunchKernelGGL((gemm_dma_kernel<WGM, WGN, SLOTS, true, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_ring_kernel<WGM, WGN, SLOTS, true, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else if (chunked)
-        hipLaunchKernelGGL((gemm_dma_kernel<WGM, WGN, SLOTS, false, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_ring_kernel<WGM, WGN, SLOTS, false, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
     else
-        hipLaunchKernelGGL((gemm_dma_kernel<WGM, WGN, SLOTS, false, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_ring_kernel<WGM, WGN, SLOTS, false, false>), grid, block, 0, stream, p, (int)tm, (int)tn);
     return hipGetLastError();
 }
 
 // Tile configurations.  All share the MFMA instruction and the K order.
-enum Config { k256x256w2x2, k256x256w2x4, k256x256w4x2, k256x128w4x2, k256x128w4x1, k128x128w2x2, k256x256dma,
+enum Config { k256x256w2x2, k256x256w2x4, k256x256w4x2, k256x128w4x2, k256x128w4x1, k128x128w2x2, k256x256ring,
               k128x256w2x2k32, k256x256w4x2k32, k256x256bt, k256x256il2, k256x256il4, k256x256btil2, kNumConfigs };
 
 const char *config_name(int c) {
@@ -796,7 +830,7 @@ const char *config_name(int c) {
         case k256x256w4x2: return "256x256w4x2";
         case k256x128w4x2: return "256x128w4x2";
         case k256x128w4x1: return "256x128w4x1";
-        case k256x256dma: return "256x256dma";
+        case k256x256ring: return "256x256ring";
         case k128x256w2x2k32: return "128x256w2x2k32";
         case k256x256w4x2k32: return "256x256w4x2k32";
         case k256x256bt: return "256x256bt";
@@ -825,15 +859,15 @@ int resolve(const GemmProblem &p, GemmTile t) {
     if (p.plan.chunk_rows) {  // chunk-ordered: the tile height must divide the chunk
         if (forced_config() >= 0 && p.plan.chunk_rows % config_rows(forced_config()) == 0)
             return forced_config();
-        return p.plan.chunk_rows % 256 == 0 ? k256x256w4x2 : k128x128w2x2;
+        return p.plan.chunk_rows % 256 == 0 ? k256x256ring : k128x128w2x2;
     }
     if (forced_config() >= 0) return forced_config();
-    if (t == GemmTile::T256x256) return k256x256w4x2;
+    if (t == GemmTile::T256x256) return k256x256ring;
     if (t == GemmTile::T128x128) return k128x128w2x2;
     // One wave of 256 x 256 tiles needs about one workgroup per CU (256 on MI355X); below
     // that, 128 x 128 tiles keep every CU busy.
     const int64_t big = ((p.m + 255) / 256) * ((p.n + 255) / 256);
-    return big >= 240 ? k256x256w4x2 : k128x128w2x2;
+    return big >= 240 ? k256x256ring : k128x128w2x2;
 }
 
 }  // namespace
@@ -863,7 +897,7 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile) 
         case k256x256w4x2: return launch_cfg<256, 256, 4, 2>(p, stream);
         case k256x128w4x2: return launch_cfg<256, 128, 4, 2>(p, stream);
         case k256x128w4x1: return launch_cfg<256, 128, 4, 1>(p, stream);
-        case k256x256dma: return launch_dma<4, 2, 4>(p, stream);
+        case k256x256ring: return launch_ring<4, 2, 4>(p, stream);
         case k128x256w2x2k32: return launch_cfg<128, 256, 2, 2, 32, 2>(p, stream);
         case k256x256w4x2k32: return launch_cfg<256, 256, 4, 2, 32>(p, stream);
         case k256x256bt: return launch_cfg<256, 256, 4, 2, kBK, 1, true>(p, stream);
