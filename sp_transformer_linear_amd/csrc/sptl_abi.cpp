@@ -3,6 +3,7 @@
 // layout, ownership and error behaviour, are in include/sptl.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -26,6 +27,7 @@ struct sptl_ctx {
     uint64_t *ts_dev = nullptr;         // [3 * kMaxPlanChunks + 1] chunk timestamps
     uint64_t *flags_dev = nullptr;      // landed flags, kFlagSetWords per stager set
     int wallclock_khz = 100000;
+    int64_t cus = 256;                  // compute units of the device
     uint64_t wait_timeout_us = 10000000;  // bound on one chunk wait inside the GEMM (10 s)
     int t_mode = 0;                     // 0: event timeline, 1: chunk-ordered timeline
     int t_rank_first = 0, t_rank_count = 0;
@@ -124,6 +126,9 @@ int create_ctx(sptl_ctx **out, int device) {
     if (!rc) {
         (void)hipDeviceGetAttribute(&c->wallclock_khz, hipDeviceAttributeWallClockRate, device);
         if (c->wallclock_khz <= 0) c->wallclock_khz = 100000;
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && cus > 0)
+            c->cus = cus;
         const char *e = getenv("SPTL_STAGING");
         c->events_only = e && !strcmp(e, "events");
         // SPTL_WAIT_TIMEOUT_US shortens the bound on a chunk wait (failure-path tests)
@@ -227,7 +232,6 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     }
     if (!own_aliased)
         copies.push_back({xg + (size_t)rank * cpr * chunk_elems, shard_src[rank], chunk_bytes * cpr, sptl::kJoinChunk});
-    std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies);
     const int n = n_chunks;
     gp.a = xg;
     gp.b = static_cast<const uint16_t *>(w);
@@ -254,9 +258,21 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     plan.poll_sleep = poll_sleep;
     plan.ts = timing ? ctx->ts_dev : nullptr;
 
+    // The GEMM's first round of tiles (one per CU) spans the own chunks and the first `lead`
+    // peer chunks; those peers are staged together so that the round starts complete as early
+    // as the engines allow.  The round is sized for an output at least `hidden` wide, so that a
+    // narrower weight stages its chunks the same way as a full-width one.
+    const int64_t wgs = sptl::gemm_workgroups(gp);
+    sptl::GemmProblem wide = gp;
+    wide.n = std::max(gp.n, gp.k);
+    const int64_t per_chunk = std::max<int64_t>(1, sptl::gemm_workgroups(wide) / n);
+    const int64_t first_round = (ctx->cus + per_chunk - 1) / per_chunk;
+    const int lead = (int)std::max<int64_t>(1, std::min<int64_t>(first_round - cpr, (int64_t)(n - cpr)));
+    std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies, lead);
+
     sptl::StageCall call;
     std::string why;
-    if (sptl::stager_begin(ctx->stager, pieces, sptl::gemm_workgroups(gp), &call, &why))
+    if (sptl::stager_begin(ctx->stager, pieces, wgs, &call, &why))
         return fail(SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
     for (int c = 0; c < n; ++c) {
         plan.ready[c] = call.ready[c];

@@ -20,6 +20,7 @@ struct CopyPiece {
     size_t bytes;
     int chunk;
     int piece;
+    int engine = 0;  // index into the stager's engines (set by stager_plan)
 };
 constexpr int kJoinChunk = kMaxPlanChunks;
 constexpr int kStageSets = 4;   // calls that can be in flight on one stager
@@ -61,10 +62,13 @@ SdmaStager *stager_create(int device, std::string *err);
 void stager_destroy(SdmaStager *s);
 int stager_engine_count(const SdmaStager *s);
 
-// Splits every chunk copy into at most kMaxPieces pieces striped over the engines and returns
-// them in submission order with their chunk and piece ids; the result is what stager_begin and
-// stager_submit expect.
-std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies);
+// Splits every chunk copy into at most kMaxPieces pieces and assigns each piece an engine; returns
+// them in submission order with their chunk and piece ids, which is what stager_begin and
+// stager_submit expect.  The first `lead` copies are split together, about one piece per
+// engine in proportion to their sizes, so that they land at about the same time, as early as
+// the engines allow; every later copy is striped over all engines (piece p on engine p), and
+// each engine takes its pieces in submission order.
+std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies, int lead = 1);
 
 // Reserves a completion-signal set for one call whose consuming kernel has `workgroups`
 // workgroups, and arms it with the number of pieces per chunk.  Blocks (bounded) while the
