@@ -37,6 +37,7 @@
 //            cycle; a transposing read by lanes 0..31 touches rows kb..kb+3 at units u
 //            (lanes 0..15) and u + 1 (lanes 16..31), u even, which this map sends to 8
 //            distinct 32-byte bank groups.
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -124,6 +125,32 @@ __device__ __forceinline__ void wait_chunk(const ChunkPlan &plan, int chunk, int
     __atomic_thread_fence(__ATOMIC_ACQUIRE);
 }
 
+// Non-blocking form of wait_chunk, run by a whole wave: whether chunk `chunk` has landed now
+// (setting the landed flags when this wave is the first to see it).  When it returns true the
+// copied rows are visible to the workgroup's later loads (after a barrier).
+__device__ __forceinline__ bool chunk_ready_now(const ChunkPlan &plan, int chunk, int bid) {
+    const int64_t *const *words = plan.ready[chunk];
+    if (!words) return true;
+    const int n = plan.ready_n[chunk];
+    bool ok;
+    if (plan.flags &&
+        __hip_atomic_load(plan.flags + (size_t)(bid % kFlagReplicas) * kFlagStride + chunk, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_SYSTEM) == plan.epoch) {
+        ok = true;
+    } else {
+        ok = pieces_landed(words, n);
+        if (ok && plan.flags) {
+            __atomic_thread_fence(__ATOMIC_ACQ_REL);
+            const int lane = threadIdx.x & 63;
+            if (lane < kFlagReplicas)
+                __hip_atomic_store(plan.flags + (size_t)lane * kFlagStride + chunk, plan.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+    if (ok) __atomic_thread_fence(__ATOMIC_ACQUIRE);
+    return ok;
+}
+
 // Output tile of this workgroup and, for a chunk-ordered launch, the wait for its chunk.
 struct TileOrigin {
     int64_t m0, n0;          // output tile origin
@@ -132,9 +159,9 @@ struct TileOrigin {
     int chunk;               // chunk-ordered launches: the tile's chunk, else -1
 };
 
+// Origin of tile `bid` (the workgroup index of a one-tile-per-workgroup launch).
 template <int BM, int BN, bool CHUNKED>
-__device__ __forceinline__ void tile_begin(const GemmProblem &p, int tiles_m, int tiles_n, TileOrigin &o) {
-    const int bid = blockIdx.x, tid = threadIdx.x;
+__device__ __forceinline__ void tile_origin(const GemmProblem &p, int tiles_m, int tiles_n, TileOrigin &o, int bid) {
     const ChunkPlan &plan = p.plan;
     int64_t &m0 = o.m0, &n0 = o.n0;
     const uint16_t *&a_tile = o.a_tile;
@@ -195,24 +222,39 @@ __device__ __forceinline__ void tile_begin(const GemmProblem &p, int tiles_m, in
         a_tile = (own_idx >= 0 && own_idx < plan.own_count)
                      ? plan.own_a + ((int64_t)own_idx * plan.chunk_rows + (int64_t)sub * BM) * p.lda
                      : p.a + m0 * p.lda;
+    }
+}
+
+// Chunk-ordered launches: the wait of tile `bid` for its chunk (first wave), then a barrier.
+template <bool CHUNKED>
+__device__ __forceinline__ void tile_wait(const GemmProblem &p, const TileOrigin &o, int bid) {
+    if constexpr (CHUNKED) {
+        const ChunkPlan &plan = p.plan;
+        const int tid = threadIdx.x;
         if (plan.ts && bid == 0 && tid == 0) plan.ts[3 * plan.n_chunks] = wall_clock64();
         if (tid < 64) {
-            wait_chunk(plan, chunk, bid);  // this chunk's copy pieces have landed
+            wait_chunk(plan, o.chunk, bid);  // this chunk's copy pieces have landed
             if (plan.ts && tid == 0) {
                 const unsigned long long now = wall_clock64();
-                atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + chunk), now);
-                atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + plan.n_chunks + chunk), now);
+                atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + o.chunk), now);
+                atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + plan.n_chunks + o.chunk), now);
             }
         }
         __syncthreads();
     }
 }
 
+template <int BM, int BN, bool CHUNKED>
+__device__ __forceinline__ void tile_begin(const GemmProblem &p, int tiles_m, int tiles_n, TileOrigin &o) {
+    tile_origin<BM, BN, CHUNKED>(p, tiles_m, tiles_n, o, blockIdx.x);
+    tile_wait<CHUNKED>(p, o, blockIdx.x);
+}
+
 // Stores the tile's accumulators and, for a chunk-ordered launch, records the tile's end and
 // completes the call when this is its last workgroup.
 template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED>
 __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin &o,
-                                         const f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+                                         const f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32], int bid) {
     constexpr int TM = BM / WGM / 32, TN = BN / WGN / 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm0 = (wave / WGN) * (BM / WGM), wn0 = (wave % WGN) * (BN / WGN);
@@ -277,7 +319,7 @@ __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin 
             if (plan.ts)
                 atomicMax(reinterpret_cast<unsigned long long *>(plan.ts + 2 * plan.n_chunks + chunk),
                           (unsigned long long)wall_clock64());
-            const int g = blockIdx.x % kEndGroups;
+            const int g = bid % kEndGroups;
             last = __hip_atomic_fetch_add(plan.wg_count + g * kEndLine, 1ull, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT) == plan.grp_last[g] &&
                    __hip_atomic_fetch_add(plan.wg_count + kEndGroups * kEndLine, 1ull, __ATOMIC_RELAXED,
@@ -558,7 +600,7 @@ gemm_bf16_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         __syncthreads();
     }
 
-    tile_end<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc);
+    tile_end<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc, blockIdx.x);
 #endif
 }
 
@@ -602,6 +644,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // stage kt, and both of its fragment steps are read during stage kt: every fragment is read
 // two MFMA steps before its use, which covers the LDS latency of a CU whose 8 waves all read
 // at once.  Three fragment register sets rotate, so the loop is unrolled three times.
+//
+// Persistent: workgroup b takes tiles b, b + G, b + 2 G, ... (G = gridDim.x, a multiple of 8,
+// so every tile keeps the XCD of a one-tile-per-workgroup launch).  The ring runs on across
+// tiles: SLOTS - 1 stages before the end of a tile its first wave checks, without waiting,
+// whether the next tile's chunk has landed; if it has, the ring's next SLOTS - 1 stages are
+// the next tile's first stages, so the next tile starts with its data in LDS.  If it has not,
+// those stages read zeros and the next tile waits and loads as the first one does.
+//
 // The per-lane global addresses apply the LDS swizzles in reverse:
 //   A slot: 256 rows of 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
 //           (a ds_read_b128 by 16 lanes then covers all 16 bank groups once);
@@ -617,21 +667,18 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     constexpr int B_ROW = BN * 2;
     constexpr int SLOT = 2 * kDmaSlotBytes;  // ring slot: A (16 KB) then B (16 KB)
     __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT];
+    __shared__ int next_ok_lds;              // the first wave's prefetch decision
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm0 = (wave / WGN) * (BM / WGM);
     const int wn0 = (wave % WGN) * (BN / WGN);
+    const int nt = tiles_m * tiles_n;
+    const int nk = (int)((p.k + kDmaBK - 1) / kDmaBK);
 
-    TileOrigin o;
-    tile_begin<BM, BN, CHUNKED>(p, tiles_m, tiles_n, o);
-    const int64_t n0 = o.n0;
-    const uint16_t *a_tile = o.a_tile;
-    const int rows_valid = o.rows_valid;
-
-    // Per-lane source offsets of this wave's NBLK A blocks (16 rows each) and NBLK B blocks
-    // (2 k-rows each) of a stage.
-    int a_off[NBLK], a_kc[NBLK], b_off[NBLK];
+    // Per-lane offsets of this wave's NBLK A blocks (16 rows each) and NBLK B blocks (2 k-rows
+    // each) of a stage, relative to a tile's origin.
+    int a_off[NBLK], a_kc[NBLK];
 #pragma unroll
     for (int t = 0; t < NBLK; ++t) {
         const int blk = wave * NBLK + t;
@@ -639,23 +686,17 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         const int c = (lane & 3) ^ ((row >> 2) & 3);
         a_kc[t] = c * 8;
         a_off[t] = (int)((row * p.lda + c * 8) * 2);
-        const int krow = blk * 2 + (lane >> 5);
-        const int q = lane & 31;
-        const int u = (q >> 1) ^ ((krow & 3) << 1);
-        const int64_t n = n0 + u * 16 + (q & 1) * 8;
-        b_off[t] = n < p.n ? (int)((krow * p.ldb + n) * 2) : kOutOfRange;
     }
-    const int nk = (int)((p.k + kDmaBK - 1) / kDmaBK);
     const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * NBLK) * 1024;  // this wave's first block
 
-    // Stage kt into ring slot `slot`.  Stages past the end (kt >= nk) read an empty range
-    // (zeros), so every stage issues exactly 2 NBLK loads per wave and the wait counts stay
-    // fixed.
-    auto issue = [&](int kt, int slot) {
-        const bool live = kt < nk;
+    // Stage kt of the tile at `o` into ring slot `slot`; live = false (or kt >= nk) reads an
+    // empty range (zeros), so every stage issues exactly 2 NBLK loads per wave and the wait
+    // counts stay fixed.
+    auto issue = [&](const TileOrigin &o, bool live_tile, int kt, int slot) {
+        const bool live = live_tile && kt < nk;
         const int64_t k0 = live ? (int64_t)kt * kDmaBK : 0;
-        const int64_t a_bytes = live ? ((int64_t)rows_valid * p.lda - k0) * 2 : 0;
-        const u32x4_t ar = buffer_desc(a_tile + k0, (uint32_t)a_bytes);
+        const int64_t a_bytes = live ? ((int64_t)o.rows_valid * p.lda - k0) * 2 : 0;
+        const u32x4_t ar = buffer_desc(o.a_tile + k0, (uint32_t)a_bytes);
         const bool k_tail = k0 + kDmaBK > p.k;
         const int64_t k_rows = !live ? 0 : (p.k - k0) < kDmaBK ? (p.k - k0) : kDmaBK;
         const u32x4_t br = buffer_desc(p.b + k0 * p.ldb, (uint32_t)(k_rows * p.ldb * 2));
@@ -666,7 +707,15 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
             load_to_lds(ar, la + t * 1024, off);
         }
 #pragma unroll
-        for (int t = 0; t < NBLK; ++t) load_to_lds(br, lb + t * 1024, b_off[t]);
+        for (int t = 0; t < NBLK; ++t) {
+            // B block: k-rows 2 blk, 2 blk + 1 (lane / 32); lanes q, q + 1 read the two halves
+            // of the swizzled 32-byte unit (q / 2) of that row (recomputed here rather than kept
+            // in registers across the tiles)
+            const int krow = (wave * NBLK + t) * 2 + (lane >> 5);
+            const int q = lane & 31;
+            const int64_t n = o.n0 + (((q >> 1) ^ ((krow & 3) << 1)) * 16 + (q & 1) * 8);
+            load_to_lds(br, lb + t * 1024, n < p.n ? (int)((krow * p.ldb + n) * 2) : kOutOfRange);
+        }
     };
 
     // fragment read addresses (within a slot); step st of a stage adds 16 k
@@ -687,13 +736,6 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     }
 
     f32x16_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
     auto load_frags = [&](const char *slot, int st, bf16x8_t *af, bf16x8_t *bfr) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(slot + a_addr[st][i]);
@@ -723,56 +765,81 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
             if (with_loads && (m & 1) && m / 2 < 2 * NBLK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     };
+    auto slot_of = [&](int s) { return s % SLOTS; };
 
     bf16x8_t fa[3][TM], fb[3][TN];
+    int slot0 = 0;            // ring slot of the current tile's stage 0
+    bool prefetched = false;  // the current tile's stages 0 .. SLOTS - 2 are already in flight
+    const int kt_check = nk - SLOTS;  // stage during which the next tile's chunk is checked
+    for (int vb = blockIdx.x; vb < nt; vb += gridDim.x) {
+        TileOrigin o, on;
+        tile_origin<BM, BN, CHUNKED>(p, tiles_m, tiles_n, o, vb);
+        const int vn = vb + (int)gridDim.x;
+        const bool has_next = vn < nt && kt_check >= 0;
+        if (has_next) tile_origin<BM, BN, CHUNKED>(p, tiles_m, tiles_n, on, vn);
+        else on = o;  // never loaded from (its stages are issued with an empty range)
+        tile_wait<CHUNKED>(p, o, vb);  // at once when prefetched: the chunk was seen landed
+        if (!prefetched) {
 #pragma unroll
-    for (int st = 0; st < SLOTS - 1; ++st) issue(st, st);
-    wait_vmcnt<2 * NBLK * (SLOTS - 2)>();  // stage 0 landed (stages 1 .. SLOTS - 2 may be in flight)
-    __syncthreads();
-    load_frags(smem, 0, fa[0], fb[0]);
-    load_frags(smem, 1, fa[1], fb[1]);
-    // Stage kt: fragment sets S0 = (kt, step 0) and S1 = (kt, step 1) are loaded.  Wait for
-    // this wave's loads of stage kt + 1 and make every wave's visible (the barrier also
-    // retires the slot of stage kt - 1, whose fragments were read during stage kt - 2); start
-    // stage kt + SLOTS - 1 into that slot; read (kt + 1, 0) into S2 during step 0 and
-    // (kt + 1, 1) into S0 during step 1.
-    auto stage = [&](int kt, int slot, int S0, int S1, int S2) {
-        const int nslot = slot + 1 == SLOTS ? 0 : slot + 1;
-        const int fslot = slot == 0 ? SLOTS - 1 : slot - 1;
-        wait_vmcnt<2 * NBLK * (SLOTS - 3)>();  // SLOTS - 3 later stages may stay in flight
+            for (int st = 0; st < SLOTS - 1; ++st) issue(o, true, st, slot_of(slot0 + st));
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        // stage 0 landed (stages 1 .. SLOTS - 2 may be in flight; so may the previous tile's
+        // stores, which only makes this wait longer)
+        wait_vmcnt<2 * NBLK * (SLOTS - 2)>();
         __syncthreads();
-        issue(kt + SLOTS - 1, fslot);
-        load_frags(smem + nslot * SLOT, 0, fa[S2], fb[S2]);
-        mfmas(fa[S0], fb[S0]);
-        pin(true);
-        load_frags(smem + nslot * SLOT, 1, fa[S0], fb[S0]);
-        mfmas(fa[S1], fb[S1]);
-        pin(false);
-    };
-    int kt = 0, slot = 0;
-    auto advance = [&]() {
-        ++kt;
-        slot = slot + 1 == SLOTS ? 0 : slot + 1;
-    };
-    while (kt + 3 <= nk) {
-        stage(kt, slot, 0, 1, 2);
-        advance();
-        stage(kt, slot, 2, 0, 1);
-        advance();
-        stage(kt, slot, 1, 2, 0);
-        advance();
-    }
-    if (kt < nk) {
-        stage(kt, slot, 0, 1, 2);
-        advance();
-    }
-    if (kt < nk) {
-        stage(kt, slot, 2, 0, 1);
-        advance();
+        load_frags(smem + slot_of(slot0) * SLOT, 0, fa[0], fb[0]);
+        load_frags(smem + slot_of(slot0) * SLOT, 1, fa[1], fb[1]);
+        bool next_ok = false;
+        // Stage kt: fragment sets S0 = (kt, step 0) and S1 = (kt, step 1) are loaded.  Wait for
+        // this wave's loads of stage kt + 1 and make every wave's visible (the barrier also
+        // retires the slot of stage kt - 1, whose fragments were read during stage kt - 2);
+        // start stage kt + SLOTS - 1 (of the next tile past the end) into that slot; read
+        // (kt + 1, 0) into S2 during step 0 and (kt + 1, 1) into S0 during step 1.
+        auto stage = [&](int kt, int S0, int S1, int S2) {
+            const int slot = slot_of(slot0 + kt);
+            const int nslot = slot_of(slot0 + kt + 1);
+            const int fslot = slot_of(slot0 + kt + SLOTS - 1);
+            wait_vmcnt<2 * NBLK * (SLOTS - 3)>();  // SLOTS - 3 later stages may stay in flight
+            __syncthreads();
+            if (has_next && kt == kt_check + 1) next_ok = __builtin_amdgcn_readfirstlane(next_ok_lds) != 0;
+            const int g = kt + SLOTS - 1;
+            if (g < nk) issue(o, true, g, fslot);
+            else issue(on, next_ok, g - nk, fslot);
+            load_frags(smem + nslot * SLOT, 0, fa[S2], fb[S2]);
+            mfmas(fa[S0], fb[S0]);
+            pin(true);
+            load_frags(smem + nslot * SLOT, 1, fa[S0], fb[S0]);
+            mfmas(fa[S1], fb[S1]);
+            pin(false);
+        };
+        int kt = 0;
+        while (kt + 3 <= nk) {
+            // The check falls in this group of three stages (kt_check = nk - SLOTS always lies
+            // below the last full group); the barrier of a later stage publishes the decision
+            // before stage kt_check + 1 reads it.
+            if (kt <= kt_check && kt_check < kt + 3 && wave == 0) {
+                const bool ok = has_next && (!CHUNKED || chunk_ready_now(p.plan, on.chunk, vn));
+                if (lane == 0) next_ok_lds = ok ? 1 : 0;
+            }
+            stage(kt, 0, 1, 2);
+            stage(kt + 1, 2, 0, 1);
+            stage(kt + 2, 1, 2, 0);
+            kt += 3;
+        }
+        if (kt < nk) stage(kt++, 0, 1, 2);
+        if (kt < nk) stage(kt++, 2, 0, 1);
+        tile_end<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc, vb);
+        prefetched = has_next && next_ok;
+        slot0 = slot_of(slot0 + nk);
     }
     // no load may still be writing this workgroup's LDS when it exits
     wait_vmcnt<0>();
-    tile_end<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc);
 #endif
 }
 
@@ -800,13 +867,36 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Workgroups of a persistent launch on the current device: its CU count, rounded down to a
+// multiple of 8 (one workgroup per CU, each keeping its XCD).
+int persistent_grid() {
+    // SPTL_GEMM_PERSIST=0 launches one workgroup per tile instead (measurement aid)
+    static const bool off = [] {
+        const char *e = getenv("SPTL_GEMM_PERSIST");
+        return e && !strcmp(e, "0");
+    }();
+    if (off) return 0x7fffffff;
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int g = cached[dev].load(std::memory_order_relaxed);
+    if (g == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+        g = cus & ~7;
+        cached[dev].store(g, std::memory_order_relaxed);
+    }
+    return g;
+}
+
 template <int WGM, int WGN, int SLOTS>
 hipError_t launch_ring(const GemmProblem &p, hipStream_t stream) {
     const int64_t tm = (p.m + 255) / 256, tn = (p.n + 255) / 256;
     const int64_t nt = tm * tn;
     if (nt == 0) return hipSuccess;
     if (nt > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)nt), block(64 * WGM * WGN);
+    const int64_t g = persistent_grid();
+    const dim3 grid((unsigned)(nt < g ? nt : g)), block(64 * WGM * WGN);
     const bool chunked = p.plan.chunk_rows != 0;
     if (p.c_f32 && chunked)
         hipLaunchKernelGGL((gemm_ring_kernel<WGM, WGN, SLOTS, true, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
