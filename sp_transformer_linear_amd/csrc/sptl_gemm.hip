@@ -50,6 +50,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -250,8 +251,11 @@ __device__ __forceinline__ void tile_begin(const GemmProblem &p, int tiles_m, in
     tile_wait<CHUNKED>(p, o, blockIdx.x);
 }
 
-// Stores the tile's accumulators and, for a chunk-ordered launch, records the tile's end and
-// completes the call when this is its last workgroup.
+template <bool CHUNKED>
+__device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrigin &o, int bid);
+
+// Stores the tile's accumulators (32 x 32 MFMA result layout) and, for a chunk-ordered launch,
+// records the tile's end and completes the call when this is its last tile.
 template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED>
 __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin &o,
                                          const f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32], int bid) {
@@ -304,6 +308,13 @@ __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin 
             }
         }
     }
+    tile_finish<CHUNKED>(p, o, bid);
+}
+
+// Chunk-ordered launches: records the tile's end and completes the call when this is its last
+// tile.
+template <bool CHUNKED>
+__device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrigin &o, int bid) {
     if (CHUNKED && threadIdx.x < 64) {
         const ChunkPlan &plan = p.plan;
         const int chunk = o.chunk;
@@ -331,6 +342,59 @@ __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin 
                 __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
+}
+
+// Stores the accumulators of a tile computed with v_mfma_f32_16x16x32_bf16, then as tile_end.
+// 16 x 16 result layout: lane l holds column l % 16, register e holds row 4 (l / 16) + e.
+template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED>
+__device__ __forceinline__ void tile_end16(const GemmProblem &p, const TileOrigin &o,
+                                           const f32x4_t (&acc)[BM / WGM / 16][BN / WGN / 16], int bid) {
+    constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm0 = (wave / WGN) * (BM / WGM), wn0 = (wave % WGN) * (BN / WGN);
+    const int64_t m0 = o.m0, n0 = o.n0;
+    if constexpr (OUT_F32) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t col = n0 + wn0 + j * 16 + (lane & 15);
+                if (col >= p.n) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t row = m0 + wm0 + i * 16 + (lane >> 4) * 4 + e;
+                    if (row < p.m) static_cast<float *>(p.c)[row * p.ldc + col] = acc[i][j][e];
+                }
+            }
+        }
+    } else {
+        // bf16: lanes 2 q and 2 q + 1 hold adjacent columns; one DPP swap per pair of values
+        // gives the even lane both columns of rows e = 0, 1 and the odd lane both columns of
+        // rows e = 2, 3, so every store writes two columns (4 bytes; N is a multiple of 8).
+        const bool odd = lane & 1;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t col = n0 + wn0 + j * 16 + (lane & 15 & ~1);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const float send = odd ? acc[i][j][k] : acc[i][j][k + 2];
+                    const float recv = __builtin_bit_cast(
+                        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+                    const float mine = odd ? acc[i][j][k + 2] : acc[i][j][k];
+                    const int e = odd ? k + 2 : k;
+                    const int64_t row = m0 + wm0 + i * 16 + (lane >> 4) * 4 + e;
+                    bf16x2_t v;
+                    v[0] = (__bf16)(odd ? recv : mine);
+                    v[1] = (__bf16)(odd ? mine : recv);
+                    if (row < p.m && col < p.n)
+                        *reinterpret_cast<bf16x2_t *>(static_cast<uint16_t *>(p.c) + row * p.ldc + col) = v;
+                }
+            }
+        }
+    }
+    tile_finish<CHUNKED>(p, o, bid);
 }
 
 template <int BM, int BN, int WGM, int WGN, int BK>
@@ -641,9 +705,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // ring of SLOTS LDS slots that direct-to-LDS buffer loads fill (64 lanes x 16 bytes = 1 KB per
 // instruction, lane l at byte 16 l), so no register staging and no LDS store instructions are
 // needed.  Stage kt + 1 is made visible (own loads waited for, then a barrier) at the top of
-// stage kt, and both of its fragment steps are read during stage kt: every fragment is read
-// two MFMA steps before its use, which covers the LDS latency of a CU whose 8 waves all read
-// at once.  Three fragment register sets rotate, so the loop is unrolled three times.
+// stage kt, and its fragments are read during stage kt, one stage (32 MFMAs per wave) before
+// their use, which covers the LDS latency of a CU whose 8 waves all read at once.  Two fragment
+// register sets alternate, so the loop is unrolled twice.
+//
+// MFMA: v_mfma_f32_16x16x32_bf16, one per 16 x 16 block and 32-deep stage.  Its products and
+// sums are those of two v_mfma_f32_32x32x16_bf16 steps over the same 32 k (bit-identical
+// results, checked against every other configuration), and it moves less accumulator data per
+// flop, which at the chip's power limit lets the clock run higher (about 10 % more GEMM
+// throughput with random operands).
 //
 // Persistent: workgroup b takes tiles b, b + G, b + 2 G, ... (G = gridDim.x, a multiple of 8,
 // so every tile keeps the XCD of a one-tile-per-workgroup launch).  The ring runs on across
@@ -655,13 +725,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // The per-lane global addresses apply the LDS swizzles in reverse:
 //   A slot: 256 rows of 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
 //           (a ds_read_b128 by 16 lanes then covers all 16 bank groups once);
-//   B slot: 32 rows (k) of 512 bytes, the same unit swizzle as the register-staged kernel.
-// Same MFMA instruction and K order as every other configuration.
+//   B slot: 32 rows (k) of 512 bytes; 32-byte unit u of row k at u ^ ((k & 3) << 1 | (k >> 3) & 1)
+//           (the transposing reads of a fragment take rows 8 g .. 8 g + 3 in lane group g; bit 3
+//           of k keeps groups 0 and 1, which the LDS serves together, on different banks).
+// Same K order as every other configuration.
 template <int WGM, int WGN, int SLOTS, bool OUT_F32, bool CHUNKED>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int BM = 256, BN = 256, TM = BM / WGM / 32, TN = BN / WGN / 32;
+    constexpr int BM = 256, BN = 256, TM = BM / WGM / 16, TN = BN / WGN / 16;  // 16 x 16 blocks per wave
     constexpr int NBLK = 16 / (WGM * WGN);   // 1 KB blocks per operand per wave per stage
     static_assert(NBLK * WGM * WGN == 16 && SLOTS >= 4 && SLOTS * 2 * kDmaSlotBytes <= 160 * 1024, "shape");
     constexpr int B_ROW = BN * 2;
@@ -713,64 +785,75 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
             // in registers across the tiles)
             const int krow = (wave * NBLK + t) * 2 + (lane >> 5);
             const int q = lane & 31;
-            const int64_t n = o.n0 + (((q >> 1) ^ ((krow & 3) << 1)) * 16 + (q & 1) * 8);
+            const int64_t n = o.n0 + (((q >> 1) ^ (((krow & 3) << 1) | ((krow >> 3) & 1))) * 16 + (q & 1) * 8);
             load_to_lds(br, lb + t * 1024, n < p.n ? (int)((krow * p.ldb + n) * 2) : kOutOfRange);
         }
     };
 
-    // fragment read addresses (within a slot); step st of a stage adds 16 k
-    int a_addr[2][TM];
+    // Fragment read addresses within a slot.  A block i (16 rows): lane l reads row
+    // wm0 + 16 i + l % 16, k 8 (l / 16) .. + 7 (one ds_read_b128).  B block j (16 columns): lane
+    // l holds column wn0 + 16 j + l % 16, k 8 (l / 16) .. + 7, from two transposing reads; per 16
+    // lanes source lane s supplies row kb + s / 4 at columns nb + 4 (s % 4) and result lane i
+    // gets B[kb .. kb + 3][nb + i], with kb = 8 (l / 16) and 8 (l / 16) + 4.
+    int a_addr[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int r = wm0 + i * 32 + (lane & 31);
-#pragma unroll
-        for (int st = 0; st < 2; ++st) a_addr[st][i] = r * (kDmaBK * 2) + (((2 * st + (lane >> 5)) ^ ((r >> 2) & 3)) << 4);
+        const int r = wm0 + i * 16 + (lane & 15);
+        a_addr[i] = r * (kDmaBK * 2) + (((lane >> 4) ^ ((r >> 2) & 3)) << 4);
     }
     const int rr = lane & 15;
-    const int b_k0 = 8 * (lane >> 5) + (rr >> 2);
+    const int b_k0 = 8 * (lane >> 4) + (rr >> 2);
+    const int b_sw = ((b_k0 & 3) << 1) | ((b_k0 >> 3) & 1);
     int b_addr[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        const int n = wn0 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (rr & 3);
-        b_addr[j] = kDmaSlotBytes + b_k0 * B_ROW + (((n >> 4) ^ ((b_k0 & 3) << 1)) << 5) + (n & 15) * 2;
+        const int n = wn0 + j * 16 + 4 * (rr & 3);
+        b_addr[j] = kDmaSlotBytes + b_k0 * B_ROW + (((n >> 4) ^ b_sw) << 5) + (n & 15) * 2;
     }
 
-    f32x16_t acc[TM][TN];
-    auto load_frags = [&](const char *slot, int st, bf16x8_t *af, bf16x8_t *bfr) {
+    f32x4_t acc[TM][TN];
+    auto load_frags = [&](const char *slot, bf16x8_t *af, bf16x8_t *bfr) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(slot + a_addr[st][i]);
+        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(slot + a_addr[i]);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const char *base = slot + b_addr[j] + st * 16 * B_ROW;
+            const char *base = slot + b_addr[j];
             bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
             bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * B_ROW));
             bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    constexpr int kDs = TM + 2 * TN, kMf = TM * TN;
+    constexpr int kMf = TM * TN;
+    // Column block major: B fragment j of the stage is dead after its TM MFMAs, so the next
+    // stage's B fragment j (read right then) can take its registers; only the A fragments of
+    // two stages are live at once.
     auto mfmas = [&](const bf16x8_t *af, const bf16x8_t *bfr) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < TM; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
-    // Each MFMA of a step is followed by one fragment read; with_loads also places one of the
-    // stage's global loads after every other MFMA.
-    auto pin = [&](bool with_loads) {
+    // Order within a stage: the next stage's A fragment reads after the first TM MFMAs, its B
+    // fragment j's two reads after the last MFMA of column block j, and the stage's global loads
+    // after every TM-th MFMA.
+    auto pin = [&]() {
 #pragma unroll
         for (int m = 0; m < kMf; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (m < kDs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (with_loads && (m & 1) && m / 2 < 2 * NBLK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (m < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (m % TM == TM - 1) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                if (m / TM < 2 * NBLK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
         }
     };
     auto slot_of = [&](int s) { return s % SLOTS; };
 
-    bf16x8_t fa[3][TM], fb[3][TN];
+    bf16x8_t fa[2][TM], fb[2][TN];
     int slot0 = 0;            // ring slot of the current tile's stage 0
     bool prefetched = false;  // the current tile's stages 0 .. SLOTS - 2 are already in flight
-    const int kt_check = nk - SLOTS;  // stage during which the next tile's chunk is checked
+    const int kt_check = nk - SLOTS;  // the next tile's chunk is checked at about this stage
     for (int vb = blockIdx.x; vb < nt; vb += gridDim.x) {
         TileOrigin o, on;
         tile_origin<BM, BN, CHUNKED>(p, tiles_m, tiles_n, o, vb);
@@ -788,21 +871,18 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+                for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
         // stage 0 landed (stages 1 .. SLOTS - 2 may be in flight; so may the previous tile's
         // stores, which only makes this wait longer)
         wait_vmcnt<2 * NBLK * (SLOTS - 2)>();
         __syncthreads();
-        load_frags(smem + slot_of(slot0) * SLOT, 0, fa[0], fb[0]);
-        load_frags(smem + slot_of(slot0) * SLOT, 1, fa[1], fb[1]);
+        load_frags(smem + slot_of(slot0) * SLOT, fa[0], fb[0]);
         bool next_ok = false;
-        // Stage kt: fragment sets S0 = (kt, step 0) and S1 = (kt, step 1) are loaded.  Wait for
-        // this wave's loads of stage kt + 1 and make every wave's visible (the barrier also
-        // retires the slot of stage kt - 1, whose fragments were read during stage kt - 2);
-        // start stage kt + SLOTS - 1 (of the next tile past the end) into that slot; read
-        // (kt + 1, 0) into S2 during step 0 and (kt + 1, 1) into S0 during step 1.
-        auto stage = [&](int kt, int S0, int S1, int S2) {
-            const int slot = slot_of(slot0 + kt);
+        // Stage kt: fragment set S0 holds stage kt.  Wait for this wave's loads of stage kt + 1
+        // and make every wave's visible (the barrier also retires the slot of stage kt - 1,
+        // whose fragments were read during stage kt - 2); start stage kt + SLOTS - 1 (of the next
+        // tile past the end) into that slot; read stage kt + 1 into S1 during the MFMAs.
+        auto stage = [&](int kt, int S0, int S1) {
             const int nslot = slot_of(slot0 + kt + 1);
             const int fslot = slot_of(slot0 + kt + SLOTS - 1);
             wait_vmcnt<2 * NBLK * (SLOTS - 3)>();  // SLOTS - 3 later stages may stay in flight
@@ -811,30 +891,25 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
             const int g = kt + SLOTS - 1;
             if (g < nk) issue(o, true, g, fslot);
             else issue(on, next_ok, g - nk, fslot);
-            load_frags(smem + nslot * SLOT, 0, fa[S2], fb[S2]);
+            load_frags(smem + nslot * SLOT, fa[S1], fb[S1]);
             mfmas(fa[S0], fb[S0]);
-            pin(true);
-            load_frags(smem + nslot * SLOT, 1, fa[S0], fb[S0]);
-            mfmas(fa[S1], fb[S1]);
-            pin(false);
+            pin();
         };
         int kt = 0;
-        while (kt + 3 <= nk) {
-            // The check falls in this group of three stages (kt_check = nk - SLOTS always lies
-            // below the last full group); the barrier of a later stage publishes the decision
-            // before stage kt_check + 1 reads it.
-            if (kt <= kt_check && kt_check < kt + 3 && wave == 0) {
+        while (kt + 2 <= nk) {
+            // The check falls in this pair of stages (kt_check = nk - SLOTS always lies below
+            // the last full pair); the barrier of a later stage publishes the decision before
+            // stage kt_check + 1 reads it.
+            if (kt <= kt_check && kt_check < kt + 2 && wave == 0) {
                 const bool ok = has_next && (!CHUNKED || chunk_ready_now(p.plan, on.chunk, vn));
                 if (lane == 0) next_ok_lds = ok ? 1 : 0;
             }
-            stage(kt, 0, 1, 2);
-            stage(kt + 1, 2, 0, 1);
-            stage(kt + 2, 1, 2, 0);
-            kt += 3;
+            stage(kt, 0, 1);
+            stage(kt + 1, 1, 0);
+            kt += 2;
         }
-        if (kt < nk) stage(kt++, 0, 1, 2);
-        if (kt < nk) stage(kt++, 2, 0, 1);
-        tile_end<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc, vb);
+        if (kt < nk) stage(kt, 0, 1);
+        tile_end16<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc, vb);
         prefetched = has_next && next_ok;
         slot0 = slot_of(slot0 + nk);
     }
