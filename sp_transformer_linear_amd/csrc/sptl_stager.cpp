@@ -37,7 +37,6 @@ namespace sptl {
 
 namespace {
 constexpr int kSets = kStageSets;
-constexpr size_t kMinPiece = 512 * 1024;  // below this, striping costs more than it gains
 
 struct FindAgent {
     uint32_t bdf;
@@ -382,54 +381,22 @@ int stager_wait_idle(SdmaStager *s) {
 }
 
 std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies, int lead) {
-    std::vector<CopyPiece> out;
     // tuning knob: SPTL_SDMA_SPLIT=p stripes a chunk into up to p pieces per engine
     static const size_t split = [] {
         const char *e = getenv("SPTL_SDMA_SPLIT");
         const long v = e ? strtol(e, nullptr, 10) : 1;
         return (size_t)(v >= 1 && v <= 16 ? v : 1);
     }();
-    const int engines = (int)s->engines.size();
-    size_t E = (size_t)engines * split;
-    if (E > (size_t)kMaxPieces) E = kMaxPieces;
-    // Equal pieces of copy c, rounded to 256 bytes (the last takes the remainder, so at most
-    // n pieces), on engines first, first + 1, ...
-    auto cut = [&](const CopyPiece &c, size_t n, int first) {
-        const size_t step = ((c.bytes / n) + 255) & ~(size_t)255;
-        size_t off = 0;
-        int piece = 0;
-        while (off < c.bytes) {
-            const size_t b = c.bytes - off < step ? c.bytes - off : step;
-            CopyPiece pc{static_cast<char *>(c.dst) + off, static_cast<const char *>(c.src) + off, b, c.chunk, piece};
-            pc.engine = (first + piece) % engines;
-            out.push_back(pc);
-            off += b;
-            ++piece;
-        }
-    };
-    // the leading copies share the engines: about engines * bytes_c / total pieces each
-    if (lead > (int)copies.size()) lead = (int)copies.size();
-    if (lead > engines) lead = engines;
-    if (lead < 1) lead = 1;
-    size_t lead_bytes = 0;
-    for (int i = 0; i < lead; ++i) lead_bytes += copies[i].bytes;
-    int first = 0;
-    for (int i = 0; i < lead && lead > 1; ++i) {
-        const int rest = lead - 1 - i;  // copies after this one, each needs an engine
-        size_t n = lead_bytes ? (size_t)(((double)copies[i].bytes / (double)lead_bytes) * engines + 0.5) : 1;
-        if (n < 1) n = 1;
-        if ((int)n > engines - first - rest) n = (size_t)(engines - first - rest);
-        if (i == lead - 1) n = (size_t)(engines - first);
-        if (n > (size_t)kMaxPieces) n = kMaxPieces;
-        const size_t by_size = copies[i].bytes / (kMinPiece / split);
-        if (n > by_size) n = by_size < 1 ? 1 : by_size;
-        cut(copies[i], n, first);
-        first += (int)n;
-    }
-    for (size_t i = lead > 1 ? (size_t)lead : 0; i < copies.size(); ++i) {
-        size_t n = copies[i].bytes / (kMinPiece / split);
-        n = n < 1 ? 1 : n > E ? E : n;
-        cut(copies[i], n, 0);
+    std::vector<PlanCopy> pc;
+    pc.reserve(copies.size());
+    for (const CopyPiece &c : copies) pc.push_back({c.bytes, c.chunk});
+    std::vector<CopyPiece> out;
+    for (const PlanPiece &q : plan_pieces(pc, lead, (int)s->engines.size(), split)) {
+        const CopyPiece &c = copies[(size_t)q.copy];
+        CopyPiece piece{static_cast<char *>(c.dst) + q.offset, static_cast<const char *>(c.src) + q.offset, q.bytes,
+                        q.chunk, q.piece};
+        piece.engine = q.engine;
+        out.push_back(piece);
     }
     return out;
 }

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "sptl_internal.h"
+#include "sptl_plan.h"
 
 namespace sptl {
 
@@ -24,7 +25,6 @@ struct CopyPiece {
 };
 constexpr int kJoinChunk = kMaxPlanChunks;
 constexpr int kStageSets = 4;   // calls that can be in flight on one stager
-constexpr int kMaxPieces = 16;  // copy pieces per chunk, each with a completion signal of its own
 static_assert(kMaxPieces <= 64, "the GEMM watches a chunk's pieces with one lane each");
 
 // One call's view of its completion-signal set.  ready[c] is a device array of the value
@@ -62,12 +62,9 @@ SdmaStager *stager_create(int device, std::string *err);
 void stager_destroy(SdmaStager *s);
 int stager_engine_count(const SdmaStager *s);
 
-// Splits every chunk copy into at most kMaxPieces pieces and assigns each piece an engine; returns
+// Splits the chunk copies into pieces with an engine each (plan_pieces, sptl_plan.h) and returns
 // them in submission order with their chunk and piece ids, which is what stager_begin and
-// stager_submit expect.  The first `lead` copies are split together, about one piece per
-// engine in proportion to their sizes, so that they land at about the same time, as early as
-// the engines allow; every later copy is striped over all engines (piece p on engine p), and
-// each engine takes its pieces in submission order.
+// stager_submit expect; each engine takes its pieces in submission order.
 std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies, int lead = 1);
 
 // Reserves a completion-signal set for one call whose consuming kernel has `workgroups`
