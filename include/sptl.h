@@ -138,16 +138,19 @@ const char *sptl_ctx_info(sptl_ctx *ctx);
  * Staged path (copy == NULL, the default; used when the device's SDMA engines can be driven
  * through HSA, seq_len / n_chunks is a multiple of 128 and n_chunks <= 64; else the
  * per-chunk path runs on the context's own copy stream):
- *   - Every peer chunk is split into pieces striped over all SDMA copy engines.  The pieces
- *     are submitted by the context's worker thread as soon as an event recorded on
- *     `compute` at the call's position has completed, so the copies never overwrite
- *     x_gathered while earlier work on `compute` still reads it.  Copy order: chunks of
- *     ranks rank+1, ..., rank+tp-1 (mod tp), then this rank's own slot unless
- *     shard_src[rank] aliases it.
+ *   - Every peer chunk is split into pieces for the SDMA copy engines.  The peer chunks that
+ *     the GEMM's first round of tiles needs (one tile per compute unit, the round sized for
+ *     an output at least `hidden` wide) are split together, one piece per engine, so that
+ *     they land together; every later chunk is striped over all engines.  The pieces are
+ *     submitted by the context's worker thread as soon as an event recorded on `compute` at
+ *     the call's position has completed, so the copies never overwrite x_gathered while
+ *     earlier work on `compute` still reads it.  Copy order: chunks of ranks rank+1, ...,
+ *     rank+tp-1 (mod tp), then this rank's own slot unless shard_src[rank] aliases it.
  *   - ONE GEMM launch on `compute` processes row tiles in chunk order: this rank's chunks
  *     first (read straight from shard_src[rank]), then the peers' chunks in copy order;
- *     each tile waits on the GPU for its own chunk's pieces to land.  The launch ends only
- *     after every copy of the call (own slot included) has landed.
+ *     each tile waits on the GPU for its own chunk's pieces to land (a launch with more tiles
+ *     than compute units runs one workgroup per unit, each taking its tiles in that order).
+ *     The launch ends only after every copy of the call (own slot included) has landed.
  *   - Up to 4 staged calls per context may be in flight; a fifth blocks the calling thread
  *     until the oldest has finished on the GPU.
  * Per-chunk path (copy != NULL): for each peer chunk, one SDMA-class hipMemcpyAsync on
