@@ -12,7 +12,8 @@ in HBM:
   3. reduce_residual_rmsnorm   own partial + the peers' partials + residual, RMSNorm;
   4. dtp_accumulate      delayed-TP update (own partial now, peers' partials of an earlier
                          module), RMSNorm.
-Per-call times come from HIP events on the compute stream that every call is issued on.
+Per-call times come from HIP events on the compute stream that every call is issued on, created
+with hipEventDisableSystemFence (timing only: recording them writes back no cache).
 Per-chunk landing and tile times come from the library's device timestamps (one
 instrumented call outside the timed region).
 
@@ -119,6 +120,44 @@ def max_sclk_mhz(device: int):
     except OSError:
         pass
     return None
+
+
+class TimingEvent:
+    """A HIP event used only for timing: created with hipEventDisableSystemFence, so recording it
+    does not write back and invalidate the caches (a system-scope release, which would add its
+    own time to the interval and slow the work that follows it).  Same interface as the parts of
+    torch.cuda.Event used here."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")  # by soname: the runtime torch already loaded
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        if TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if TimingEvent._hip.hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        ms = self._ct.c_float()
+        if TimingEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and self.h:
+            TimingEvent._hip.hipEventDestroy(self.h)
 
 
 def cpu_model() -> str:
@@ -230,7 +269,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = TimingEvent
 
     def agmm(wt, yt, timing=False):
         sptl.agmm_chunked(shards, xg, wt, yt, n_chunks=wl.n_chunks, rank=0, compute=cs, timing=timing, ctx=ctx)
