@@ -256,6 +256,13 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
         return (int)(v >= 0 && v <= 64 ? v : 0);
     }();
     plan.poll_sleep = poll_sleep;
+    // SPTL_CHUNK_XCDS=g (1, 2, 4 or 8) spreads every chunk's tiles over g XCDs (measurement aid)
+    static const int xcd_group = [] {
+        const char *e = getenv("SPTL_CHUNK_XCDS");
+        const long v = e ? strtol(e, nullptr, 10) : 0;
+        return (int)(v == 1 || v == 2 || v == 4 || v == 8 ? v : 0);
+    }();
+    plan.xcd_group = xcd_group;
     plan.ts = timing ? ctx->ts_dev : nullptr;
 
     // The GEMM's first round of tiles (one per CU) spans the own chunks and the first `lead`

@@ -188,26 +188,21 @@ __device__ __forceinline__ void tile_origin(const GemmProblem &p, int tiles_m, i
     } else {
         // Chunk-ordered: each XCD (workgroups x mod 8) runs its workgroups in index order, so
         // on every XCD the tiles of chunks that land first come first.  A chunk is a whole
-        // number of tile rows.  When the chunks divide evenly, a chunk's tiles go to a group
-        // of g XCDs (the fewest that keeps each XCD's share at 32 tiles or less, one per CU),
-        // 8 / g chunks run side by side, and each XCD's share of a chunk is a contiguous run
-        // of the chunk's banded order (4 tile rows, column-major), so the workgroups an XCD
-        // runs at once share a few A and B panels in its L2.
+        // number of tile rows.  With g = plan.xcd_group > 0 a chunk's tiles go to a group of g
+        // XCDs, 8 / g chunks run side by side, and each XCD's share of a chunk is a contiguous
+        // run of the chunk's banded order (plan.chunk_band tile rows, column-major), so the
+        // workgroups an XCD runs at once share a few A and B panels in its L2 (chunk_layout).
         const int tpc = plan.chunk_rows / BM;
         const int per_chunk = tpc * tiles_n;
-        int g = 0;
-        for (int c = 1; c <= 8 && !g; c *= 2)
-            if (per_chunk % c == 0 && plan.n_chunks % (8 / c) == 0 && per_chunk / c <= 32) g = c;
-        for (int c = 8; c >= 1 && !g; c /= 2)
-            if (per_chunk % c == 0 && plan.n_chunks % (8 / c) == 0) g = c;
+        const int g = plan.xcd_group, kb = plan.chunk_band;
         int pos, sub, tn;
         if (g) {
             const int x = bid & 7, slot = bid >> 3, share = per_chunk / g;
             pos = (slot / share) * (8 / g) + x / g;
             const int t = (x % g) * share + slot % share;
-            const int band = t / (kBand * tiles_n), in_band = t - band * (kBand * tiles_n);
-            const int band_rows = tpc - band * kBand < kBand ? tpc - band * kBand : kBand;
-            sub = band * kBand + in_band % band_rows;
+            const int band = t / (kb * tiles_n), in_band = t - band * (kb * tiles_n);
+            const int band_rows = tpc - band * kb < kb ? tpc - band * kb : kb;
+            sub = band * kb + in_band % band_rows;
             tn = in_band / band_rows;
         } else {
             pos = bid / per_chunk;
@@ -1007,6 +1002,36 @@ const char *config_name(int c) {
 }
 
 int config_rows(int c) { return c == k128x128w2x2 || c == k128x256w2x2k32 ? 128 : 256; }
+int config_cols(int c) { return c == k256x128w4x2 || c == k256x128w4x1 || c == k128x128w2x2 ? 128 : 256; }
+
+// Chunk-ordered tile layout (see tile_origin).  XCDs per chunk g: the forced value if it divides
+// evenly, else the most XCDs that divide a chunk's tiles (with 8 / g dividing the chunk count),
+// so that a chunk that has landed while others have not spreads over the whole chip; 0 when
+// none divides (plain chunk order).  Band height: each XCD runs `conc` workgroups at once (one
+// per CU), which cover min(conc, share) tiles of each of ceil(conc / share) chunks, every chunk's
+// share a band rows x ceil(share / band) columns block at the same columns; the band minimises
+// the A plus B panels those workgroups read (ties: the band nearest kBand).
+void chunk_layout(ChunkPlan &plan, int bm, int64_t tiles_n) {
+    const int64_t tpc = plan.chunk_rows / bm, per_chunk = tpc * tiles_n;
+    auto fits = [&](int c) { return per_chunk % c == 0 && plan.n_chunks % (8 / c) == 0; };
+    int g = plan.xcd_group > 0 && fits(plan.xcd_group) ? plan.xcd_group : 0;
+    for (int c = 8; c >= 1 && !g; c /= 2)
+        if (fits(c)) g = c;
+    plan.xcd_group = g;
+    plan.chunk_band = kBand;
+    if (!g) return;
+    const int64_t conc = persistent_grid() / 8, share = per_chunk / g;
+    const int64_t width = share < conc ? share : conc, chunks = (conc + share - 1) / share;
+    int64_t best = -1;
+    for (int b = 1; b <= 8 && b <= tpc; b *= 2) {
+        const int64_t panels = chunks * b + (width + b - 1) / b;
+        const int dist = b > kBand ? b - kBand : kBand - b, best_dist = plan.chunk_band > kBand ? plan.chunk_band - kBand : kBand - plan.chunk_band;
+        if (best < 0 || panels < best || (panels == best && dist < best_dist)) {
+            best = panels;
+            plan.chunk_band = b;
+        }
+    }
+}
 
 // SPTL_GEMM_CFG=<name> forces one configuration for every GEMM (measurement aid).
 int forced_config() {
@@ -1051,12 +1076,15 @@ hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t strea
 
 int64_t gemm_workgroups(const GemmProblem &p, GemmTile tile) {
     const int c = resolve(p, tile);
-    const int64_t bm = config_rows(c), bn = (c == k256x128w4x2 || c == k256x128w4x1 || c == k128x128w2x2) ? 128 : 256;
+    const int64_t bm = config_rows(c), bn = config_cols(c);
     return ((p.m + bm - 1) / bm) * ((p.n + bn - 1) / bn);
 }
 
-hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile) {
-    switch (resolve(p, tile)) {
+hipError_t launch_gemm(const GemmProblem &problem, hipStream_t stream, GemmTile tile) {
+    const int c = resolve(problem, tile);
+    GemmProblem p = problem;
+    if (p.plan.chunk_rows) chunk_layout(p.plan, config_rows(c), (p.n + config_cols(c) - 1) / config_cols(c));
+    switch (c) {
         case k256x256w2x2: return launch_cfg<256, 256, 2, 2>(p, stream);
         case k256x256w2x4: return launch_cfg<256, 256, 2, 4>(p, stream);
         case k256x256w4x2: return launch_cfg<256, 256, 4, 2>(p, stream);

@@ -37,6 +37,10 @@ struct ChunkPlan {
     int *err;                                // set to 1 when a wait times out
     uint64_t timeout_ticks;                  // wall-clock ticks of the bounded waits
     int poll_sleep;                          // extra s_sleep 127 per poll (0: ~1 us between polls)
+    int xcd_group;                           // XCDs per chunk: a forced value or 0 (choose) on entry
+                                             // to launch_gemm; the kernel sees the chosen one (0: plain
+                                             // chunk order)
+    int chunk_band;                          // tile rows per band inside a chunk (set by launch_gemm)
     uint64_t *flags;                         // landed flags (kFlagSetWords words), or nullptr
     uint64_t epoch;                          // value a landed flag holds for this launch
     uint64_t *finished;                      // pinned host word: epoch once the launch is done
