@@ -20,6 +20,10 @@
 //     (streamed out rather than kept in the caches: ~11 % more bandwidth on cold inputs).
 #include "sptl_internal.h"
 
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+
 namespace sptl {
 namespace {
 
@@ -175,12 +179,61 @@ __global__ void __launch_bounds__(kMaxThreads) epilogue_wide_kernel(EpilogueProb
 // two-pass kernel.
 constexpr int kMaxLiveVectors = 36;
 
+// Loads in flight per CU.  Every workgroup keeps all of its row's loads in flight, so the
+// workgroups resident on a CU set how many rows HBM serves at once.  As many as the registers
+// allow (5 per CU at 9 inputs and 4096 columns: 368 KiB of loads) streamed about 3 % slower
+// than 2 or 3 per CU, which keep fewer rows, and so fewer DRAM pages, open at once.  The
+// launch caps the workgroups per CU through their LDS allocation (unused) so that about
+// kInflightBytes of loads are in flight per CU; the result bits do not depend on it.
+constexpr int64_t kInflightBytes = 192 * 1024;
+
+struct LdsLimits {
+    int per_cu = 0, per_block = 0;
+};
+
+LdsLimits lds_limits() {
+    constexpr int kDevices = 64;
+    static std::atomic<int> per_cu[kDevices], per_block[kDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return {};
+    LdsLimits l{per_cu[dev].load(std::memory_order_relaxed), per_block[dev].load(std::memory_order_relaxed)};
+    if (l.per_cu == 0) {
+        int a = 0, b = 0;
+        if (hipDeviceGetAttribute(&a, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return {};
+        per_cu[dev].store(a, std::memory_order_relaxed);
+        per_block[dev].store(b, std::memory_order_relaxed);
+        l = {a, b};
+    }
+    return l;
+}
+
+// Dynamic LDS bytes that cap a launch at the workgroups per CU that keep about kInflightBytes
+// of loads in flight (0: no cap).  SPTL_EPI_INFLIGHT_KIB overrides the target (0: never cap; a
+// measurement aid).
+size_t inflight_cap_lds(int64_t bytes_per_wg) {
+    static const int64_t target = [] {
+        const char *e = getenv("SPTL_EPI_INFLIGHT_KIB");
+        const long v = e ? strtol(e, nullptr, 10) : -1;
+        return v >= 0 && v <= 65536 ? (int64_t)v * 1024 : kInflightBytes;
+    }();
+    if (target == 0 || bytes_per_wg <= 0) return 0;
+    const LdsLimits l = lds_limits();
+    const int64_t wgs = std::max<int64_t>(1, (target + bytes_per_wg / 2) / bytes_per_wg);
+    // a 1 KiB margin for the kernel's own LDS, in 1 KiB steps
+    const int64_t dyn = (l.per_cu / wgs - 1024) / 1024 * 1024;
+    if (dyn <= 0 || dyn > l.per_block - 1024) return 0;
+    return (size_t)dyn;
+}
+
 template <int N, int VPT>
 bool launch_nin(const EpilogueProblem &p, int threads, hipStream_t s) {
     if constexpr (N * VPT <= kMaxLiveVectors) {
         if (p.n_in == N) {
+            const size_t lds = inflight_cap_lds((int64_t)threads * VPT * N * 16);
             hipLaunchKernelGGL((epilogue_kernel<N, VPT>), dim3((unsigned)p.rows),
-                               dim3((unsigned)threads), 0, s, p);
+                               dim3((unsigned)threads), lds, s, p);
             return true;
         }
     }
