@@ -180,50 +180,57 @@ __global__ void __launch_bounds__(kMaxThreads) epilogue_wide_kernel(EpilogueProb
 constexpr int kMaxLiveVectors = 36;
 
 // Loads in flight per CU.  Every workgroup keeps all of its row's loads in flight, so the
-// workgroups resident on a CU set how many rows HBM serves at once.  As many as the registers
-// allow (5 per CU at 9 inputs and 4096 columns: 368 KiB of loads) streamed about 3 % slower
-// than 2 or 3 per CU, which keep fewer rows, and so fewer DRAM pages, open at once.  The
-// launch caps the workgroups per CU through their LDS allocation (unused) so that about
-// kInflightBytes of loads are in flight per CU; the result bits do not depend on it.
+// workgroups resident on a CU set how many rows HBM serves at once.  At 8192 rows of 9 inputs
+// and 4096 columns, as many as the registers allow (5 per CU: 368 KiB of loads) streamed
+// about 4 % slower than 3 per CU.  The launch caps the workgroups per CU through their LDS
+// allocation (unused) so that about kInflightBytes of loads are in flight per CU, for launches
+// of at most kCapRowsPerCu rows per CU: at 64 rows per CU the cap was neutral and at 256 it
+// cost about 2 %.  The result bits do not depend on it.
 constexpr int64_t kInflightBytes = 192 * 1024;
+constexpr int64_t kCapRowsPerCu = 48;
 
-struct LdsLimits {
-    int per_cu = 0, per_block = 0;
+struct DeviceLimits {
+    int lds_per_cu = 0, lds_per_block = 0, cus = 0;
 };
 
-LdsLimits lds_limits() {
+DeviceLimits device_limits() {
     constexpr int kDevices = 64;
-    static std::atomic<int> per_cu[kDevices], per_block[kDevices];
+    static std::atomic<int> per_cu[kDevices], per_block[kDevices], cus[kDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return {};
-    LdsLimits l{per_cu[dev].load(std::memory_order_relaxed), per_block[dev].load(std::memory_order_relaxed)};
-    if (l.per_cu == 0) {
-        int a = 0, b = 0;
+    DeviceLimits l{per_cu[dev].load(std::memory_order_relaxed), per_block[dev].load(std::memory_order_relaxed),
+                   cus[dev].load(std::memory_order_relaxed)};
+    if (l.cus == 0) {
+        int a = 0, b = 0, c = 0;
         if (hipDeviceGetAttribute(&a, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
-            hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
             return {};
         per_cu[dev].store(a, std::memory_order_relaxed);
         per_block[dev].store(b, std::memory_order_relaxed);
-        l = {a, b};
+        cus[dev].store(c, std::memory_order_relaxed);
+        l = {a, b, c};
     }
     return l;
 }
 
-// Dynamic LDS bytes that cap a launch at the workgroups per CU that keep about kInflightBytes
-// of loads in flight (0: no cap).  SPTL_EPI_INFLIGHT_KIB overrides the target (0: never cap; a
-// measurement aid).
-size_t inflight_cap_lds(int64_t bytes_per_wg) {
-    static const int64_t target = [] {
+// Dynamic LDS bytes that cap a launch of `rows` workgroups at the workgroups per CU that keep
+// about kInflightBytes of loads in flight (0: no cap).  SPTL_EPI_INFLIGHT_KIB overrides the
+// target and applies it at any row count (0: never cap; a measurement aid).
+size_t inflight_cap_lds(int64_t bytes_per_wg, int64_t rows) {
+    static const int64_t forced = [] {
         const char *e = getenv("SPTL_EPI_INFLIGHT_KIB");
         const long v = e ? strtol(e, nullptr, 10) : -1;
-        return v >= 0 && v <= 65536 ? (int64_t)v * 1024 : kInflightBytes;
+        return v >= 0 && v <= 65536 ? (int64_t)v * 1024 : (int64_t)-1;
     }();
-    if (target == 0 || bytes_per_wg <= 0) return 0;
-    const LdsLimits l = lds_limits();
+    const DeviceLimits l = device_limits();
+    if (forced == 0 || bytes_per_wg <= 0 || l.cus == 0) return 0;
+    if (forced < 0 && rows > kCapRowsPerCu * l.cus) return 0;
+    const int64_t target = forced > 0 ? forced : kInflightBytes;
     const int64_t wgs = std::max<int64_t>(1, (target + bytes_per_wg / 2) / bytes_per_wg);
     // a 1 KiB margin for the kernel's own LDS, in 1 KiB steps
-    const int64_t dyn = (l.per_cu / wgs - 1024) / 1024 * 1024;
-    if (dyn <= 0 || dyn > l.per_block - 1024) return 0;
+    const int64_t dyn = (l.lds_per_cu / wgs - 1024) / 1024 * 1024;
+    if (dyn <= 0 || dyn > l.lds_per_block - 1024) return 0;
     return (size_t)dyn;
 }
 
@@ -231,7 +238,7 @@ template <int N, int VPT>
 bool launch_nin(const EpilogueProblem &p, int threads, hipStream_t s) {
     if constexpr (N * VPT <= kMaxLiveVectors) {
         if (p.n_in == N) {
-            const size_t lds = inflight_cap_lds((int64_t)threads * VPT * N * 16);
+            const size_t lds = inflight_cap_lds((int64_t)threads * VPT * N * 16, p.rows);
             hipLaunchKernelGGL((epilogue_kernel<N, VPT>), dim3((unsigned)p.rows),
                                dim3((unsigned)threads), lds, s, p);
             return true;

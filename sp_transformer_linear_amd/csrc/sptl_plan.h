@@ -10,8 +10,11 @@
 //   * the first `lead` copies (the peer chunks that the GEMM's first round of tiles needs) are
 //     split together, about one piece per engine in proportion to their sizes, so that they
 //     land at about the same time, as early as the engines allow;
-//   * every later copy is striped over all engines (piece p on engine p), at most kMaxPieces
-//     pieces and no piece below kMinPiece / split bytes;
+//   * the later copies are split together in groups, like the leading group, with enough
+//     copies per group that every engine's piece is at least kGroupPiece bytes (a copy engine
+//     streams a small piece at about half its rate); copies large enough for that on their own
+//     are striped over all engines one after another (piece p on engine p), at most
+//     kMaxPieces pieces and no piece below kMinPiece / split bytes;
 //   * pieces are equal and rounded up to 256 bytes; the last piece of a copy takes the rest.
 // Each engine takes its pieces in the order returned.
 #pragma once
@@ -39,8 +42,23 @@ struct PlanPiece {
     int engine;     // in [0, engines)
 };
 
-// `split` (>= 1) allows up to split pieces per engine and copy; `engines` >= 1.
-inline std::vector<PlanPiece> plan_pieces(const std::vector<PlanCopy> &copies, int lead, int engines, size_t split) {
+// Group size for the later copies of `chunk_bytes` each: the fewest copies that give every
+// engine a piece of at least kGroupPiece bytes (1 when a striped copy already does).
+constexpr size_t kGroupPiece = 2 * 1024 * 1024;
+
+inline int later_group(int engines, size_t chunk_bytes) {
+    if (engines < 1 || chunk_bytes == 0) return 1;
+    const size_t want = (size_t)engines * kGroupPiece;
+    const size_t g = (want + chunk_bytes - 1) / chunk_bytes;
+    return g < 1 ? 1 : g > (size_t)engines ? engines : (int)g;
+}
+
+// `split` (>= 1) allows up to split pieces per engine and copy; `engines` >= 1.  `group` (>= 1)
+// splits the later copies together in successive groups of `group` copies, like the leading
+// group (1: each later copy striped over all engines on its own); a last group shorter than
+// `group` is merged into the one before when both fit on the engines.
+inline std::vector<PlanPiece> plan_pieces(const std::vector<PlanCopy> &copies, int lead, int engines, size_t split,
+                                          int group = 1) {
     std::vector<PlanPiece> out;
     size_t E = (size_t)engines * split;
     if (E > (size_t)kMaxPieces) E = kMaxPieces;
@@ -58,28 +76,46 @@ inline std::vector<PlanPiece> plan_pieces(const std::vector<PlanCopy> &copies, i
             ++piece;
         }
     };
-    if (lead > (int)copies.size()) lead = (int)copies.size();
+    // copies [b, e) (e - b <= engines) split together: each takes a run of distinct engines, about
+    // in proportion to its size, and the runs cover every engine
+    auto joint = [&](int b, int e) {
+        size_t bytes = 0;
+        for (int i = b; i < e; ++i) bytes += copies[(size_t)i].bytes;
+        int first = 0;
+        for (int i = b; i < e; ++i) {
+            const int rest = e - 1 - i;  // copies after this one, each needs an engine
+            size_t n = bytes ? (size_t)(((double)copies[(size_t)i].bytes / (double)bytes) * engines + 0.5) : 1;
+            if (n < 1) n = 1;
+            if ((int)n > engines - first - rest) n = (size_t)(engines - first - rest);
+            if (i == e - 1) n = (size_t)(engines - first);
+            if (n > (size_t)kMaxPieces) n = kMaxPieces;
+            const size_t by_size = copies[(size_t)i].bytes / (kMinPiece / split);
+            if (n > by_size) n = by_size < 1 ? 1 : by_size;
+            cut(i, n, first);
+            first += (int)n;
+        }
+    };
+    const int count = (int)copies.size();
+    if (lead > count) lead = count;
     if (lead > engines) lead = engines;
     if (lead < 1) lead = 1;
-    size_t lead_bytes = 0;
-    for (int i = 0; i < lead; ++i) lead_bytes += copies[(size_t)i].bytes;
-    int first = 0;
-    for (int i = 0; i < lead && lead > 1; ++i) {
-        const int rest = lead - 1 - i;  // copies after this one, each needs an engine
-        size_t n = lead_bytes ? (size_t)(((double)copies[(size_t)i].bytes / (double)lead_bytes) * engines + 0.5) : 1;
-        if (n < 1) n = 1;
-        if ((int)n > engines - first - rest) n = (size_t)(engines - first - rest);
-        if (i == lead - 1) n = (size_t)(engines - first);
-        if (n > (size_t)kMaxPieces) n = kMaxPieces;
-        const size_t by_size = copies[(size_t)i].bytes / (kMinPiece / split);
-        if (n > by_size) n = by_size < 1 ? 1 : by_size;
-        cut(i, n, first);
-        first += (int)n;
-    }
-    for (size_t i = lead > 1 ? (size_t)lead : 0; i < copies.size(); ++i) {
-        size_t n = copies[i].bytes / (kMinPiece / split);
-        n = n < 1 ? 1 : n > E ? E : n;
-        cut((int)i, n, 0);
+    if (group > engines) group = engines;
+    if (group < 1) group = 1;
+    if (lead > 1) joint(0, lead);
+    for (int i = lead > 1 ? lead : 0; i < count;) {
+        if (group > 1) {
+            int e = i + group < count ? i + group : count;
+            // a short last group joins this one when they fit on the engines together, so no
+            // copy is left to run alone at the end
+            if (e < count && count - e < group && count - i <= engines) e = count;
+            joint(i, e);
+            i = e;
+        } else {
+            size_t n = copies[(size_t)i].bytes / (kMinPiece / split);
+            n = n < 1 ? 1 : n > E ? E : n;
+            cut(i, n, 0);
+            ++i;
+        }
     }
     return out;
 }

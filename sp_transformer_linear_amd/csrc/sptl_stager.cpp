@@ -387,11 +387,19 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
         const long v = e ? strtol(e, nullptr, 10) : 1;
         return (size_t)(v >= 1 && v <= 16 ? v : 1);
     }();
+    // tuning knob: SPTL_SDMA_GROUP=g splits the later copies together in groups of g (0: by size)
+    static const int forced_group = [] {
+        const char *e = getenv("SPTL_SDMA_GROUP");
+        const long v = e ? strtol(e, nullptr, 10) : 0;
+        return (int)(v >= 1 && v <= 64 ? v : 0);
+    }();
     std::vector<PlanCopy> pc;
     pc.reserve(copies.size());
     for (const CopyPiece &c : copies) pc.push_back({c.bytes, c.chunk});
+    const int engines = (int)s->engines.size();
+    const int group = forced_group ? forced_group : later_group(engines, copies.empty() ? 0 : copies[0].bytes);
     std::vector<CopyPiece> out;
-    for (const PlanPiece &q : plan_pieces(pc, lead, (int)s->engines.size(), split)) {
+    for (const PlanPiece &q : plan_pieces(pc, lead, engines, split, group)) {
         const CopyPiece &c = copies[(size_t)q.copy];
         CopyPiece piece{static_cast<char *>(c.dst) + q.offset, static_cast<const char *>(c.src) + q.offset, q.bytes,
                         q.chunk, q.piece};

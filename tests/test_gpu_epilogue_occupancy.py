@@ -1,11 +1,11 @@
 """The epilogue's workgroups-per-CU cap does not change any bit.
 
-The register-resident epilogue keeps all of a row's loads in flight, and its launch caps the
-workgroups resident per CU (through an unused LDS allocation) so that about a fixed number of
-bytes of loads is in flight per CU.  Rows are independent and every row is reduced in the same
-order whatever the launch, so the outputs must be identical with the default cap, with no cap
-(SPTL_EPI_INFLIGHT_KIB=0) and with a tight one (64 KiB: one workgroup per CU at 9 inputs of
-4096 columns).  The variable is read once per process, so each setting runs in a child
+The register-resident epilogue keeps all of a row's loads in flight, and for launches of up to
+48 rows per CU its launch caps the workgroups resident per CU (through an unused LDS
+allocation) so that about a fixed number of bytes of loads is in flight per CU.  Rows are
+independent and every row is reduced in the same order whatever the launch, so the outputs
+must be identical with the default cap, with no cap (SPTL_EPI_INFLIGHT_KIB=0) and with a tight
+one (64 KiB: one workgroup per CU at 9 inputs of 4096 columns).  The variable is read once per process, so each setting runs in a child
 process.  The default run is also compared with the float64 oracle (bf16 tolerance).
 """
 import os

@@ -9,7 +9,10 @@ staging shapes of the workloads and for edge cases.  Properties checked:
   * with a leading group of copies (lead > 1), each engine takes at most one of the group's
     pieces, the group takes every engine when it is large enough, and the pieces per copy
     follow the copy sizes;
-  * every later copy is striped over the engines, piece p on engine p.
+  * the later copies are grouped so that every engine's piece is at least 2 MiB: copies that
+    large on their own are striped over the engines one after another, piece p on engine p;
+    smaller ones are split together in groups like the leading group, and a short last group
+    is merged into the one before, so no copy runs alone at the end.
 """
 import os
 import shutil
@@ -36,10 +39,21 @@ def driver(tmp_path_factory):
     return exe
 
 
-def plan(driver, engines, split, lead, sizes):
-    out = subprocess.run([driver, str(engines), str(split), str(lead), *map(str, sizes)], check=True,
-                         capture_output=True, text=True, timeout=30).stdout
-    return [tuple(int(v) for v in line.split()) for line in out.splitlines()]
+def plan(driver, engines, split, lead, sizes, group=1):
+    out = subprocess.run([driver, str(engines), str(split), str(lead), str(group), *map(str, sizes)], check=True,
+                         capture_output=True, text=True, timeout=30).stdout.splitlines()
+    assert out[0].startswith("group ")
+    plan.group = int(out[0].split()[1])
+    return [tuple(int(v) for v in line.split()) for line in out[1:]]
+
+
+def check_group(by_copy, copies, engines):
+    """The copies of one group take distinct engines, every engine when they can."""
+    group = [p for c in copies for p in by_copy[c]]
+    used = [e for _, _, _, e in group]
+    assert len(used) == len(set(used)), f"an engine takes two pieces of the group {copies}"
+    if sum(len(by_copy[c]) for c in copies) >= engines or all(len(by_copy[c]) > 1 for c in copies):
+        assert len(group) == engines
 
 
 def check_cover(pieces, sizes, split):
@@ -63,31 +77,61 @@ def check_cover(pieces, sizes, split):
     return by_copy
 
 
-# staged peers (+ own slot) of the workloads: (engines, lead, sizes)
+# staged peers (+ own slot) of the workloads: (engines, lead, sizes, expected later groups)
 WORKLOAD_PLANS = [
-    (14, 3, [8 * MiB] * 7 + [8 * MiB]),        # 8192 x 4096, tp = 8: peers 1-3 lead the first round
-    (14, 1, [28 * MiB] * 3 + [28 * MiB]),      # Qwen2-like, tp = 4
-    (14, 1, [64 * MiB] * 7 + [64 * MiB]),      # M-sweep top, tp = 8
-    (14, 7, [8 * MiB] * 7),                    # every peer in the first round
+    # 8192 x 4096, tp = 8: peers 1-3 lead the first round; peers 4-7 and the own slot are split
+    # together (8 MiB striped over 14 engines would give 585 KB pieces)
+    (14, 3, [8 * MiB] * 7 + [8 * MiB], [[3, 4, 5, 6, 7]]),
+    (14, 1, [28 * MiB] * 3 + [28 * MiB], [[0], [1], [2], [3]]),      # Qwen2-like, tp = 4
+    (14, 1, [64 * MiB] * 7 + [64 * MiB], [[c] for c in range(8)]),  # M-sweep top, tp = 8
+    (14, 7, [8 * MiB] * 7, []),                                     # every peer in the first round
 ]
 
 
-@pytest.mark.parametrize("engines,lead,sizes", WORKLOAD_PLANS)
-def test_workload_plans(driver, engines, lead, sizes):
-    pieces = plan(driver, engines, 1, lead, sizes)
+@pytest.mark.parametrize("engines,lead,sizes,groups", WORKLOAD_PLANS)
+def test_workload_plans(driver, engines, lead, sizes, groups):
+    pieces = plan(driver, engines, 1, lead, sizes, group=0)
     by_copy = check_cover(pieces, sizes, 1)
     if lead > 1:
-        group = [p for c in range(lead) for p in by_copy[c]]
-        engines_used = [e for _, _, _, e in group]
-        assert len(engines_used) == len(set(engines_used)), "an engine takes two pieces of the leading group"
-        assert len(group) == engines
+        check_group(by_copy, range(lead), engines)
         counts = [len(by_copy[c]) for c in range(lead)]
         assert max(counts) - min(counts) <= 1, f"equal copies get unequal piece counts {counts}"
-    for c in range(lead if lead > 1 else 0, len(sizes)):
-        for off, n, piece, engine in by_copy[c]:
-            assert engine == piece % engines
-    if lead == 1:
-        assert len(by_copy[0]) == min(MAX_PIECES, engines, sizes[0] // MIN_PIECE)
+    for g in groups:
+        if len(g) == 1:  # striped alone
+            for off, n, piece, engine in by_copy[g[0]]:
+                assert engine == piece % engines
+            assert len(by_copy[g[0]]) == min(MAX_PIECES, engines, sizes[g[0]] // MIN_PIECE)
+        else:
+            check_group(by_copy, g, engines)
+            assert min(n for c in g for _, n, _, _ in by_copy[c][:-1]) >= 2 * MiB - 256
+    # pieces are submitted group by group, in copy order
+    order = [c for c, *_ in pieces]
+    assert order == sorted(order)
+
+
+@pytest.mark.parametrize("engines,chunk,want", [
+    (14, 8 * MiB, 4), (14, 28 * MiB, 1), (14, 64 * MiB, 1), (14, 64 * 1024, 14), (1, 8 * MiB, 1), (7, 8 * MiB, 2),
+])
+def test_group_size_rule(driver, engines, chunk, want):
+    plan(driver, engines, 1, 1, [chunk], group=0)
+    assert plan.group == want
+
+
+def test_explicit_groups_and_short_last_group(driver):
+    sizes = [4 * MiB] * 8
+    by_copy = check_cover(plan(driver, 14, 1, 1, sizes, group=3), sizes, 1)
+    # groups [0, 1, 2] and [3 .. 7]: the last two copies join the group before them
+    check_group(by_copy, [0, 1, 2], 14)
+    check_group(by_copy, [3, 4, 5, 6, 7], 14)
+    # too many to merge on 4 engines: groups [0..3], [4..7] stay apart
+    by_copy = check_cover(plan(driver, 4, 1, 1, sizes, group=4), sizes, 1)
+    check_group(by_copy, [0, 1, 2, 3], 4)
+    check_group(by_copy, [4, 5, 6, 7], 4)
+    # a last group of one that cannot merge (5 copies on 4 engines in groups of 4)
+    sizes = [4 * MiB] * 5
+    by_copy = check_cover(plan(driver, 4, 1, 1, sizes, group=4), sizes, 1)
+    check_group(by_copy, [0, 1, 2, 3], 4)
+    assert [e for _, _, _, e in by_copy[4]] == [0, 1, 2, 3]
 
 
 def test_leading_group_follows_sizes(driver):
