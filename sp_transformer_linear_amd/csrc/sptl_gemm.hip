@@ -937,15 +937,9 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Workgroups of a persistent launch on the current device: its CU count, rounded down to a
-// multiple of 8 (one workgroup per CU, each keeping its XCD).
-int persistent_grid() {
-    // SPTL_GEMM_PERSIST=0 launches one workgroup per tile instead (measurement aid)
-    static const bool off = [] {
-        const char *e = getenv("SPTL_GEMM_PERSIST");
-        return e && !strcmp(e, "0");
-    }();
-    if (off) return 0x7fffffff;
+// CUs of the current device, rounded down to a multiple of 8 (so that workgroup b of a grid of
+// that size runs on XCD b mod 8, as in any larger grid).
+int device_cus8() {
     static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -957,6 +951,16 @@ int persistent_grid() {
         cached[dev].store(g, std::memory_order_relaxed);
     }
     return g;
+}
+
+// Workgroups of a persistent launch on the current device: one per CU (device_cus8).
+int persistent_grid() {
+    // SPTL_GEMM_PERSIST=0 launches one workgroup per tile instead (measurement aid)
+    static const bool off = [] {
+        const char *e = getenv("SPTL_GEMM_PERSIST");
+        return e && !strcmp(e, "0");
+    }();
+    return off ? 0x7fffffff : device_cus8();
 }
 
 template <int WGM, int WGN, int SLOTS>
@@ -1020,7 +1024,7 @@ void chunk_layout(ChunkPlan &plan, int bm, int64_t tiles_n) {
     plan.xcd_group = g;
     plan.chunk_band = kBand;
     if (!g) return;
-    const int64_t conc = persistent_grid() / 8, share = per_chunk / g;
+    const int64_t conc = device_cus8() / 8, share = per_chunk / g;
     const int64_t width = share < conc ? share : conc, chunks = (conc + share - 1) / share;
     int64_t best = -1;
     for (int b = 1; b <= 8 && b <= tpc; b *= 2) {
