@@ -3,7 +3,7 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input, inputs resident
 in HBM:
-  1. agmm_chunked        sequence all-gather staged by the SDMA copy engines (striped over
+  1. agmm_chunked        sequence all-gather staged by the SDMA copy engines (spread over
                          all engines, released at the call's fork point) overlapped with one
                          chunk-ordered column-parallel GEMM launch (bf16 MFMA, fp32
                          accumulate) whose tiles wait for their chunk's completion signal;

@@ -141,7 +141,9 @@ const char *sptl_ctx_info(sptl_ctx *ctx);
  *   - Every peer chunk is split into pieces for the SDMA copy engines.  The peer chunks that
  *     the GEMM's first round of tiles needs (one tile per compute unit, the round sized for
  *     an output at least `hidden` wide) are split together, one piece per engine, so that
- *     they land together; every later chunk is striped over all engines.  The pieces are
+ *     they land together.  The later copies are split together in groups large enough that
+ *     every engine's piece is at least 2 MiB (a chunk that large on its own is striped over
+ *     all engines), a short last group joining the one before.  The pieces are
  *     submitted by the context's worker thread as soon as an event recorded on `compute` at
  *     the call's position has completed, so the copies never overwrite x_gathered while
  *     earlier work on `compute` still reads it.  Copy order: chunks of ranks rank+1, ...,
