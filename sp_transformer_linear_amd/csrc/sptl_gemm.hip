@@ -710,6 +710,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // flop, which at the chip's power limit lets the clock run higher (about 10 % more GEMM
 // throughput with random operands).
 //
+// Four waves (WGM = WGN = 2): each wave owns 128 x 128 (8 x 8 blocks), so a stage's fragment
+// reads are a third fewer bytes per MFMA than with eight waves of 64 x 128.  Its 256
+// accumulator registers per lane live in the AGPRs: the MFMAs are written as inline assembly
+// with the accumulator tied to an AGPR operand (with the builtin, the register allocator
+// permutes the accumulators between AGPRs and VGPRs at the loop head every iteration).  With
+// one wave per SIMD, each stage interleaves its work so that the matrix core always has MFMAs
+// queued: the barrier comes after the first column block of MFMAs (which need only registers),
+// and after each column block follow one of the stage's global loads and the next stage's
+// fragment reads for that block (the A fragments, all of which the next stage's first block
+// needs, in the first half).
+//
 // Persistent: workgroup b takes tiles b, b + G, b + 2 G, ... (G = gridDim.x, a multiple of 8,
 // so every tile keeps the XCD of a one-tile-per-workgroup launch).  The ring runs on across
 // tiles: SLOTS - 1 stages before the end of a tile its first wave checks, without waiting,
@@ -730,7 +741,12 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BM = 256, BN = 256, TM = BM / WGM / 16, TN = BN / WGN / 16;  // 16 x 16 blocks per wave
     constexpr int NBLK = 16 / (WGM * WGN);   // 1 KB blocks per operand per wave per stage
+    constexpr bool kFour = WGM * WGN == 4;   // the four-wave form (AGPR accumulators)
     static_assert(NBLK * WGM * WGN == 16 && SLOTS >= 4 && SLOTS * 2 * kDmaSlotBytes <= 160 * 1024, "shape");
+    static_assert(!kFour || (TN == 2 * NBLK && TM % 2 == 0 && TM / 2 <= TN), "four-wave stage layout");
+    // The four-wave form keeps its accumulators in AGPRs; naming one here makes the compiler
+    // allocate them (it assumes none are used otherwise).
+    if constexpr (kFour) asm volatile("; agprs in use" ::: "a0");
     constexpr int B_ROW = BN * 2;
     constexpr int SLOT = 2 * kDmaSlotBytes;  // ring slot: A (16 KB) then B (16 KB)
     __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT];
@@ -755,6 +771,20 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         a_off[t] = (int)((row * p.lda + c * 8) * 2);
     }
     const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * NBLK) * 1024;  // this wave's first block
+    // Load t of a stage's A blocks and of its B blocks, into the slot at la / lb.
+    auto load_a = [&](const u32x4_t &ar, uint32_t la, int t, bool k_tail, int64_t k0) __attribute__((always_inline)) {
+        const int off = (k_tail && k0 + a_kc[t] >= p.k) ? kOutOfRange : a_off[t];
+        load_to_lds(ar, la + t * 1024, off);
+    };
+    auto load_b = [&](const u32x4_t &br, uint32_t lb, int t, int64_t n0) __attribute__((always_inline)) {
+        // B block: k-rows 2 blk, 2 blk + 1 (lane / 32); lanes q, q + 1 read the two halves of the
+        // swizzled 32-byte unit (q / 2) of that row (recomputed here rather than kept in
+        // registers across the tiles)
+        const int krow = (wave * NBLK + t) * 2 + (lane >> 5);
+        const int q = lane & 31;
+        const int64_t n = n0 + (((q >> 1) ^ (((krow & 3) << 1) | ((krow >> 3) & 1))) * 16 + (q & 1) * 8);
+        load_to_lds(br, lb + t * 1024, n < p.n ? (int)((krow * p.ldb + n) * 2) : kOutOfRange);
+    };
 
     // Stage kt of the tile at `o` into ring slot `slot`; live = false (or kt >= nk) reads an
     // empty range (zeros), so every stage issues exactly 2 NBLK loads per wave and the wait
@@ -769,20 +799,9 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         const u32x4_t br = buffer_desc(p.b + k0 * p.ldb, (uint32_t)(k_rows * p.ldb * 2));
         const uint32_t la = lds0 + (uint32_t)(slot * SLOT), lb = la + kDmaSlotBytes;
 #pragma unroll
-        for (int t = 0; t < NBLK; ++t) {
-            const int off = (k_tail && k0 + a_kc[t] >= p.k) ? kOutOfRange : a_off[t];
-            load_to_lds(ar, la + t * 1024, off);
-        }
+        for (int t = 0; t < NBLK; ++t) load_a(ar, la, t, k_tail, k0);
 #pragma unroll
-        for (int t = 0; t < NBLK; ++t) {
-            // B block: k-rows 2 blk, 2 blk + 1 (lane / 32); lanes q, q + 1 read the two halves
-            // of the swizzled 32-byte unit (q / 2) of that row (recomputed here rather than kept
-            // in registers across the tiles)
-            const int krow = (wave * NBLK + t) * 2 + (lane >> 5);
-            const int q = lane & 31;
-            const int64_t n = o.n0 + (((q >> 1) ^ (((krow & 3) << 1) | ((krow >> 3) & 1))) * 16 + (q & 1) * 8);
-            load_to_lds(br, lb + t * 1024, n < p.n ? (int)((krow * p.ldb + n) * 2) : kOutOfRange);
-        }
+        for (int t = 0; t < NBLK; ++t) load_b(br, lb, t, o.n0);
     };
 
     // Fragment read addresses within a slot.  A block i (16 rows): lane l reads row
@@ -849,11 +868,13 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     int slot0 = 0;            // ring slot of the current tile's stage 0
     bool prefetched = false;  // the current tile's stages 0 .. SLOTS - 2 are already in flight
     const int kt_check = nk - SLOTS;  // the next tile's chunk is checked at about this stage
-    for (int vb = blockIdx.x; vb < nt; vb += gridDim.x) {
+    for (int vb = blockIdx.x; vb < nt; vb = kFour ? nt : vb + (int)gridDim.x) {
         TileOrigin o, on;
         tile_origin<BM, BN, CHUNKED>(p, tiles_m, tiles_n, o, vb);
         const int vn = vb + (int)gridDim.x;
-        const bool has_next = vn < nt && kt_check >= 0;
+        // the four-wave form runs one tile per workgroup (its launch has a workgroup per tile),
+        // which leaves out the next tile's state and keeps its registers within the VGPRs
+        const bool has_next = !kFour && vn < nt && kt_check >= 0;
         if (has_next) tile_origin<BM, BN, CHUNKED>(p, tiles_m, tiles_n, on, vn);
         else on = o;  // never loaded from (its stages are issued with an empty range)
         tile_wait<CHUNKED>(p, o, vb);  // at once when prefetched: the chunk was seen landed
@@ -877,6 +898,49 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         // and make every wave's visible (the barrier also retires the slot of stage kt - 1,
         // whose fragments were read during stage kt - 2); start stage kt + SLOTS - 1 (of the next
         // tile past the end) into that slot; read stage kt + 1 into S1 during the MFMAs.
+        // Four-wave stage kt (see above): column block j of the MFMAs, then (after block 0) the
+        // wait and barrier of the eight-wave stage, then global load j of stage kt + SLOTS - 1
+        // (past the tile's end, an empty range, as the eight-wave stage issues with no next
+        // tile), then the next stage's fragment reads for block j.  Empty asm statements with a
+        // memory clobber keep the reads and loads between the blocks they were written between.
+        auto stage4 = [&](int kt, int S0, int S1) __attribute__((always_inline)) {
+            const int nslot = slot_of(slot0 + kt + 1);
+            const int fslot = slot_of(slot0 + kt + SLOTS - 1);
+            const int g = kt + SLOTS - 1;
+            const bool live = g < nk;
+            const int64_t k0 = live ? (int64_t)g * kDmaBK : 0;
+            const int64_t a_bytes = live ? ((int64_t)o.rows_valid * p.lda - k0) * 2 : 0;
+            const u32x4_t ar = buffer_desc(o.a_tile + k0, (uint32_t)a_bytes);
+            const bool k_tail = k0 + kDmaBK > p.k;
+            const int64_t k_rows = !live ? 0 : (p.k - k0) < kDmaBK ? (p.k - k0) : kDmaBK;
+            const u32x4_t br = buffer_desc(p.b + k0 * p.ldb, (uint32_t)(k_rows * p.ldb * 2));
+            const uint32_t la = lds0 + (uint32_t)(fslot * SLOT), lb = la + kDmaSlotBytes;
+            const char *ns = smem + nslot * SLOT;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                                 : "+a"(acc[i][j])
+                                 : "v"(fa[S0][i]), "v"(fb[S0][j]));
+                asm volatile("" ::: "memory");
+                if (j == 0) {
+                    wait_vmcnt<2 * NBLK * (SLOTS - 3)>();  // SLOTS - 3 later stages may stay in flight
+                    __syncthreads();
+                }
+                if (j < NBLK) load_a(ar, la, j, k_tail, k0);
+                else load_b(br, lb, j - NBLK, o.n0);
+                if (2 * j < TM) {
+                    fa[S1][2 * j] = *reinterpret_cast<const bf16x8_t *>(ns + a_addr[2 * j]);
+                    fa[S1][2 * j + 1] = *reinterpret_cast<const bf16x8_t *>(ns + a_addr[2 * j + 1]);
+                }
+                const char *base = ns + b_addr[j];
+                bf16x4_t blo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
+                bf16x4_t bhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * B_ROW));
+                fb[S1][j] = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
+                asm volatile("" ::: "memory");
+            }
+        };
         auto stage = [&](int kt, int S0, int S1) {
             const int nslot = slot_of(slot0 + kt + 1);
             const int fslot = slot_of(slot0 + kt + SLOTS - 1);
@@ -899,11 +963,22 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
                 const bool ok = has_next && (!CHUNKED || chunk_ready_now(p.plan, on.chunk, vn));
                 if (lane == 0) next_ok_lds = ok ? 1 : 0;
             }
-            stage(kt, 0, 1);
-            stage(kt + 1, 1, 0);
+            if constexpr (kFour) {
+                stage4(kt, 0, 1);
+                stage4(kt + 1, 1, 0);
+            } else {
+                stage(kt, 0, 1);
+                stage(kt + 1, 1, 0);
+            }
             kt += 2;
         }
-        if (kt < nk) stage(kt, 0, 1);
+        if (kt < nk) {
+            if constexpr (kFour) stage4(kt, 0, 1);
+            else stage(kt, 0, 1);
+        }
+        // the accumulators are read next; the compiler does not know the inline-assembly MFMAs
+        // wrote them, so their result latency is waited out here (32 wait states)
+        if constexpr (kFour) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         tile_end16<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc, vb);
         prefetched = has_next && next_ok;
         slot0 = slot_of(slot0 + nk);
@@ -969,7 +1044,8 @@ hipError_t launch_ring(const GemmProblem &p, hipStream_t stream) {
     const int64_t nt = tm * tn;
     if (nt == 0) return hipSuccess;
     if (nt > 0x7fffffff) return hipErrorInvalidValue;
-    const int64_t g = persistent_grid();
+    // one workgroup per CU, each taking several tiles; the four-wave form one workgroup per tile
+    const int64_t g = WGM * WGN == 4 ? nt : persistent_grid();
     const dim3 grid((unsigned)(nt < g ? nt : g)), block(64 * WGM * WGN);
     const bool chunked = p.plan.chunk_rows != 0;
     if (p.c_f32 && chunked)
@@ -985,7 +1061,8 @@ hipError_t launch_ring(const GemmProblem &p, hipStream_t stream) {
 
 // Tile configurations.  All share the MFMA instruction and the K order.
 enum Config { k256x256w2x2, k256x256w2x4, k256x256w4x2, k256x128w4x2, k256x128w4x1, k128x128w2x2, k256x256ring,
-              k128x256w2x2k32, k256x256w4x2k32, k256x256bt, k256x256il2, k256x256il4, k256x256btil2, kNumConfigs };
+              k128x256w2x2k32, k256x256w4x2k32, k256x256bt, k256x256il2, k256x256il4, k256x256btil2, k256x256ring4,
+              kNumConfigs };
 
 const char *config_name(int c) {
     switch (c) {
@@ -1001,9 +1078,12 @@ const char *config_name(int c) {
         case k256x256il2: return "256x256il2";
         case k256x256il4: return "256x256il4";
         case k256x256btil2: return "256x256btil2";
+        case k256x256ring4: return "256x256ring4";
         default: return "128x128w2x2";
     }
 }
+
+constexpr int64_t kFourWaveMinK = 2048;
 
 int config_rows(int c) { return c == k128x128w2x2 || c == k128x256w2x2k32 ? 128 : 256; }
 int config_cols(int c) { return c == k256x128w4x2 || c == k256x128w4x1 || c == k128x128w2x2 ? 128 : 256; }
@@ -1056,12 +1136,16 @@ int resolve(const GemmProblem &p, GemmTile t) {
         return p.plan.chunk_rows % 256 == 0 ? k256x256ring : k128x128w2x2;
     }
     if (forced_config() >= 0) return forced_config();
-    if (t == GemmTile::T256x256) return k256x256ring;
+    // 256 x 256 tiles: the four-wave form when K is long enough to carry its per-tile start (it
+    // runs one tile per workgroup, with no next-tile prefetch); measured +1 to +3 % at K = 3584
+    // and 4096, -9 % at K = 768
+    const int wide = p.k >= kFourWaveMinK ? k256x256ring4 : k256x256ring;
+    if (t == GemmTile::T256x256) return wide;
     if (t == GemmTile::T128x128) return k128x128w2x2;
     // One wave of 256 x 256 tiles needs about one workgroup per CU (256 on MI355X); below
     // that, 128 x 128 tiles keep every CU busy.
     const int64_t big = ((p.m + 255) / 256) * ((p.n + 255) / 256);
-    return big >= 240 ? k256x256ring : k128x128w2x2;
+    return big >= 240 ? wide : k128x128w2x2;
 }
 
 }  // namespace
@@ -1095,6 +1179,7 @@ hipError_t launch_gemm(const GemmProblem &problem, hipStream_t stream, GemmTile 
         case k256x128w4x2: return launch_cfg<256, 128, 4, 2>(p, stream);
         case k256x128w4x1: return launch_cfg<256, 128, 4, 1>(p, stream);
         case k256x256ring: return launch_ring<4, 2, 4>(p, stream);
+        case k256x256ring4: return launch_ring<2, 2, 4>(p, stream);
         case k128x256w2x2k32: return launch_cfg<128, 256, 2, 2, 32, 2>(p, stream);
         case k256x256w4x2k32: return launch_cfg<256, 256, 4, 2, 32>(p, stream);
         case k256x256bt: return launch_cfg<256, 256, 4, 2, kBK, 1, true>(p, stream);

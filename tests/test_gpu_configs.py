@@ -101,7 +101,7 @@ def reference(inputs):
 
 
 @pytest.mark.parametrize("cfg", ["256x256w4x2", "256x256w2x4", "256x256w2x2", "256x128w4x2", "256x128w4x1",
-                                 "128x128w2x2", "256x256ring", "128x256w2x2k32", "256x256w4x2k32",
+                                 "128x128w2x2", "256x256ring", "256x256ring4", "128x256w2x2k32", "256x256w4x2k32",
                                  "256x256bt", "256x256il2", "256x256il4", "256x256btil2"])
 def test_forced_config_is_bit_identical(inputs, reference, cfg):
     d, inp, _ = inputs
