@@ -1133,12 +1133,15 @@ int resolve(const GemmProblem &p, GemmTile t) {
     if (p.plan.chunk_rows) {  // chunk-ordered: the tile height must divide the chunk
         if (forced_config() >= 0 && p.plan.chunk_rows % config_rows(forced_config()) == 0)
             return forced_config();
-        return p.plan.chunk_rows % 256 == 0 ? k256x256ring : k128x128w2x2;
+        if (p.plan.chunk_rows % 256) return k128x128w2x2;
+        // measured at 8192 x 4096 x 4096: 907-920 against 880-891 TFLOP/s for the eight-wave
+        // persistent kernel (whose next-tile prefetch the four-wave form does not have)
+        return p.k >= kFourWaveMinK ? k256x256ring4 : k256x256ring;
     }
     if (forced_config() >= 0) return forced_config();
     // 256 x 256 tiles: the four-wave form when K is long enough to carry its per-tile start (it
-    // runs one tile per workgroup, with no next-tile prefetch); measured +1 to +3 % at K = 3584
-    // and 4096, -9 % at K = 768
+    // runs one tile per workgroup, with no next-tile prefetch); gemm_partial measured +1 to +3 %
+    // at K = 3584 and 4096, -9 % at K = 768
     const int wide = p.k >= kFourWaveMinK ? k256x256ring4 : k256x256ring;
     if (t == GemmTile::T256x256) return wide;
     if (t == GemmTile::T128x128) return k128x128w2x2;
