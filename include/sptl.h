@@ -150,9 +150,9 @@ const char *sptl_ctx_info(sptl_ctx *ctx);
  *     rank+tp-1 (mod tp), then this rank's own slot unless shard_src[rank] aliases it.
  *   - ONE GEMM launch on `compute` processes row tiles in chunk order: this rank's chunks
  *     first (read straight from shard_src[rank]), then the peers' chunks in copy order;
- *     each tile waits on the GPU for its own chunk's pieces to land.  At hidden >= 2048 the
- *     launch has one workgroup per tile; below, one workgroup per compute unit, each taking
- *     its tiles in that order.
+ *     each tile waits on the GPU for its own chunk's pieces to land.  The launch has one
+ *     workgroup per tile, except with 256-row tiles at hidden < 2048: then one workgroup per
+ *     compute unit, each taking its tiles in that order.
  *     The launch ends only after every copy of the call (own slot included) has landed.
  *   - Up to 4 staged calls per context may be in flight; a fifth blocks the calling thread
  *     until the oldest has finished on the GPU.
