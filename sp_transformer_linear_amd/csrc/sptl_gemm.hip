@@ -5,7 +5,16 @@
 // all-gather + matmul and the row-parallel partial-sum GEMM ("Potential Solution" of the
 // AReaL async-TP issue; "partial output" in the delayed-TP abstract).
 //
-// Design for gfx950:
+// Two kernels, chosen per call (resolve()):
+//   * the ring kernel (gemm_ring_kernel, described at its definition): 256 x 256 tiles,
+//     v_mfma_f32_16x16x32_bf16, direct-to-LDS loads into a ring of stages.  Its four-wave form
+//     runs every 256 x 256 GEMM with K >= 2048 (one workgroup per tile); its eight-wave form
+//     runs shorter K (persistent, with the next tile's first stages prefetched);
+//   * the register-staged kernel (gemm_bf16_kernel, described next): 128 x 128 tiles for
+//     GEMMs too small to fill the chip with 256 x 256 tiles or chunks of 128-row multiples,
+//     and the other measured configurations.
+//
+// Register-staged kernel, design for gfx950:
 //   * A workgroup owns a BM x BN output tile; its WGM x WGN wave64s each own a (BM/WGM) x
 //     (BN/WGN) block made of 32 x 32 blocks of v_mfma_f32_32x32x16_bf16.
 //   * K is walked in stages of 64.  A stage of A ([BM][64]) and B ([64][BN]) sits in LDS,
