@@ -158,7 +158,10 @@ def test_agmm_timeline(env):
 # ------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,K,H", [(256, 512, 256), (300, 200, 136), (1, 8, 8), (777, 1032, 520),
-                                   (2048, 256, 2048)])
+                                   (2048, 256, 2048),
+                                   # 17 x 17 tiles of 256 x 256 at K >= 2048: the four-wave form,
+                                   # ragged in M, N and K
+                                   (4100, 2056, 4104)])
 @pytest.mark.parametrize("out_f32", [True, False])
 def test_gemm_partial_parity(env, M, K, H, out_f32):
     torch, sptl, ctx = env
@@ -347,6 +350,9 @@ STAGED_CASES = [
     (2, 2, 384, 256, 264, 0),      # 384-row chunks: 128 x 128 tiles, ragged N
     (8, 16, 256, 200, 520, 5),     # two chunks per rank, ragged K and N
     (3, 3, 512, 1024, 1024, 2),    # odd TP degree
+    # K >= 2048: the four-wave form, one workgroup per tile
+    (4, 8, 512, 2048, 520, 2),     # two chunks per rank, ragged N
+    (2, 2, 256, 2056, 264, 1),     # K ends on a partial stage
 ]
 
 
