@@ -55,7 +55,8 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("sp_transformer_linear_amd/csrc/sptl_gemm.hip", "sp_transformer_linear_amd/csrc/sptl_internal.h")
+KERNEL_SOURCES = ("sp_transformer_linear_amd/csrc/sptl_gemm.hip", "sp_transformer_linear_amd/csrc/sptl_internal.h",
+                  "sp_transformer_linear_amd/csrc/sptl_tilemap.h")
 
 
 def kernel_source_hash() -> str:

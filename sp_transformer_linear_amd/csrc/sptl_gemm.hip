@@ -51,6 +51,7 @@
 #include <cstring>
 
 #include "sptl_internal.h"
+#include "sptl_tilemap.h"
 
 namespace sptl {
 namespace {
@@ -67,7 +68,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kBK = 64;                   // K depth of one LDS stage
 constexpr int kRsrcFlags = 0x00020000;    // raw buffer, 32-bit data format
 constexpr int kOutOfRange = 0x7ffffff0;   // an offset past any num_records used here
-constexpr int kBand = 4;                  // tile rows per band of the plain tile order
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -179,46 +179,19 @@ __device__ __forceinline__ void tile_origin(const GemmProblem &p, int tiles_m, i
     int &chunk = o.chunk;
     chunk = -1;
     if constexpr (!CHUNKED) {
-        // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes a contiguous run
-        // of a banded order (bands of kBand tile rows, column-major inside a band), so the
-        // workgroups an XCD runs at once cover a few rows by several columns and share A
-        // and B panels in its L2.
-        const int nt = tiles_m * tiles_n;
-        const int per = nt >> 3, rem = nt & 7;
-        const int xcd = bid & 7, slot = bid >> 3;
-        const int t = xcd * per + (xcd < rem ? xcd : rem) + slot;
-        const int band = t / (kBand * tiles_n), in_band = t - band * (kBand * tiles_n);
-        const int band_rows = tiles_m - band * kBand < kBand ? tiles_m - band * kBand : kBand;
-        const int tm = band * kBand + in_band % band_rows, tn = in_band / band_rows;
+        // XCD-aware tile order (plain_tile, sptl_tilemap.h)
+        int tm, tn;
+        plain_tile(tiles_m, tiles_n, bid, tm, tn);
         m0 = (int64_t)tm * BM;
         n0 = (int64_t)tn * BN;
         a_tile = p.a + m0 * p.lda;
         rows_valid = (int)((p.m - m0) < BM ? (p.m - m0) : BM);
     } else {
-        // Chunk-ordered: each XCD (workgroups x mod 8) runs its workgroups in index order, so
-        // on every XCD the tiles of chunks that land first come first.  A chunk is a whole
-        // number of tile rows.  With g = plan.xcd_group > 0 a chunk's tiles go to a group of g
-        // XCDs, 8 / g chunks run side by side, and each XCD's share of a chunk is a contiguous
-        // run of the chunk's banded order (plan.chunk_band tile rows, column-major), so the
-        // workgroups an XCD runs at once share a few A and B panels in its L2 (chunk_layout).
-        const int tpc = plan.chunk_rows / BM;
-        const int per_chunk = tpc * tiles_n;
-        const int g = plan.xcd_group, kb = plan.chunk_band;
+        // Chunk-ordered: on every XCD the tiles of chunks that land first come first (chunk_tile,
+        // sptl_tilemap.h, with the layout chunk_layout chose).  A chunk is a whole number of
+        // tile rows.
         int pos, sub, tn;
-        if (g) {
-            const int x = bid & 7, slot = bid >> 3, share = per_chunk / g;
-            pos = (slot / share) * (8 / g) + x / g;
-            const int t = (x % g) * share + slot % share;
-            const int band = t / (kb * tiles_n), in_band = t - band * (kb * tiles_n);
-            const int band_rows = tpc - band * kb < kb ? tpc - band * kb : kb;
-            sub = band * kb + in_band % band_rows;
-            tn = in_band / band_rows;
-        } else {
-            pos = bid / per_chunk;
-            const int local = bid - pos * per_chunk;
-            sub = local / tiles_n;
-            tn = local - sub * tiles_n;
-        }
+        chunk_tile(plan.chunk_rows / BM, tiles_n, plan.xcd_group, plan.chunk_band, bid, pos, sub, tn);
         chunk = plan.order[pos];
         m0 = (int64_t)chunk * plan.chunk_rows + (int64_t)sub * BM;
         n0 = (int64_t)tn * BN;
@@ -1097,33 +1070,12 @@ constexpr int64_t kFourWaveMinK = 2048;
 int config_rows(int c) { return c == k128x128w2x2 || c == k128x256w2x2k32 ? 128 : 256; }
 int config_cols(int c) { return c == k256x128w4x2 || c == k256x128w4x1 || c == k128x128w2x2 ? 128 : 256; }
 
-// Chunk-ordered tile layout (see tile_origin).  XCDs per chunk g: the forced value if it divides
-// evenly, else the most XCDs that divide a chunk's tiles (with 8 / g dividing the chunk count),
-// so that a chunk that has landed while others have not spreads over the whole chip; 0 when
-// none divides (plain chunk order).  Band height: each XCD runs `conc` workgroups at once (one
-// per CU), which cover min(conc, share) tiles of each of ceil(conc / share) chunks, every chunk's
-// share a band rows x ceil(share / band) columns block at the same columns; the band minimises
-// the A plus B panels those workgroups read (ties: the band nearest kBand).
+// Chunk-ordered tile layout (chunk_layout_choice, sptl_tilemap.h): plan.xcd_group holds a
+// forced group size or 0 on entry and the chosen one on return; each XCD runs one workgroup per
+// CU at once.
 void chunk_layout(ChunkPlan &plan, int bm, int64_t tiles_n) {
-    const int64_t tpc = plan.chunk_rows / bm, per_chunk = tpc * tiles_n;
-    auto fits = [&](int c) { return per_chunk % c == 0 && plan.n_chunks % (8 / c) == 0; };
-    int g = plan.xcd_group > 0 && fits(plan.xcd_group) ? plan.xcd_group : 0;
-    for (int c = 8; c >= 1 && !g; c /= 2)
-        if (fits(c)) g = c;
-    plan.xcd_group = g;
-    plan.chunk_band = kBand;
-    if (!g) return;
-    const int64_t conc = device_cus8() / 8, share = per_chunk / g;
-    const int64_t width = share < conc ? share : conc, chunks = (conc + share - 1) / share;
-    int64_t best = -1;
-    for (int b = 1; b <= 8 && b <= tpc; b *= 2) {
-        const int64_t panels = chunks * b + (width + b - 1) / b;
-        const int dist = b > kBand ? b - kBand : kBand - b, best_dist = plan.chunk_band > kBand ? plan.chunk_band - kBand : kBand - plan.chunk_band;
-        if (best < 0 || panels < best || (panels == best && dist < best_dist)) {
-            best = panels;
-            plan.chunk_band = b;
-        }
-    }
+    plan.xcd_group = chunk_layout_choice(plan.chunk_rows / bm, tiles_n, plan.n_chunks, plan.xcd_group,
+                                         device_cus8() / 8, &plan.chunk_band);
 }
 
 // SPTL_GEMM_CFG=<name> forces one configuration for every GEMM (measurement aid).
