@@ -19,6 +19,7 @@
 //   * h and y are rounded to bf16 (nearest-even) and stored with 16-byte non-temporal stores
 //     (streamed out rather than kept in the caches: ~11 % more bandwidth on cold inputs).
 #include "sptl_internal.h"
+#include "sptl_epilogue_plan.h"
 
 #include <algorithm>
 #include <atomic>
@@ -179,15 +180,7 @@ __global__ void __launch_bounds__(kMaxThreads) epilogue_wide_kernel(EpilogueProb
 // two-pass kernel.
 constexpr int kMaxLiveVectors = 36;
 
-// Loads in flight per CU.  Every workgroup keeps all of its row's loads in flight, so the
-// workgroups resident on a CU set how many rows HBM serves at once.  At 8192 rows of 9 inputs
-// and 4096 columns, as many as the registers allow (5 per CU: 368 KiB of loads) streamed
-// about 4 % slower than 3 per CU.  The launch caps the workgroups per CU through their LDS
-// allocation (unused) so that about kInflightBytes of loads are in flight per CU, for launches
-// of at most kCapRowsPerCu rows per CU: at 64 rows per CU the cap was neutral and at 256 it
-// cost about 2 %.  The result bits do not depend on it.
-constexpr int64_t kInflightBytes = 192 * 1024;
-constexpr int64_t kCapRowsPerCu = 48;
+// Workgroups per CU of the register-resident kernel: epilogue_cap_lds (sptl_epilogue_plan.h).
 
 struct DeviceLimits {
     int lds_per_cu = 0, lds_per_block = 0, cus = 0;
@@ -214,24 +207,19 @@ DeviceLimits device_limits() {
     return l;
 }
 
-// Dynamic LDS bytes that cap a launch of `rows` workgroups at the workgroups per CU that keep
-// about kInflightBytes of loads in flight (0: no cap).  SPTL_EPI_INFLIGHT_KIB overrides the
-// target and applies it at any row count (0: never cap; a measurement aid).
+// Dynamic LDS bytes of a launch of `rows` workgroups with `bytes_per_wg` bytes of loads each
+// (0: no cap).  SPTL_EPI_INFLIGHT_KIB overrides the in-flight target and applies it at any row
+// count (0: never cap; a measurement aid).
 size_t inflight_cap_lds(int64_t bytes_per_wg, int64_t rows) {
     static const int64_t forced = [] {
         const char *e = getenv("SPTL_EPI_INFLIGHT_KIB");
         const long v = e ? strtol(e, nullptr, 10) : -1;
         return v >= 0 && v <= 65536 ? (int64_t)v * 1024 : (int64_t)-1;
     }();
+    if (forced == 0) return 0;
     const DeviceLimits l = device_limits();
-    if (forced == 0 || bytes_per_wg <= 0 || l.cus == 0) return 0;
-    if (forced < 0 && rows > kCapRowsPerCu * l.cus) return 0;
-    const int64_t target = forced > 0 ? forced : kInflightBytes;
-    const int64_t wgs = std::max<int64_t>(1, (target + bytes_per_wg / 2) / bytes_per_wg);
-    // a 1 KiB margin for the kernel's own LDS, in 1 KiB steps
-    const int64_t dyn = (l.lds_per_cu / wgs - 1024) / 1024 * 1024;
-    if (dyn <= 0 || dyn > l.lds_per_block - 1024) return 0;
-    return (size_t)dyn;
+    return (size_t)epilogue_cap_lds(bytes_per_wg, rows, forced > 0 ? forced : kInflightBytes, forced > 0,
+                                    l.lds_per_cu, l.lds_per_block, l.cus);
 }
 
 template <int N, int VPT>
