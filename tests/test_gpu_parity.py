@@ -113,6 +113,48 @@ def test_agmm_own_slot_aliased(env):
     assert_within(y.cpu().numpy().astype(np.float64), y_want, fp32_tol(y_want), "y")
 
 
+def test_boundary_epilogue_into_gather_slot(env):
+    """Sub-layer boundary: the epilogue writes its normalised rows straight into the own slot of
+    the next gather, and agmm_chunked reads them there (no own-slot copy).  The GEMM output is
+    bit for bit the one from the same rows in a buffer of their own, and within the oracle's
+    bound: the GEMM tolerance plus |y error| @ |W|, the epilogue's own tolerance carried
+    through the product."""
+    torch, sptl, ctx = env
+    tp, rows, H, N, rank, P = 4, 136, 264, 200, 1, 3
+    seed = 41
+    parts_b, res_b, g_b = epi_inputs(seed, rows, H, P)
+    shards_b = [gen(seed, (0, q), rows, H) for q in range(tp)]
+    w_b = gen(seed, (1,), H, N, 1.0 / H)
+    w, res, g = to_dev(w_b), to_dev(res_b), to_dev(g_b)
+    parts = [to_dev(b) for b in parts_b]
+    h_out = torch.empty_like(res)
+    xg = torch.zeros((tp * rows, H), dtype=torch.bfloat16, device="cuda")
+    slot = xg[rank * rows:(rank + 1) * rows]
+    y_sep = torch.empty_like(res)
+    outs = {}
+    for name, dst in (("separate", y_sep), ("in_place", slot)):
+        sptl.reduce_residual_rmsnorm(parts, res, g, 1e-6, dst, residual_out=h_out, ctx=ctx)
+        src = [to_dev(b) for b in shards_b]
+        src[rank] = dst
+        outs[name] = torch.empty((tp * rows, N), dtype=torch.float32, device="cuda")
+        sptl.agmm_chunked(src, xg, w, outs[name], n_chunks=tp, rank=rank, ctx=ctx)
+        torch.cuda.synchronize()
+    assert np.array_equal(to_bits(slot), to_bits(y_sep))
+    assert torch.equal(outs["separate"], outs["in_place"])
+    _, y_norm = O.reduce_residual_rmsnorm(parts_b, res_b, g_b, 1e-6)
+    tol_norm = bf16_tol(y_norm)
+    assert_within(dec(slot), y_norm, tol_norm, "normalised rows in the gather slot")
+    gathered = list(shards_b)
+    gathered[rank] = y_norm
+    _, y_want = O.agmm(gathered, w_b)
+    tol = fp32_tol(y_want) + np.zeros_like(y_want)
+    tol[rank * rows:(rank + 1) * rows] += tol_norm @ np.abs(O.bf16_bits_to_f64(w_b))
+    assert_within(outs["in_place"].cpu().numpy().astype(np.float64), y_want, tol, "y")
+    others = [q for q in range(tp) if q != rank]
+    for q in others:
+        assert np.array_equal(to_bits(xg[q * rows:(q + 1) * rows]), shards_b[q])
+
+
 def test_agmm_default_context_and_copy_stream(env):
     """ctx NULL (per-device default) and a caller-supplied copy stream give the same bits."""
     torch, sptl, ctx = env
