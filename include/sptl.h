@@ -204,7 +204,9 @@ int gemm_partial(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden
  *   gamma     [hidden] bf16;  eps >= 0
  *   residual_out [seq_len, hidden] bf16 receives h; may equal residual (in place);
  *            NULL = do not write h
- *   y         [seq_len, hidden] bf16
+ *   y         [seq_len, hidden] bf16; may point at this rank's own slot of the next layer's
+ *            x_gathered, which agmm_chunked then reads in place when shard_src[rank] is
+ *            the same pointer (no own-slot copy)
  */
 int reduce_residual_rmsnorm(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int tp,
                             const void *const *partials, const void *residual,
