@@ -2,23 +2,29 @@
 """Benchmark of one GPU's share of the SP-TP linear layer on MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input, inputs resident
-in HBM:
+in HBM.  The headline workload (default: M = 65536 tokens x dim 4096 in 8 chunks, tp = 8, the
+top of the M sweep of "Add forward all-gather overlap", Megatron-LM pull request 5513,
+"Observations"; the largest single-GPU workload) runs
   1. agmm_chunked        sequence all-gather staged by the SDMA copy engines (spread over
                          all engines, released at the call's fork point) overlapped with one
                          chunk-ordered column-parallel GEMM launch (bf16 MFMA, fp32
-                         accumulate) whose tiles wait for their chunk's completion signal;
+                         accumulate) whose tiles wait for their chunk's completion signals;
   2. gemm_partial        row-parallel GEMM producing this rank's bf16 partial sum
                          (input = the column GEMM's bf16 output, same weight);
   3. reduce_residual_rmsnorm   own partial + the peers' partials + residual, RMSNorm;
-  4. dtp_accumulate      delayed-TP update (own partial now, peers' partials of an earlier
-                         module), RMSNorm.
+and the delayed-TP module runs at its own workload (Qwen3-0.6B-shaped shard: T = 32768,
+hidden 1024, tp = 4, delta = 1):
+  4. gemm_partial        FFN-down shard 32768 x 768 x 1024 producing the own partial;
+  5. dtp_accumulate      own partial now + the 3 peers' partials of the previous module,
+                         RMSNorm.
 Per-call times come from HIP events on the compute stream that every call is issued on, created
 with hipEventDisableSystemFence (timing only: recording them writes back no cache).
-Per-chunk landing and tile times come from the library's device timestamps (one
-instrumented call outside the timed region).
+Per-chunk landing and tile times come from the library's device timestamps (instrumented calls
+outside the timed region).  Other workloads are measured the same way after the timed region
+(fewer steps) and reported under "other_workloads".
 
-Prints ONE JSON line.  `value` is the chunked AG-GEMM throughput in TFLOP/s (2*M*K*N per
-call over the call's event time, exposed copy included).
+Prints ONE JSON line.  `value` is the chunked AG-GEMM throughput of the headline workload in
+TFLOP/s (2*M*K*N per call over the call's event time, exposed copy included).
 """
 from __future__ import annotations
 
@@ -36,7 +42,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 flop/clk/CU (dense)
 PEAK_HBM_GBS = 8000.0        # HBM3E
-DEFAULT_WORKLOAD = "h100_page_8192x4096"
+DEFAULT_WORKLOAD = "msweep_65536x4096"
+DTP_WORKLOAD = "dtp_qwen3_0p6b_tp4"
+OTHER_WORKLOADS = ("h100_page_8192x4096", "qwen2_7b_tp4_16384")
 
 
 def parse():
@@ -48,6 +56,8 @@ def parse():
     # is 150 steps (~130 ms) and the timed steps measure the settled clock.
     ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--others", default=",".join(OTHER_WORKLOADS),
+                    help="comma-separated workloads measured after the timed region ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 disables it)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -220,6 +230,51 @@ def cpu_baseline(wl, budget_s):
     }
 
 
+def epilogue_bytes(n_in, rows, hidden):
+    """Algorithmic bytes of one epilogue call: n_in bf16 inputs read, h and y written, gamma read."""
+    return n_in * rows * hidden * 2 + 2 * rows * hidden * 2 + hidden * 2
+
+
+class LayerTensors:
+    """Device tensors of one workload's column GEMM, row GEMM and reduce epilogue (bf16)."""
+
+    def __init__(self, wl, torch, dev):
+        def up(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.shards = [up(wl.shard(q)) for q in range(wl.tp)]
+        self.w_col = up(wl.w_col())
+        same_w = wl.K == wl.N and wl.K_row == wl.K and wl.H == wl.N
+        self.w_row = self.w_col if same_w else up(wl.w_row())
+        self.peers = [up(wl.partial(p)) for p in range(1, wl.P)]
+        self.residual = up(wl.residual())
+        self.gamma = up(wl.gamma())
+        self.xg = torch.empty((wl.M, wl.K), dtype=torch.bfloat16, device=dev)
+        self.y_col = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+        self.a_row = self.y_col if wl.N == wl.K_row else up(wl.a_row())
+        self.own = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
+        self.y_norm = torch.empty_like(self.h)
+
+
+class DtpTensors:
+    """Device tensors of the delayed-TP module: FFN-down shard GEMM + delayed accumulation."""
+
+    def __init__(self, wl, torch, dev):
+        def up(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.delta = wl.delta
+        self.a = up(wl.a_row())                     # [T, 768] input of the FFN-down shard
+        self.w = up(wl.w_row())                     # [768, 1024]
+        self.own = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
+        # the peers' partials of module (delta - delta) = 0, in peer rank order
+        self.peers = [up(wl.peer(0, q)) for q in range(wl.tp - 1)]
+        self.x = up(wl.residual())
+        self.gamma = up(wl.gamma())
+        self.y = torch.empty_like(self.x)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -231,36 +286,20 @@ def main():
     from sp_transformer_linear_amd import sptl, synth
 
     wl = synth.WORKLOADS[args.workload]
+    wd = synth.WORKLOADS[DTP_WORKLOAD]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
 
-    def up(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
     t_gen = time.perf_counter()
-    shards = [up(wl.shard(q)) for q in range(wl.tp)]
-    w_col = up(wl.w_col())
-    same_w = wl.K == wl.N and wl.K_row == wl.K and wl.H == wl.N
-    w_row = w_col if same_w else up(wl.w_row())
-    peers = [up(wl.partial(p)) for p in range(1, wl.P)]
-    residual = up(wl.residual())
-    gamma = up(wl.gamma())
-    x_res = residual.clone()
-    xg = torch.empty((wl.M, wl.K), dtype=torch.bfloat16, device=dev)
-    y_col = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
-    a_row = y_col if wl.N == wl.K_row else up(wl.a_row())
-    own = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
-    h = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
-    y_norm = torch.empty_like(h)
-    y_dtp = torch.empty_like(h)
+    L = LayerTensors(wl, torch, dev)
+    D = DtpTensors(wd, torch, dev)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
 
     ctx = sptl.Context(0)
     cs = torch.cuda.current_stream()
-    delta = wl.delta if wl.delta is not None else 1
-    dtp_peers = peers[:wl.tp - 1]
+    ev = TimingEvent
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -270,28 +309,35 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ev = TimingEvent
+    def agmm(T, w, y, timing=False, n_chunks=None, shards=None):
+        sptl.agmm_chunked(shards or T.shards, T.xg, w, y, n_chunks=n_chunks or T.n_chunks, rank=0, compute=cs,
+                          timing=timing, ctx=ctx)
 
-    def agmm(wt, yt, timing=False):
-        sptl.agmm_chunked(shards, xg, wt, yt, n_chunks=wl.n_chunks, rank=0, compute=cs, timing=timing, ctx=ctx)
+    L.n_chunks = wl.n_chunks
+
+    def gemm_p(T):
+        sptl.gemm_partial(T.a_row, T.w_row, T.own, stream=cs, ctx=ctx)
+
+    def reduce(T, eps):
+        sptl.reduce_residual_rmsnorm([T.own] + T.peers, T.residual, T.gamma, eps, T.y_norm, residual_out=T.h,
+                                     stream=cs, ctx=ctx)
+
+    def dtp_gemm():
+        sptl.gemm_partial(D.a, D.w, D.own, stream=cs, ctx=ctx)
+
+    def dtp():
+        sptl.dtp_accumulate(D.x, D.own, D.peers, D.gamma, wd.eps, D.y, tp=wd.tp, delta=D.delta,
+                            module_idx=D.delta, stream=cs, ctx=ctx)
+
+    calls = [lambda: agmm(L, L.w_col, L.y_col), lambda: gemm_p(L), lambda: reduce(L, wl.eps), dtp_gemm, dtp]
 
     def step(rec=None):
+        for i, fn in enumerate(calls):
+            if rec:
+                rec[i].record(cs)
+            fn()
         if rec:
-            rec[0].record(cs)
-        agmm(w_col, y_col)
-        if rec:
-            rec[1].record(cs)
-        sptl.gemm_partial(a_row, w_row, own, stream=cs, ctx=ctx)
-        if rec:
-            rec[2].record(cs)
-        sptl.reduce_residual_rmsnorm([own] + peers, residual, gamma, wl.eps, y_norm, residual_out=h,
-                                     stream=cs, ctx=ctx)
-        if rec:
-            rec[3].record(cs)
-        sptl.dtp_accumulate(x_res, own, dtp_peers, gamma, wl.eps, y_dtp, tp=wl.tp, delta=delta,
-                            module_idx=delta, stream=cs, ctx=ctx)
-        if rec:
-            rec[4].record(cs)
+            rec[len(calls)].record(cs)
 
     for _ in range(args.warmup):
         step()
@@ -299,7 +345,7 @@ def main():
     ctx.check()
 
     # ---- timed region: `steps` passes of the whole hot path ------------------------------
-    recs = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    recs = [[ev() for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     t_start.record(cs)
@@ -311,16 +357,9 @@ def main():
 
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    agmm_ms = np.array([r[0].elapsed_time(r[1]) for r in recs])
-    gemmp_ms = np.array([r[1].elapsed_time(r[2]) for r in recs])
-    red_ms = np.array([r[2].elapsed_time(r[3]) for r in recs])
-    dtp_ms = np.array([r[3].elapsed_time(r[4]) for r in recs])
+    per_call = [np.array([r[i].elapsed_time(r[i + 1]) for r in recs]) for i in range(len(calls))]
+    agmm_ms, gemmp_ms, red_ms, dgemm_ms, dtp_ms = per_call
 
-    M, K, N = wl.M, wl.K, wl.N
-    agmm_flops = 2.0 * M * K * N
-    agmm_tflops = agmm_flops / (agmm_ms.mean() * 1e-3) / 1e12
-
-    # ---- overlap accounting (outside the timed region) ------------------------------------
     def timed(fn, reps):
         fn()
         torch.cuda.synchronize()
@@ -331,43 +370,6 @@ def main():
         b.record(cs)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
-
-    reps = max(3, min(10, args.steps))
-    # the same GEMM on already-gathered rows (no staging)
-    y_tmp = torch.empty_like(y_col)
-    t_gemm = timed(lambda: sptl.gemm_partial(xg, w_col, y_tmp, stream=cs, ctx=ctx), reps)
-    # Staging alone: the same copies with an 8-column weight.  Its workgroups (one column
-    # tile per row tile) are all resident from the start, so the time the first of them sees
-    # a chunk's completion signal is when that chunk landed; the peers' last landing time,
-    # from the kernel's start, is the staging time.  (The call's own duration is not: each
-    # tile still walks the whole K.)
-    w_thin = torch.zeros((K, 8), dtype=torch.bfloat16, device=dev)
-    y_thin = torch.empty((M, 8), dtype=torch.bfloat16, device=dev)
-    # Each instrumented call is issued right behind an ordinary one, with no host wait in
-    # between: as in the timed steps, the staging worker is then already running when the
-    # call arrives (after a host wait it may be asleep, which delays the first copies by tens
-    # of microseconds).
-    copy_runs = []
-    for _ in range(reps):
-        agmm(w_thin, y_thin)
-        agmm(w_thin, y_thin, timing=True)
-        copy_runs.append(max(r[1] for r in ctx.timeline(wl.n_chunks)))
-    ctx.check()
-    t_copy = float(np.median(copy_runs))
-    t_agmm = float(agmm_ms.mean())
-    exposed = max(0.0, t_agmm - t_gemm)
-    hidden_cross = None if t_copy <= 0 else max(0.0, 1.0 - exposed / t_copy)
-    staged_bytes = (wl.tp - 1) * (M // wl.tp) * K * 2
-    # per-chunk timeline: the median, entry by entry, of `reps` instrumented calls (each right
-    # behind an ordinary call, as above)
-    tls = []
-    for _ in range(reps):
-        agmm(w_col, y_col)
-        agmm(w_col, y_col, timing=True)
-        tls.append(ctx.timeline(wl.n_chunks))
-    ctx.check()
-    tl = [tuple(float(np.median([t[c][j] for t in tls])) for j in range(4)) for c in range(wl.n_chunks)]
-    hidden_iv = interval_hidden_fraction(tl)
 
     # Epilogues with cold caches: a 1 GiB fill between calls evicts the 256 MB MALL, outside
     # the timed calls (the step above runs them right after the GEMMs, as the layer does).
@@ -385,24 +387,80 @@ def main():
             out.append(a.elapsed_time(b))
         return float(np.median(out))
 
-    red_cold_ms = cold(lambda: sptl.reduce_residual_rmsnorm([own] + peers, residual, gamma, wl.eps, y_norm,
-                                                            residual_out=h, stream=cs, ctx=ctx), reps)
-    dtp_cold_ms = cold(lambda: sptl.dtp_accumulate(x_res, own, dtp_peers, gamma, wl.eps, y_dtp, tp=wl.tp, delta=delta,
-                                                   module_idx=delta, stream=cs, ctx=ctx), reps)
-    del flush
+    def overlap(T, w, reps, t_agmm, n_chunks):
+        """Pre-staged GEMM time, staging alone, the per-chunk timeline and the hidden fractions."""
+        M, K, N = T.xg.shape[0], T.xg.shape[1], w.shape[1]
+        tp = len(T.shards)
+        # the same GEMM on already-gathered rows (no staging)
+        y_tmp = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t_gemm = timed(lambda: sptl.gemm_partial(T.xg, w, y_tmp, stream=cs, ctx=ctx), reps)
+        del y_tmp
+        # Staging alone: the same copies with an 8-column weight.  Its workgroups (one column
+        # tile per row tile) are all resident from the start, so the time the first of them
+        # sees a chunk's completion signals is when that chunk landed; the peers' last landing
+        # time, from the kernel's start, is the staging time.  Each instrumented call is issued
+        # right behind an ordinary one, with no host wait in between: as in the timed steps,
+        # the staging worker is then already running when the call arrives.
+        w_thin = torch.zeros((K, 8), dtype=torch.bfloat16, device=dev)
+        y_thin = torch.empty((M, 8), dtype=torch.bfloat16, device=dev)
+        copy_runs = []
+        for _ in range(reps):
+            agmm(T, w_thin, y_thin, n_chunks=n_chunks)
+            agmm(T, w_thin, y_thin, timing=True, n_chunks=n_chunks)
+            copy_runs.append(max(r[1] for r in ctx.timeline(n_chunks)))
+        ctx.check()
+        t_copy = float(np.median(copy_runs))
+        exposed = max(0.0, t_agmm - t_gemm)
+        staged_bytes = (tp - 1) * (M // tp) * K * 2
+        tls = []
+        for _ in range(reps):
+            agmm(T, w, T.y_col, n_chunks=n_chunks)
+            agmm(T, w, T.y_col, timing=True, n_chunks=n_chunks)
+            tls.append(ctx.timeline(n_chunks))
+        ctx.check()
+        tl = [tuple(float(np.median([t[c][j] for t in tls])) for j in range(4)) for c in range(n_chunks)]
+        covered = interval_hidden_fraction(tl)
+        flops = 2.0 * M * K * N
+        return {
+            "gemm_prestaged_ms": round(t_gemm, 4),
+            "gemm_prestaged_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 2),
+            "gemm_prestaged_frac_peak": round(flops / (t_gemm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "copy_alone_ms": round(t_copy, 4),
+            "copy_alone_GBps": round(staged_bytes / (t_copy * 1e-3) / 1e9, 1),
+            "copy_exposed_ms": round(exposed, 4),
+            # 1 - (T_agmm - T_gemm_prestaged) / T_copy_alone: the share of the staging time
+            # that does not lengthen the call
+            "copy_hidden_frac": None if t_copy <= 0 else round(max(0.0, 1.0 - exposed / t_copy), 4),
+            # share of the staging time during which some chunk GEMM tile was running
+            "copy_interval_covered_frac": None if covered is None else round(covered, 4),
+            "chunk_ready_ms": [round(r[1], 4) for r in tl],
+            "chunk_gemm_ms": [[round(r[2], 4), round(r[3], 4)] for r in tl],
+        }
+
+    reps = max(3, min(10, args.steps))
+    M, K, N = wl.M, wl.K, wl.N
+    agmm_flops = 2.0 * M * K * N
+    t_agmm = float(agmm_ms.mean())
+    agmm_tflops = agmm_flops / (t_agmm * 1e-3) / 1e12
+    ov = overlap(L, L.w_col, reps, t_agmm, wl.n_chunks)
+
+    red_bytes = epilogue_bytes(wl.P + 1, M, wl.H)
+    dtp_bytes = epilogue_bytes(1 + 1 + (wd.tp - 1), wd.M, wd.H)
+    red_cold_ms = cold(lambda: reduce(L, wl.eps), reps)
+    dtp_cold_ms = cold(dtp, reps)
 
     # Staging check: with x_gathered poisoned (bf16 NaN everywhere, outside the timed region),
     # one more call must land every chunk before its tiles read it, so y comes out bit for bit
     # as in the timed region and no NaN is left in x_gathered.
-    y_ref = y_col.clone()
-    xg.fill_(float("nan"))
+    y_ref = L.y_col.clone()
+    L.xg.fill_(float("nan"))
     torch.cuda.synchronize()
-    agmm(w_col, y_col)
+    agmm(L, L.w_col, L.y_col)
     torch.cuda.synchronize()
     ctx.check()
     staging_check = {"x_gathered_poisoned_with": "NaN",
-                     "y_bitwise_equal": bool(torch.equal(y_col.view(torch.int16), y_ref.view(torch.int16))),
-                     "x_gathered_nan_free": not bool(torch.isnan(xg).any())}
+                     "y_bitwise_equal": bool(torch.equal(L.y_col.view(torch.int16), y_ref.view(torch.int16))),
+                     "x_gathered_nan_free": not bool(torch.isnan(L.xg).any())}
     del y_ref
 
     # Sub-layer boundary: the epilogue of the own M/tp rows writes its normalised rows straight
@@ -412,17 +470,17 @@ def main():
     boundary = None
     if wl.H == wl.K:
         R = M // wl.tp
-        parts_r = [t[:R] for t in [own] + peers]
+        parts_r = [t[:R] for t in [L.own] + L.peers]
         y_own = torch.empty((R, wl.H), dtype=torch.bfloat16, device=dev)
         h_own = torch.empty_like(y_own)
-        y_alias = torch.empty_like(y_col)
+        y_alias = torch.empty_like(L.y_col)
 
         def chain(alias):
-            dst = xg[:R] if alias else y_own
-            sptl.reduce_residual_rmsnorm(parts_r, residual[:R], gamma, wl.eps, dst, residual_out=h_own,
+            dst = L.xg[:R] if alias else y_own
+            sptl.reduce_residual_rmsnorm(parts_r, L.residual[:R], L.gamma, wl.eps, dst, residual_out=h_own,
                                          stream=cs, ctx=ctx)
-            src = [dst] + shards[1:]
-            sptl.agmm_chunked(src, xg, w_col, y_alias if alias else y_col, n_chunks=wl.n_chunks, rank=0,
+            src = [dst] + L.shards[1:]
+            sptl.agmm_chunked(src, L.xg, L.w_col, y_alias if alias else L.y_col, n_chunks=wl.n_chunks, rank=0,
                               compute=cs, ctx=ctx)
 
         pair_ms = {False: [], True: []}
@@ -436,20 +494,20 @@ def main():
                 torch.cuda.synchronize()
                 pair_ms[alias].append(a.elapsed_time(b))
         ctx.check()
-        same = bool(torch.equal(y_col.view(torch.int16), y_alias.view(torch.int16))
-                    and torch.equal(xg[:R].view(torch.int16), y_own.view(torch.int16)))
+        same = bool(torch.equal(L.y_col.view(torch.int16), y_alias.view(torch.int16))
+                    and torch.equal(L.xg[:R].view(torch.int16), y_own.view(torch.int16)))
         boundary = {"rows": R, "ms_own_slot_copied": round(float(np.median(pair_ms[False])), 4),
                     "ms_own_slot_in_place": round(float(np.median(pair_ms[True])), 4),
                     "bitwise_equal": same}
         del y_own, h_own, y_alias
 
-    P = wl.P
-    red_bytes = (P + 1) * M * wl.H * 2 + 2 * M * wl.H * 2 + wl.H * 2
-    dtp_bytes = (1 + 1 + (wl.tp - 1)) * M * wl.H * 2 + 2 * M * wl.H * 2 + wl.H * 2
-    red_gbs = red_bytes / (red_ms.mean() * 1e-3) / 1e9
-    dtp_gbs = dtp_bytes / (dtp_ms.mean() * 1e-3) / 1e9
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
     gemmp_flops = 2.0 * M * wl.K_row * wl.H
     gemmp_tflops = gemmp_flops / (gemmp_ms.mean() * 1e-3) / 1e12
+    dgemm_flops = 2.0 * wd.M * wd.K_row * wd.H
+    dgemm_tflops = dgemm_flops / (dgemm_ms.mean() * 1e-3) / 1e12
 
     out = {
         "metric": "AG-GEMM TFLOP/s & %MFMA peak; reduce+RMSNorm GB/s & %HBM; % copy hidden",
@@ -467,7 +525,9 @@ def main():
         "config": {
             "workload": wl.name,
             "seq_len": M, "hidden": K, "n_local": N, "k_row": wl.K_row, "tp": wl.tp,
-            "n_chunks": wl.n_chunks, "rank": 0, "partials": P, "dtp_delta": delta,
+            "n_chunks": wl.n_chunks, "rank": 0, "partials": wl.P,
+            "dtp_workload": wd.name, "dtp_tokens": wd.M, "dtp_hidden": wd.H, "dtp_tp": wd.tp,
+            "dtp_delta": wd.delta,
             "parallelism": "one GPU's share of SP-TP (peer chunks staged from local HBM)",
         },
         "roofline": {
@@ -484,35 +544,79 @@ def main():
         "agmm": {
             "tflops": round(agmm_tflops, 2), "frac_peak": round(agmm_tflops / PEAK_BF16_TFLOPS, 4),
             "ms": round(t_agmm, 4),
-            "gemm_prestaged_ms": round(t_gemm, 4),
-            "gemm_prestaged_tflops": round(agmm_flops / (t_gemm * 1e-3) / 1e12, 2),
             "ms_median": round(float(np.median(agmm_ms)), 4), "ms_min": round(float(agmm_ms.min()), 4),
-            "copy_alone_ms": round(t_copy, 4),
-            "copy_alone_GBps": round(staged_bytes / (t_copy * 1e-3) / 1e9, 1),
-            "copy_exposed_ms": round(exposed, 4),
-            "copy_hidden_frac": None if hidden_iv is None else round(hidden_iv, 4),
-            "copy_hidden_frac_crosscheck": None if hidden_cross is None else round(hidden_cross, 4),
-            "chunk_ready_ms": [round(r[1], 4) for r in tl],
-            "chunk_gemm_ms": [[round(r[2], 4), round(r[3], 4)] for r in tl],
+            **ov,
             "staging_check": staging_check,
             "boundary": boundary,
         },
         "gemm_partial": {"tflops": round(gemmp_tflops, 2), "frac_peak": round(gemmp_tflops / PEAK_BF16_TFLOPS, 4),
                          "ms": round(float(gemmp_ms.mean()), 4), "ms_median": round(float(np.median(gemmp_ms)), 4)},
-        "reduce_residual_rmsnorm": {"GBps": round(red_gbs, 1), "frac_hbm": round(red_gbs / PEAK_HBM_GBS, 4),
-                                    "ms": round(float(red_ms.mean()), 4), "ms_median": round(float(np.median(red_ms)), 4),
-                                    "GBps_cold": round(red_bytes / (red_cold_ms * 1e-3) / 1e9, 1),
-                                    "frac_hbm_cold": round(red_bytes / (red_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                                    "bytes": red_bytes},
-        "dtp_accumulate": {"GBps": round(dtp_gbs, 1), "frac_hbm": round(dtp_gbs / PEAK_HBM_GBS, 4),
-                           "ms": round(float(dtp_ms.mean()), 4), "ms_median": round(float(np.median(dtp_ms)), 4),
-                           "GBps_cold": round(dtp_bytes / (dtp_cold_ms * 1e-3) / 1e9, 1),
-                           "frac_hbm_cold": round(dtp_bytes / (dtp_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                           "bytes": dtp_bytes},
+        "reduce_residual_rmsnorm": {
+            "GBps": round(gbs(red_bytes, red_ms.mean()), 1), "frac_hbm": round(gbs(red_bytes, red_ms.mean()) / PEAK_HBM_GBS, 4),
+            "ms": round(float(red_ms.mean()), 4), "ms_median": round(float(np.median(red_ms)), 4),
+            "GBps_cold": round(gbs(red_bytes, red_cold_ms), 1),
+            "frac_hbm_cold": round(gbs(red_bytes, red_cold_ms) / PEAK_HBM_GBS, 4),
+            "bytes": red_bytes},
+        "dtp_gemm_partial": {"workload": wd.name, "shape": [wd.M, wd.K_row, wd.H],
+                             "tflops": round(dgemm_tflops, 2), "frac_peak": round(dgemm_tflops / PEAK_BF16_TFLOPS, 4),
+                             "ms": round(float(dgemm_ms.mean()), 4)},
+        "dtp_accumulate": {
+            "workload": wd.name,
+            "GBps": round(gbs(dtp_bytes, dtp_ms.mean()), 1), "frac_hbm": round(gbs(dtp_bytes, dtp_ms.mean()) / PEAK_HBM_GBS, 4),
+            "ms": round(float(dtp_ms.mean()), 4), "ms_median": round(float(np.median(dtp_ms)), 4),
+            "GBps_cold": round(gbs(dtp_bytes, dtp_cold_ms), 1),
+            "frac_hbm_cold": round(gbs(dtp_bytes, dtp_cold_ms) / PEAK_HBM_GBS, 4),
+            "bytes": dtp_bytes},
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", ""), "max_sclk_mhz": max_sclk_mhz(0)},
         "input_gen_s": round(t_gen, 2),
     }
+
+    # ---- other workloads, after the timed region: the same calls, fewer steps ---------------
+    del L, D
+    torch.cuda.empty_cache()
+    others = {}
+    for name in [n for n in args.others.split(",") if n and n != wl.name]:
+        wo = synth.WORKLOADS[name]
+        T = LayerTensors(wo, torch, dev)
+        T.n_chunks = wo.n_chunks
+        fns = [lambda: agmm(T, T.w_col, T.y_col), lambda: gemm_p(T), lambda: reduce(T, wo.eps)]
+        for _ in range(max(10, args.warmup // 2)):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        n_o = max(10, args.steps // 2)
+        rr = [[ev() for _ in range(len(fns) + 1)] for _ in range(n_o)]
+        for r in rr:
+            for i, fn in enumerate(fns):
+                r[i].record(cs)
+                fn()
+            r[len(fns)].record(cs)
+        torch.cuda.synchronize()
+        ctx.check()
+        ms = [float(np.mean([r[i].elapsed_time(r[i + 1]) for r in rr])) for i in range(len(fns))]
+        fl = 2.0 * wo.M * wo.K * wo.N
+        gfl = 2.0 * wo.M * wo.K_row * wo.H
+        rb = epilogue_bytes(wo.P + 1, wo.M, wo.H)
+        ovo = overlap(T, T.w_col, reps, ms[0], wo.n_chunks)
+        rc = cold(lambda: reduce(T, wo.eps), reps)
+        others[name] = {
+            "agmm_tflops": round(fl / (ms[0] * 1e-3) / 1e12, 2),
+            "agmm_frac_peak": round(fl / (ms[0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "agmm_ms": round(ms[0], 4),
+            **{k: ovo[k] for k in ("gemm_prestaged_tflops", "gemm_prestaged_frac_peak", "copy_alone_ms",
+                                   "copy_alone_GBps", "copy_hidden_frac", "copy_interval_covered_frac")},
+            "gemm_partial_tflops": round(gfl / (ms[1] * 1e-3) / 1e12, 2),
+            "gemm_partial_frac_peak": round(gfl / (ms[1] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "reduce_GBps": round(gbs(rb, ms[2]), 1), "reduce_frac_hbm": round(gbs(rb, ms[2]) / PEAK_HBM_GBS, 4),
+            "reduce_GBps_cold": round(gbs(rb, rc), 1), "reduce_frac_hbm_cold": round(gbs(rb, rc) / PEAK_HBM_GBS, 4),
+        }
+        del T, fns
+        torch.cuda.empty_cache()
+    if others:
+        out["other_workloads"] = others
+    del flush
+
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     ctx.close()

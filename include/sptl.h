@@ -66,8 +66,8 @@ typedef enum {
 } sptl_status;
 
 /* Limits. */
-#define SPTL_MAX_PARTIALS 16   /* partial sums per reduce call (tp)                      */
-#define SPTL_MAX_TP 64         /* TP degree of agmm_chunked and dtp_accumulate           */
+#define SPTL_MAX_PARTIALS 16   /* partials per reduce call; also bounds dtp_accumulate's tp */
+#define SPTL_MAX_TP 64         /* TP degree of agmm_chunked                              */
 #define SPTL_MAX_CHUNKS 512    /* chunk count of agmm_chunked                            */
 #define SPTL_MAX_K 2097152     /* GEMM reduction size (hidden of agmm_chunked, k_local)  */
 #define SPTL_MAX_N 8388608     /* GEMM output width (n_local, hidden of gemm_partial)    */
@@ -91,12 +91,22 @@ const char *sptl_last_error(void);
 /* ABI version (major * 100 + minor). */
 int sptl_version(void);
 
-/* Waits (bounded, 30 s per call) until every staged agmm_chunked call made on ctx has
- * completed on the GPU, then reports asynchronous failures recorded since the last check:
- * SPTL_E_ASYNC if a staging wait timed out (the affected call's y is invalid; a chunk wait
- * gives up after 10 s) or a staging copy could not be submitted (the staged path is then
- * disabled for ctx); SPTL_OK otherwise.  Clears the recorded state. */
+/* Waits (bounded, 30 s per wait) until every staged agmm_chunked call made on ctx has
+ * completed on the GPU, including the copies of a call whose chunk wait timed out (those may
+ * still write that call's x_gathered after its kernel has ended; once this returns they have
+ * landed), then reports asynchronous failures recorded since the last check: SPTL_E_ASYNC if
+ * a staging wait timed out (the affected call's y is invalid; a chunk wait gives up after
+ * 10 s unless sptl_ctx_set_wait_timeout_us says otherwise), a staging copy could not be
+ * submitted (the staged path is then disabled for ctx) or the copies of a timed-out call did
+ * not complete within the bound; SPTL_OK otherwise.  Clears the recorded state. */
 int sptl_ctx_check(sptl_ctx *ctx);
+
+/* Sets the bound on one chunk wait inside the staged GEMM of later agmm_chunked calls on ctx,
+ * in microseconds: 1..10000000, or 0 for the default (10 s).  A wait that runs out lets its
+ * workgroups go on with whatever the chunk's rows hold; the call is then reported by
+ * sptl_ctx_check (SPTL_E_ASYNC).  Meant for failure-path tests and for callers that prefer an
+ * early error over a long stall.  SPTL_E_NULL for a NULL ctx, SPTL_E_RANGE otherwise. */
+int sptl_ctx_set_wait_timeout_us(sptl_ctx *ctx, int64_t us);
 
 /* Short text naming how agmm_chunked stages chunks on ctx with copy == NULL (copy engines
  * driven directly with a chunk-ordered GEMM, or one copy and one GEMM launch per chunk) and,
@@ -154,8 +164,14 @@ const char *sptl_ctx_info(sptl_ctx *ctx);
  *     workgroup per tile, except with 256-row tiles at hidden < 2048: then one workgroup per
  *     compute unit, each taking its tiles in that order.
  *     The launch ends only after every copy of the call (own slot included) has landed.
+ *   - The waiting tiles depend on the context's worker thread: the copies start only once it
+ *     has seen the fork event and submitted them.  A worker kept off the CPU for longer than
+ *     the wait bound (sptl_ctx_set_wait_timeout_us) makes the waits time out; the call's
+ *     results are then invalid and sptl_ctx_check reports SPTL_E_ASYNC.  Until then the
+ *     waiting workgroups hold their compute units.
  *   - Up to 4 staged calls per context may be in flight; a fifth blocks the calling thread
- *     until the oldest has finished on the GPU.
+ *     until the oldest has finished on the GPU (and, if a wait of that call timed out, until
+ *     its copies have landed; SPTL_E_ASYNC if they do not within 30 s).
  * Per-chunk path (copy != NULL): for each peer chunk, one SDMA-class hipMemcpyAsync on
  * `copy` (forked from `compute`) and an event; then one GEMM launch per chunk on `compute`
  * after that chunk's event, own chunks first; `compute` joins `copy` at the end.

@@ -28,7 +28,7 @@ struct sptl_ctx {
     uint64_t *flags_dev = nullptr;      // landed flags, kFlagSetWords per stager set
     int wallclock_khz = 100000;
     int64_t cus = 256;                  // compute units of the device
-    uint64_t wait_timeout_us = 10000000;  // bound on one chunk wait inside the GEMM (10 s)
+    uint64_t wait_timeout_us = 10000000;  // bound on one chunk wait inside the GEMM (default 10 s)
     int t_mode = 0;                     // 0: event timeline, 1: chunk-ordered timeline
     int t_rank_first = 0, t_rank_count = 0;
     int t_set = -1;                     // stager set and epoch of the last timed chunk-ordered call
@@ -46,6 +46,7 @@ struct sptl_ctx {
 
 namespace {
 
+constexpr uint64_t kDefaultWaitUs = 10000000;  // default bound on one chunk wait (10 s)
 thread_local std::string g_err;
 
 int fail(int code, const char *fmt, ...) {
@@ -279,8 +280,8 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
 
     sptl::StageCall call;
     std::string why;
-    if (sptl::stager_begin(ctx->stager, pieces, wgs, &call, &why))
-        return fail(SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
+    if (int rc = sptl::stager_begin(ctx->stager, pieces, wgs, &call, &why))
+        return fail(rc == -2 ? SPTL_E_ASYNC : SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
     for (int c = 0; c < n; ++c) {
         plan.ready[c] = call.ready[c];
         plan.ready_n[c] = call.ready_n[c];
@@ -291,6 +292,7 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     plan.flags = ctx->flags_dev + (size_t)call.set * sptl::kFlagSetWords;
     plan.epoch = call.epoch;
     plan.finished = call.finished;
+    plan.timedout = call.timedout;
     plan.wg_count = call.wg_count;
     for (int g = 0; g < sptl::kEndGroups; ++g) plan.grp_last[g] = call.grp_last[g];
     plan.all_last = call.all_last;
@@ -335,8 +337,11 @@ int sptl_ctx_check(sptl_ctx *ctx) {
     if (int rc = resolve_ctx(ctx)) return rc;
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
-    if (ctx->stager && sptl::stager_wait_idle(ctx->stager))
-        return fail(SPTL_E_HIP, "sptl_ctx_check: waiting for staged calls failed");
+    if (ctx->stager)
+        if (int rc = sptl::stager_wait_idle(ctx->stager))
+            return fail(rc == -2 ? SPTL_E_ASYNC : SPTL_E_HIP,
+                        rc == -2 ? "sptl_ctx_check: the copies of a timed-out call did not complete"
+                                 : "sptl_ctx_check: waiting for staged calls failed");
     int flag = 0;
     SPTL_HIP(hipMemcpy(&flag, ctx->err_dev, sizeof flag, hipMemcpyDeviceToHost));
     if (flag) {
@@ -349,6 +354,14 @@ int sptl_ctx_check(sptl_ctx *ctx) {
 }
 
 const char *sptl_last_error(void) { return g_err.c_str(); }
+
+int sptl_ctx_set_wait_timeout_us(sptl_ctx *ctx, int64_t us) {
+    if (!ctx) return fail(SPTL_E_NULL, "sptl_ctx_set_wait_timeout_us: ctx is NULL");
+    if (us < 0 || us > 10000000)
+        return fail(SPTL_E_RANGE, "sptl_ctx_set_wait_timeout_us: us=%lld not in [0, 10000000]", (long long)us);
+    ctx->wait_timeout_us = us ? (uint64_t)us : kDefaultWaitUs;
+    return SPTL_OK;
+}
 
 int sptl_create(sptl_ctx **out, int device) {
     if (!out) return fail(SPTL_E_NULL, "out is NULL");

@@ -77,9 +77,15 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 // *plan.err and returns, so every wave exits.  The polls are relaxed (coherent loads that bypass
 // the caches, no cache invalidation); one acquire fence follows the last poll, so a waiting
 // workgroup does not invalidate its L2 while others stream through it.
+// A timed-out wait also records the launch's epoch in plan.timedout: the copies it gave up on
+// may still be in flight after the launch ends, and the stager drains them before it re-arms
+// their signals.  The fence completes that store before this workgroup counts itself done,
+// so the host sees it no later than the launch's end word.
 __device__ __forceinline__ bool timed_out(uint64_t t0, const ChunkPlan &plan) {
     if (wall_clock64() - t0 <= plan.timeout_ticks) return false;
     __hip_atomic_store(plan.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (plan.timedout) __hip_atomic_store(plan.timedout, plan.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __atomic_thread_fence(__ATOMIC_RELEASE);
     return true;
 }
 

@@ -44,6 +44,7 @@ struct ChunkPlan {
     uint64_t *flags;                         // landed flags (kFlagSetWords words), or nullptr
     uint64_t epoch;                          // value a landed flag holds for this launch
     uint64_t *finished;                      // pinned host word: epoch once the launch is done
+    uint64_t *timedout;                      // pinned host word: epoch if a wait of the launch timed out
     uint64_t *wg_count;                      // end counters of the signal set (kEndCounters lines)
     uint64_t grp_last[kEndGroups];           // group counter value seen by a group's last workgroup
     uint64_t all_last;                       // final counter value seen by the last group

@@ -17,8 +17,11 @@
 // kernel store raises no interrupt.)
 //
 // Reuse: completion-signal sets form a ring; a set is re-armed only after the kernel that
-// waited on it has reported its end through a pinned host word (by then all of the set's
-// pieces have landed).  No marker follows the kernel on the stream.
+// waited on it has reported its end through a pinned host word.  By then every piece of the
+// set has landed, unless a wait of that kernel timed out: the kernel then records the call's
+// epoch in a second pinned word, and the set is drained first (the worker has handled the
+// call's job and every armed signal has reached zero), because a late copy would otherwise
+// complete a re-armed signal of the next call.  No marker follows the kernel on the stream.
 #include "sptl_stager.h"
 
 #include <hsa/hsa.h>
@@ -76,12 +79,15 @@ struct SignalSet {
     int64_t **words = nullptr;  // device: value word of sig[c][p] at words[c * kMaxPieces + p]
     hipEvent_t fork = nullptr;
     uint64_t epoch = 0;       // of the last call begun on the set (0: never used)
+    int armed[kMaxPlanChunks + 1] = {};   // pieces per chunk armed by that call
+    std::atomic<uint64_t> handled{0};     // epoch of the last job the worker has handled
     uint64_t grp_total[kEndGroups] = {};  // workgroups counted per group, all calls on the set
     uint64_t all_total = 0;               // groups counted, all calls on the set
 };
 
 struct Job {
     int set;
+    uint64_t epoch;
     hipEvent_t fork;
     std::vector<CopyPiece> pieces;
 };
@@ -121,6 +127,36 @@ class SdmaStager {
     uint64_t *counts = nullptr;     // device, kCountWords
 
     volatile uint64_t *finished(int set) const { return host_words + 16 * set; }
+    volatile uint64_t *timedout(int set) const { return host_words + 16 * set + 8; }
+
+    // Whether the last call begun on `set` may have left copies in flight: a wait of its
+    // kernel timed out, or a submission failed (the failure path released its waiters).
+    // Only meaningful once that kernel has reported its end.
+    bool tainted(int set) const {
+        const uint64_t e = sets[set].epoch;
+        return e && (__atomic_load_n(timedout(set), __ATOMIC_ACQUIRE) == e || failed.load());
+    }
+
+    // Bounded wait until every copy of the last call on `set` is done: the worker has handled
+    // its job (submitted every piece or given up) and every armed piece signal reads <= 0.
+    bool drain(int set, double seconds) {
+        SignalSet &ss = sets[set];
+        const auto t0 = std::chrono::steady_clock::now();
+        auto expired = [&] {
+            return std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count() > seconds;
+        };
+        while (ss.handled.load(std::memory_order_acquire) < ss.epoch) {
+            if (expired()) return false;
+            std::this_thread::yield();
+        }
+        for (int c = 0; c <= kMaxPlanChunks; ++c)
+            for (int q = 0; q < ss.armed[c]; ++q)
+                for (unsigned i = 1; hsa_signal_load_scacquire(ss.sig[c][q]) > 0; ++i) {
+                    __builtin_ia32_pause();
+                    if ((i & 1023) == 0 && expired()) return false;
+                }
+        return true;
+    }
 
     // The copies should start the moment the fork completes: a blocking event wait wakes
     // up tens of microseconds late, which delays every chunk by as much.  So the worker
@@ -162,34 +198,40 @@ class SdmaStager {
                 queue.pop_front();
                 queued.fetch_sub(1, std::memory_order_relaxed);
             }
-            SignalSet &ss = sets[job.set];
-            static const bool trace = getenv("SPTL_STAGER_TRACE") != nullptr;
-            const auto tq = std::chrono::steady_clock::now();
-            bool ok = wait_fork(job.fork);
-            const auto tf = std::chrono::steady_clock::now();
-            int last_chunk = -2;
-            for (const CopyPiece &pc : job.pieces) {
-                if (trace && pc.chunk != last_chunk) {
-                    fprintf(stderr, "[stager] chunk %d submit at +%.1f us after fork (fork wait %.1f us)\n", pc.chunk,
-                            std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - tf).count(),
-                            std::chrono::duration<double, std::micro>(tf - tq).count());
-                    last_chunk = pc.chunk;
-                }
-                const uint32_t eng = engines[(size_t)pc.engine % engines.size()];
-                if (ok)
-                    ok = hsa_amd_memory_async_copy_on_engine(pc.dst, agent, pc.src, agent, pc.bytes, 0, nullptr,
-                                                             ss.sig[pc.chunk][pc.piece],
-                                                             (hsa_amd_sdma_engine_id_t)eng, true) == HSA_STATUS_SUCCESS;
-                if (!ok) {
-                    // release every waiter of this call; the call's results are invalid and
-                    // the failure is reported through stager_failed
-                    failed = true;
-                    for (int c = 0; c <= kMaxPlanChunks; ++c)
-                        for (int q = 0; q < kMaxPieces; ++q) hsa_signal_store_screlease(ss.sig[c][q], 0);
-                    break;
-                }
+            submit(job);
+        }
+    }
+
+    // Submits a job's pieces once its fork event has completed, then records the job handled.
+    void submit(const Job &job) {
+        SignalSet &ss = sets[job.set];
+        static const bool trace = getenv("SPTL_STAGER_TRACE") != nullptr;
+        const auto tq = std::chrono::steady_clock::now();
+        bool ok = wait_fork(job.fork);
+        const auto tf = std::chrono::steady_clock::now();
+        int last_chunk = -2;
+        for (const CopyPiece &pc : job.pieces) {
+            if (trace && pc.chunk != last_chunk) {
+                fprintf(stderr, "[stager] chunk %d submit at +%.1f us after fork (fork wait %.1f us)\n", pc.chunk,
+                        std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - tf).count(),
+                        std::chrono::duration<double, std::micro>(tf - tq).count());
+                last_chunk = pc.chunk;
+            }
+            const uint32_t eng = engines[(size_t)pc.engine % engines.size()];
+            if (ok)
+                ok = hsa_amd_memory_async_copy_on_engine(pc.dst, agent, pc.src, agent, pc.bytes, 0, nullptr,
+                                                         ss.sig[pc.chunk][pc.piece],
+                                                         (hsa_amd_sdma_engine_id_t)eng, true) == HSA_STATUS_SUCCESS;
+            if (!ok) {
+                // release every waiter of this call; the call's results are invalid and the
+                // failure is reported through stager_failed
+                failed = true;
+                for (int c = 0; c <= kMaxPlanChunks; ++c)
+                    for (int q = 0; q < kMaxPieces; ++q) hsa_signal_store_screlease(ss.sig[c][q], 0);
+                break;
             }
         }
+        ss.handled.store(job.epoch, std::memory_order_release);
     }
 };
 
@@ -348,21 +390,31 @@ void stager_destroy(SdmaStager *s) {
         s->stop_flag.store(true);
     }
     s->cv.notify_all();
-    if (s->worker.joinable()) s->worker.join();
+    if (s->worker.joinable()) s->worker.join();  // the worker submits every queued job first
+    // A kernel that has not reported its end may still use the counters, tables and host words,
+    // and copies still in flight still complete their signals: whatever may still be in use is
+    // leaked rather than freed.
+    bool kernels_done = true;
     for (int set = 0; set < kSets; ++set) {
         SignalSet &ss = s->sets[set];
-        if (ss.epoch && s->host_words) (void)spin_until(s->finished(set), ss.epoch, kReuseWaitSeconds);
+        if (ss.epoch && s->host_words && !spin_until(s->finished(set), ss.epoch, kReuseWaitSeconds)) {
+            kernels_done = false;
+            continue;
+        }
+        if (ss.epoch && s->host_words && s->tainted(set) && !s->drain(set, kReuseWaitSeconds)) continue;
         for (int c = 0; c <= kMaxPlanChunks; ++c)
             for (int q = 0; q < kMaxPieces; ++q)
                 if (ss.sig[c][q].handle) hsa_signal_destroy(ss.sig[c][q]);
         if (ss.words) (void)hipFree(ss.words);
         if (ss.fork) (void)hipEventDestroy(ss.fork);
     }
-    if (s->scratch) (void)hipFree(s->scratch);
-    if (s->counts) (void)hipFree(s->counts);
-    if (s->host_words) (void)hipHostFree(s->host_words);
-    delete s;
-    hsa_shut_down();
+    if (kernels_done) {
+        if (s->scratch) (void)hipFree(s->scratch);
+        if (s->counts) (void)hipFree(s->counts);
+        if (s->host_words) (void)hipHostFree(s->host_words);
+        delete s;
+        hsa_shut_down();
+    }
 }
 
 int stager_engine_count(const SdmaStager *s) { return s ? (int)s->engines.size() : 0; }
@@ -375,8 +427,11 @@ int stager_wait_call(SdmaStager *s, int set, uint64_t epoch) {
 }
 
 int stager_wait_idle(SdmaStager *s) {
-    for (int set = 0; set < kSets; ++set)
-        if (s->sets[set].epoch && !spin_until(s->finished(set), s->sets[set].epoch, kReuseWaitSeconds)) return -1;
+    for (int set = 0; set < kSets; ++set) {
+        if (!s->sets[set].epoch) continue;
+        if (!spin_until(s->finished(set), s->sets[set].epoch, kReuseWaitSeconds)) return -1;
+        if (s->tainted(set) && !s->drain(set, kReuseWaitSeconds)) return -2;
+    }
     return 0;
 }
 
@@ -434,8 +489,16 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
         *err = "an earlier staged call did not finish";
         return -1;
     }
-    for (int c = 0; c <= kMaxPlanChunks; ++c)
+    // After a timed-out wait the set's copies may still be in flight (or not yet submitted):
+    // a late one would complete a signal re-armed for this call.
+    if (s->tainted(set) && !s->drain(set, kReuseWaitSeconds)) {
+        *err = "the copies of an earlier timed-out call did not complete";
+        return -2;
+    }
+    for (int c = 0; c <= kMaxPlanChunks; ++c) {
         for (int q = 0; q < count[c]; ++q) hsa_signal_store_screlease(ss.sig[c][q], 1);
+        ss.armed[c] = count[c];
+    }
     out->set = set;
     for (int c = 0; c < kMaxPlanChunks; ++c) {
         out->ready[c] = count[c] ? ss.words + (size_t)c * kMaxPieces : nullptr;
@@ -446,6 +509,7 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
     out->epoch = ++ss.epoch;
     out->fork = ss.fork;
     out->finished = const_cast<uint64_t *>(s->finished(set));
+    out->timedout = const_cast<uint64_t *>(s->timedout(set));
     out->wg_count = s->counts + (size_t)kSetCountWords * set;
     int groups = 0;
     for (int g = 0; g < kEndGroups; ++g) {
@@ -465,7 +529,7 @@ int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> p
     (void)err;
     {
         std::lock_guard<std::mutex> lk(s->mu);
-        s->queue.push_back(Job{call.set, call.fork, std::move(pieces)});
+        s->queue.push_back(Job{call.set, call.epoch, call.fork, std::move(pieces)});
         s->queued.fetch_add(1, std::memory_order_release);
     }
     s->cv.notify_one();
@@ -473,10 +537,13 @@ int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> p
 }
 
 void stager_cancel(SdmaStager *s, const StageCall &call) {
-    // nothing ran on the set: mark the call finished and take back its workgroup count
+    // nothing ran on the set: mark the call finished and handled (no job was queued) and take
+    // back its workgroup count
     SignalSet &ss = s->sets[call.set];
     for (int g = 0; g < kEndGroups; ++g) ss.grp_total[g] = call.grp_first[g];
     ss.all_total = call.all_first;
+    for (int c = 0; c <= kMaxPlanChunks; ++c) ss.armed[c] = 0;
+    ss.handled.store(call.epoch, std::memory_order_release);
     __atomic_store_n(s->host_words + 16 * call.set, call.epoch, __ATOMIC_RELEASE);
 }
 

@@ -48,6 +48,7 @@ struct StageCall {
     hipEvent_t fork = nullptr;
     uint64_t epoch = 0;
     uint64_t *finished = nullptr;
+    uint64_t *timedout = nullptr;   // pinned host word: the kernel stores epoch here if a wait timed out
     uint64_t *wg_count = nullptr;
     uint64_t grp_last[kEndGroups] = {};
     uint64_t all_last = 0;
@@ -69,7 +70,9 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
 
 // Reserves a completion-signal set for one call whose consuming kernel has `workgroups`
 // workgroups, and arms it with the number of pieces per chunk.  Blocks (bounded) while the
-// set's previous call is still running.
+// set's previous call is still running and, if a wait of that call timed out, until its copies
+// have completed.  Returns 0, -1 (the previous call did not finish; bad pieces) or -2 (the
+// copies of a timed-out call did not complete within the bound).
 int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t workgroups, StageCall *out,
                  std::string *err);
 
@@ -86,7 +89,9 @@ bool stager_failed(const SdmaStager *s);
 // Blocks (bounded) until the kernel of the call (set, epoch) has finished.
 int stager_wait_call(SdmaStager *s, int set, uint64_t epoch);
 
-// Blocks until every call begun on the stager has completed on the GPU.
+// Blocks (bounded) until every call begun on the stager has completed on the GPU and the copies
+// of any call whose waits timed out have completed: 0, -1 (a kernel did not finish) or -2 (copies
+// of a timed-out call did not complete).
 int stager_wait_idle(SdmaStager *s);
 
 }  // namespace sptl

@@ -43,6 +43,7 @@ _SIGS = {
     "sptl_version": ([], _int),
     "sptl_ctx_check": ([_vp], _int),
     "sptl_ctx_info": ([_vp], ctypes.c_char_p),
+    "sptl_ctx_set_wait_timeout_us": ([_vp, _i64], _int),
     "agmm_chunked": ([_vp, _i64, _i64, _i64, _int, _int, _int, _ptrs, _vp, _vp, _vp, _int, _vp, _vp,
                       _int], _int),
     "sptl_agmm_timeline": ([_vp, ctypes.POINTER(ctypes.c_double), _int], _int),
@@ -137,6 +138,10 @@ class Context:
     def check(self) -> None:
         """Wait for this context's staged calls and raise SptlError on a recorded async failure."""
         _check(_lib.sptl_ctx_check(self.handle))
+
+    def set_wait_timeout_us(self, us: int) -> None:
+        """Bound on one chunk wait of later staged calls, in microseconds (0: the default 10 s)."""
+        _check(_lib.sptl_ctx_set_wait_timeout_us(self.handle, int(us)))
 
     def info(self) -> str:
         """How agmm_chunked stages chunks on this context (diagnostic)."""

@@ -76,3 +76,23 @@ def round_bf16(x: Fraction) -> Fraction:
     if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
         n += 1
     return sign * n * Fraction(2) ** (e - 7)
+
+
+def bf16_bits(x: Fraction) -> int:
+    """Storage bits of the bf16 value nearest to ``x`` (ties to even), built field by field:
+    sign bit, 8-bit biased exponent, 7-bit fraction.  Normal range and zero only."""
+    r = round_bf16(Fraction(x))
+    if r == 0:
+        return 0x8000 if Fraction(x) < 0 else 0
+    sign = 1 if r < 0 else 0
+    a = abs(r)
+    e = 0
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    while Fraction(2) ** e > a:
+        e -= 1
+    if not -126 <= e <= 127:
+        raise ValueError("outside the normal bf16 range")
+    frac = (a / Fraction(2) ** e - 1) * 128      # exact: r has 8 significant bits
+    assert frac.denominator == 1
+    return (sign << 15) | ((e + 127) << 7) | int(frac)

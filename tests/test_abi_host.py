@@ -116,3 +116,7 @@ def test_dtp_validation(sptl, kw, status):
 
 def test_create_rejects_null_out(sptl):
     assert sptl._lib.sptl_create(None, 0) == 1
+
+
+def test_wait_timeout_option_rejects_null_ctx(sptl):
+    assert sptl._lib.sptl_ctx_set_wait_timeout_us(None, 5) == 1

@@ -469,38 +469,107 @@ def test_agmm_staged_back_to_back_calls(env):
 
 
 def test_agmm_staged_wait_timeout_is_reported(env):
-    """A chunk wait that runs out of time is reported by sptl_ctx_check as SPTL_E_ASYNC.
+    """A chunk wait that runs out of time is reported, and the context stays usable at once.
 
-    The bound on a chunk wait is set to 1 us for one context (from the host, through the
-    context's configuration), so the GEMM's workgroups give up long before 8 MiB chunks land;
-    every wave still exits normally.  The result is invalid; the report is what is checked.
+    The bound on a chunk wait is set to 1 us on one context from the host
+    (sptl_ctx_set_wait_timeout_us), so the GEMM's workgroups give up long before 8 MiB chunks
+    land; every wave still exits normally.  That call's result is invalid.  The default bound
+    is then restored and eight more calls follow back to back, with no host wait: the fifth
+    reuses the timed-out call's completion-signal set while that call's copies may still be
+    landing, so the set must be drained before it is re-armed (a late copy would otherwise mark
+    a chunk of the new call landed before it is).  Every later call gathers fresh shards into a
+    NaN-poisoned buffer and must match the oracle.
     """
-    import os
-    import time
     torch, sptl, ctx = env
-    os.environ["SPTL_WAIT_TIMEOUT_US"] = "1"
-    try:
-        short = sptl.Context(0)
-    finally:
-        del os.environ["SPTL_WAIT_TIMEOUT_US"]
+    short = sptl.Context(0)
     tp, rows, K, N = 8, 1024, 4096, 256
-    shards = [torch.ones((rows, K), dtype=torch.bfloat16, device="cuda") for _ in range(tp)]
-    xg = torch.empty((tp * rows, K), dtype=torch.bfloat16, device="cuda")
-    w = torch.ones((K, N), dtype=torch.bfloat16, device="cuda")
-    y = torch.empty((tp * rows, N), dtype=torch.bfloat16, device="cuda")
+    M = tp * rows
     try:
+        short.set_wait_timeout_us(1)
+        shards = [torch.ones((rows, K), dtype=torch.bfloat16, device="cuda") for _ in range(tp)]
+        xg = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        w = torch.ones((K, N), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         sptl.agmm_chunked(shards, xg, w, y, n_chunks=tp, rank=0, ctx=short)
+        short.set_wait_timeout_us(0)
+        w2_b = gen(71, (1,), K, N, 1.0 / K)
+        w2 = to_dev(w2_b)
+        calls = []
+        for i in range(8):
+            shards_b = [gen(80 + i, (0, q), rows, K) for q in range(tp)]
+            xg_i = torch.full((M, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+            y_i = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            srcs = [to_dev(b) for b in shards_b]
+            sptl.agmm_chunked(srcs, xg_i, w2, y_i, n_chunks=tp, rank=0, ctx=short)
+            calls.append((shards_b, srcs, xg_i, y_i))
         torch.cuda.synchronize()
         with pytest.raises(sptl.SptlError) as err:
-            short.check()
+            short.check()  # also waits for the abandoned call's copies
         assert err.value.status == 9, str(err.value)
         short.check()  # the report was cleared
-        time.sleep(0.05)  # the copies of the abandoned call land before its signals go away
-        torch.cuda.synchronize()
+        for i, (shards_b, srcs, xg_i, y_i) in enumerate(calls):
+            assert torch.equal(xg_i, torch.cat(srcs)), f"call {i + 1}: x_gathered"
+            _, want = O.agmm(shards_b, w2_b)
+            got = y_i.cpu().numpy().astype(np.float64)
+            assert np.isfinite(got).all(), f"call {i + 1}: read rows that had not landed"
+            assert_within(got, want, fp32_tol(want), f"call {i + 1}")
+        del xg, y, shards  # the timed-out call's copies have landed (short.check waited)
     finally:
         short.close()
     # the shared context is unaffected
+    shards = [torch.ones((rows, K), dtype=torch.bfloat16, device="cuda") for _ in range(tp)]
+    xg = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones((K, N), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     sptl.agmm_chunked(shards, xg, w, y, n_chunks=tp, rank=0, ctx=ctx)
     torch.cuda.synchronize()
     ctx.check()
     assert torch.all(y == float(K))
+
+
+def test_agmm_overlap_pattern(env):
+    """The pipeline's copy/compute overlap pattern, read from the call's device timeline.
+
+    "Add forward all-gather overlap" (Megatron-LM pull request 5513, "Summary") checks its
+    pipeline with a profiler test: over n children, the gather of child i + 1 runs while child
+    i computes, which gives n - 1 gather/compute overlaps.  Here the children are the chunks in
+    processing order (own chunk first, then the peers in arrival order) at the page's shape
+    (M = 8192, dim = 4096, 8 chunks).  A staged chunk is in flight from the previous staged
+    chunk's landing (the start, for the first) to its own, since the engines take the chunks in
+    order; its landing is when the first tile of the chunk saw it, an upper bound.  At least
+    (staged chunks - 1) of the pairs (chunk i computing, chunk i + 1 in flight) must overlap.
+    A pipeline that staged every chunk before computing any peer chunk would give one.
+    """
+    torch, sptl, ctx = env
+    wl = synth.WORKLOADS["h100_page_8192x4096"]
+    shards = [to_dev(wl.shard(q)) for q in range(wl.tp)]
+    w = to_dev(wl.w_col())
+    xg = torch.empty((wl.M, wl.K), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+    n = wl.n_chunks
+    best = -1
+    for trial in range(3):
+        for _ in range(3):
+            sptl.agmm_chunked(shards, xg, w, y, n_chunks=n, rank=0, ctx=ctx)
+        sptl.agmm_chunked(shards, xg, w, y, n_chunks=n, rank=0, ctx=ctx, timing=True)
+        tl = ctx.timeline(n)
+        ctx.check()
+        order = list(range(n))  # rank 0, one chunk per rank: own chunk 0, then peers 1, 2, ...
+        staged = [c for c in order if tl[c][1] >= 0]
+        assert len(staged) == n - 1
+        land = sorted(tl[c][1] for c in staged)
+        start = {}
+        prev = 0.0
+        for c, t in zip(sorted(staged, key=lambda c: tl[c][1]), land):
+            start[c] = prev
+            prev = t
+        pairs = 0
+        for a, b in zip(order, order[1:]):
+            g0, g1 = tl[a][2], tl[a][3]
+            c0, c1 = start[b], tl[b][1]
+            pairs += min(g1, c1) > max(g0, c0)
+        print(f"trial {trial}: {pairs} of {n - 1} (gemm i, copy i + 1) pairs overlap; landings {land}", flush=True)
+        best = max(best, pairs)
+        if best >= len(staged) - 1:
+            break
+    assert best >= len(staged) - 1, f"only {best} copy/compute overlaps, want {len(staged) - 1}"

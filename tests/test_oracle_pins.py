@@ -108,6 +108,29 @@ def check_round_to_bf16(impl):
     assert np.array_equal(impl.round_to_bf16(f.astype(np.float64)), other)
 
 
+def check_f64_to_bf16_bits(impl):
+    # hand-worked patterns: 1/3 = 1.0101010|1010...b * 2^-2 rounds up to fraction 0101011, so
+    # 0 01111101 0101011 = 0x3EAB; 1 + 2^-8 and -(1 + 2^-8) are ties that go to the even 1.0;
+    # 1 + 3 * 2^-8 ties to the even 1 + 2^-6 (0x3F82); 1 + 2^-8 + 2^-30 is above the tie and
+    # rounds up (a double rounding through binary32 would lose the 2^-30 and go down);
+    # 65504 = 1.1111111|111b * 2^15 rounds up with a carry into the exponent: 2^16 = 0x4780
+    cases = {1.0: 0x3F80, -2.0: 0xC000, 0.0: 0x0000, 3.140625: 0x4049, 1.0 / 3.0: 0x3EAB,
+             1 + 2.0 ** -8: 0x3F80, -(1 + 2.0 ** -8): 0xBF80, 1 + 3 * 2.0 ** -8: 0x3F82,
+             1 + 2.0 ** -8 + 2.0 ** -30: 0x3F81, 2.0 ** -126: 0x0080, 65504.0: 0x4780}
+    got = impl.f64_to_bf16_bits(np.array(list(cases), dtype=np.float64))
+    assert np.array_equal(got, np.array(list(cases.values()), dtype=np.uint16))
+    # every finite normal bf16 value (and +0) encodes back to its own bits
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    exp = (b >> 7) & 0xFF
+    b = b[((exp >= 1) & (exp <= 254)) | (b == 0)]
+    assert np.array_equal(impl.f64_to_bf16_bits(O.bf16_bits_to_f64(b)), b)
+    # float64 inputs between bf16 values, against the field-by-field brute encoder
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal(3000) * np.exp2(rng.integers(-60, 60, 3000))
+    want = np.array([brute.bf16_bits(brute.Fraction(float(v))) for v in x], dtype=np.uint16)
+    assert np.array_equal(impl.f64_to_bf16_bits(x), want)
+
+
 def check_agmm_golden(impl):
     g = load_golden("agmm_worked_tp3.txt")
     shards = [bits(g[f"shard{q}"]) for q in range(3)]
@@ -308,7 +331,7 @@ def check_dtp_store_bf16(impl):
         assert np.array_equal(steps[l][0], x)
 
 
-CHECKS = [check_bf16_decode, check_round_to_bf16, check_agmm_golden, check_agmm_brute,
+CHECKS = [check_bf16_decode, check_round_to_bf16, check_f64_to_bf16_bits, check_agmm_golden, check_agmm_brute,
           check_gemm_brute, check_special_weights, check_chunked_equals_unchunked,
           check_tp_identity, check_rmsnorm_golden, check_rmsnorm_closed_forms,
           check_rmsnorm_brute, check_norm_commutes_with_gather,
@@ -424,6 +447,11 @@ def _decode_wrong_bias(b):
     return O.bf16_bits_to_f64(b) * 2.0
 
 
+def _encode_via_binary32(x):        # rounds to binary32 first: a double rounding
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
 def _round_trunc(x):
     v = O._as_f64(x)
     m, e = np.frexp(v)
@@ -443,6 +471,7 @@ MUTANTS = {
     "dtp_missing_flush": dict(dtp_sequence=_dtp_seq_no_flush),
     "decode_wrong_exponent": dict(bf16_bits_to_f64=_decode_wrong_bias),
     "round_truncates": dict(round_to_bf16=_round_trunc),
+    "encode_double_rounding": dict(f64_to_bf16_bits=_encode_via_binary32),
 }
 
 
