@@ -21,10 +21,11 @@
  *   - Ownership: the caller owns every buffer and stream.  The library never allocates,
  *     frees or retains caller memory.  A context owns its own resources only: HIP events,
  *     a few small device buffers (an error word, chunk timestamps, 256 KiB of landed
- *     flags), and, from its first agmm_chunked call, a copy stream or an SDMA stager (4160
- *     HSA completion signals, about 40 KiB of device counters and tables, one page of pinned
- *     host memory and one worker thread).  These are created on first use, never on later calls.  Inputs must stay
- *     valid until the stream work of the call completes.
+ *     flags), an SDMA stager (4160 HSA completion signals, about 40 KiB of device counters
+ *     and tables, one page of pinned host memory and one worker thread), all created with
+ *     the context, and the copy stream of the per-chunk path, created on its first use.
+ *     The library also holds one 80 KiB device array per GPU (agmm_chunked_noalloc).
+ *     Inputs must stay valid until the stream work of the call completes.
  *   - Every call is asynchronous (stream-ordered) and returns an sptl_status.  All
  *     arguments are validated BEFORE anything is enqueued: on any non-OK status nothing
  *     was enqueued and sptl_last_error() holds a message.  HIP failures after validation
@@ -72,8 +73,9 @@ typedef enum {
 #define SPTL_MAX_K 2097152     /* GEMM reduction size (hidden of agmm_chunked, k_local)  */
 #define SPTL_MAX_N 8388608     /* GEMM output width (n_local, hidden of gemm_partial)    */
 
-/* Create a context on HIP device `device` (events and small device buffers are created
- * now; the copy stream or SDMA stager on the first agmm_chunked call).  *out receives the
+/* Create a context on HIP device `device`: events, small device buffers and the SDMA stager
+ * are created now (the copy stream of the per-chunk path on its first use), together with the
+ * set-up of agmm_chunked_noalloc for the device.  *out receives the
  * context.  Returns SPTL_E_NULL if out is NULL, SPTL_E_RANGE for a bad device, SPTL_E_HIP on
  * runtime failure.  Environment read here: SPTL_STAGING=events forces the per-chunk path;
  * SPTL_WAIT_TIMEOUT_US=1..10000000 sets the bound on one chunk wait (default 10 s). */
@@ -181,6 +183,29 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
                  int tp, int n_chunks, int rank,
                  const void *const *shard_src, void *x_gathered, const void *w,
                  void *y, int y_dtype, void *compute, void *copy, int timing);
+
+/*
+ * (1') agmm_chunked for callers that cannot allocate device memory (code that must not call
+ * hipMalloc: tight serving loops, harnesses that forbid it).  The same staged path and kernels
+ * as agmm_chunked with copy == NULL and timing == 0, with the same arguments otherwise and the
+ * same bits in x_gathered and y; the call itself calls no hipMalloc, hipFree or other
+ * allocating routine.
+ *   ctx      required (not NULL): sptl_create does this call's set-up, once per device (it
+ *            resolves the device's scratch array) and once per context (its copy engines).
+ *   The chunk-ordered GEMM keeps its state (landed flags, end counters, error word) in a fixed
+ *   80 KiB device array, one per GPU, held until the process ends; the end counters are zeroed
+ *   by a small kernel on `compute` before each launch (no memset).
+ * Limits: n_chunks <= 64 (the chunks the scratch holds: SPTL_E_SHAPE beyond) and
+ * seq_len / n_chunks a multiple of 128 (SPTL_E_UNSUPPORTED otherwise); SPTL_E_UNSUPPORTED also
+ * when the context has no working copy engines.  Every call on a GPU shares that GPU's
+ * scratch: calls whose GPU work overlaps in time (on different streams, or on contexts used
+ * from different threads) race and must not be made; calls ordered on one stream are safe.
+ * Timed-out waits are reported by sptl_ctx_check(ctx) as for agmm_chunked.
+ */
+int agmm_chunked_noalloc(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
+                         int tp, int n_chunks, int rank,
+                         const void *const *shard_src, void *x_gathered, const void *w,
+                         void *y, int y_dtype, void *compute);
 
 /* Per-chunk timeline of the last agmm_chunked call on ctx that had timing = 1.  Blocks
  * until that call's work is done.  out (host) receives n_chunks rows of 4 doubles in

@@ -14,6 +14,7 @@
 
 #include "sptl.h"
 #include "sptl_internal.h"
+#include "sptl_noalloc.h"
 #include "sptl_stager.h"
 
 struct sptl_ctx {
@@ -100,6 +101,18 @@ int grow_events(std::vector<hipEvent_t> &v, size_t n) {
     return SPTL_OK;
 }
 
+// Creates the context's SDMA stager (at context creation, with the context's device current);
+// without one, agmm_chunked takes the per-chunk event path.
+void make_stager(sptl_ctx *ctx) {
+    ctx->stager_tried = true;
+    if (ctx->events_only) return;
+    std::string why;
+    ctx->stager = sptl::stager_create(ctx->device, &why);
+    ctx->staging_info = ctx->stager ? "sdma-striped over " + std::to_string(sptl::stager_engine_count(ctx->stager)) +
+                                          " engines, chunk-ordered GEMM"
+                                    : "per-chunk events (copy engines unavailable: " + why + ")";
+}
+
 int create_ctx(sptl_ctx **out, int device) {
     int count = 0;
     SPTL_HIP(hipGetDeviceCount(&count));
@@ -137,6 +150,11 @@ int create_ctx(sptl_ctx **out, int device) {
             const long long us = strtoll(t, nullptr, 10);
             if (us >= 1 && us <= 10000000) c->wait_timeout_us = (uint64_t)us;
         }
+        // set-up for agmm_chunked_noalloc: the device's scratch array and this context's
+        // copy engines, so that the call itself allocates nothing
+        std::string why;
+        if (sptl::noalloc_setup(device, &why)) rc = fail(SPTL_E_HIP, "sptl_create: %s", why.c_str());
+        if (!rc) make_stager(c);
     }
     if (rc) {
         sptl_destroy(c);
@@ -191,23 +209,17 @@ int check_gemm_dims(int64_t m, int64_t k, int64_t n) {
 // Whether the chunk-ordered path (SDMA stager + one chunk-ordered GEMM) can serve this call.
 bool staged_path(sptl_ctx *ctx, int64_t rows_c, int n_chunks) {
     if (ctx->events_only || n_chunks > sptl::kMaxPlanChunks || !sptl::chunk_tile_rows(rows_c)) return false;
-    if (!ctx->stager_tried) {
-        ctx->stager_tried = true;
-        std::string why;
-        ctx->stager = sptl::stager_create(ctx->device, &why);  // null: the event path is used
-        ctx->staging_info = ctx->stager ? "sdma-striped over " + std::to_string(sptl::stager_engine_count(ctx->stager)) +
-                                              " engines, chunk-ordered GEMM"
-                                        : "per-chunk events (copy engines unavailable: " + why + ")";
-    }
     return ctx->stager && !sptl::stager_failed(ctx->stager);
 }
 
 // Chunk-ordered agmm: all staging copies go to the SDMA stager (striped over the copy
 // engines, released at the fork point), and one GEMM launch processes the row tiles in
 // chunk order, each tile waiting for its chunk's completion signal.  Arguments validated.
+// na: null for the context's own state (landed flags, error word, the stager's cumulative end
+// counters), or the device scratch of agmm_chunked_noalloc (timing is then 0).
 int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local, int tp, int n_chunks,
                 int rank, const void *const *shard_src, uint16_t *xg, const void *w, void *y, int y_dtype,
-                hipStream_t cs, int timing) {
+                hipStream_t cs, int timing, const sptl::NoallocScratch *na = nullptr) {
     const int cpr = n_chunks / tp;
     const int64_t rows_c = seq_len / n_chunks;
     const size_t chunk_elems = (size_t)rows_c * (size_t)hidden;
@@ -249,7 +261,7 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     plan.own_first = rank * cpr;
     plan.own_count = cpr;
     plan.own_a = static_cast<const uint16_t *>(shard_src[rank]);
-    plan.err = ctx->err_dev;
+    plan.err = na ? na->err : ctx->err_dev;
     plan.timeout_ticks = (uint64_t)ctx->wallclock_khz * ctx->wait_timeout_us / 1000u;
     static const int poll_sleep = [] {
         const char *e = getenv("SPTL_POLL_SLEEP");
@@ -280,7 +292,7 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
 
     sptl::StageCall call;
     std::string why;
-    if (int rc = sptl::stager_begin(ctx->stager, pieces, wgs, &call, &why))
+    if (int rc = sptl::stager_begin(ctx->stager, pieces, wgs, &call, &why, na ? na->counts : nullptr))
         return fail(rc == -2 ? SPTL_E_ASYNC : SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
     for (int c = 0; c < n; ++c) {
         plan.ready[c] = call.ready[c];
@@ -289,15 +301,17 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     for (int s = 0; s < cpr; ++s) plan.ready[rank * cpr + s] = nullptr;  // read from the source
     plan.join = call.join;
     plan.join_n = call.join_n;
-    plan.flags = ctx->flags_dev + (size_t)call.set * sptl::kFlagSetWords;
+    plan.flags = na ? na->flags : ctx->flags_dev + (size_t)call.set * sptl::kFlagSetWords;
     plan.epoch = call.epoch;
+    plan.flag_epoch = na ? na->flag_epoch : call.epoch;  // the context's flags are the set's own
     plan.finished = call.finished;
     plan.timedout = call.timedout;
     plan.wg_count = call.wg_count;
     for (int g = 0; g < sptl::kEndGroups; ++g) plan.grp_last[g] = call.grp_last[g];
     plan.all_last = call.all_last;
     hipError_t he = hipSuccess;
-    if (timing) {
+    if (na) he = sptl::launch_fill_u64(na->counts, na->count_words, 0ull, cs);  // a kernel, not a memset
+    if (he == hipSuccess && timing) {
         he = sptl::launch_fill_u64(ctx->ts_dev, 2 * n, ~0ull, cs);
         if (he == hipSuccess) he = sptl::launch_fill_u64(ctx->ts_dev + 2 * n, n + 1, 0ull, cs);
     }
@@ -329,7 +343,7 @@ int sptl_version(void) { return 100; }
 const char *sptl_ctx_info(sptl_ctx *ctx) {
     if (resolve_ctx(ctx)) return "";
     if (ctx->events_only) return "per-chunk events (forced by SPTL_STAGING=events)";
-    if (!ctx->stager_tried) return "not yet decided (no agmm_chunked call)";
+    if (!ctx->stager_tried) return "no copy engines set up";
     return ctx->staging_info.c_str();
 }
 
@@ -346,8 +360,11 @@ int sptl_ctx_check(sptl_ctx *ctx) {
     SPTL_HIP(hipMemcpy(&flag, ctx->err_dev, sizeof flag, hipMemcpyDeviceToHost));
     if (flag) {
         SPTL_HIP(hipMemset(ctx->err_dev, 0, sizeof flag));
+        if (ctx->stager) (void)sptl::stager_take_timeouts(ctx->stager);  // the same report
         return fail(SPTL_E_ASYNC, "a staging wait timed out; the affected agmm_chunked results are invalid");
     }
+    if (ctx->stager && sptl::stager_take_timeouts(ctx->stager))
+        return fail(SPTL_E_ASYNC, "a staging wait timed out; the affected agmm_chunked results are invalid");
     if (ctx->stager && sptl::stager_failed(ctx->stager))
         return fail(SPTL_E_ASYNC, "a staging copy could not be submitted; the staged path is now disabled");
     return SPTL_OK;
@@ -393,31 +410,49 @@ int sptl_destroy(sptl_ctx *ctx) {
     return SPTL_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by agmm_chunked and agmm_chunked_noalloc (fn names the call).
+int check_agmm_args(const char *fn, int64_t seq_len, int64_t hidden, int64_t n_local, int tp, int n_chunks,
+                    int rank, const void *const *shard_src, const void *x_gathered, const void *w, const void *y,
+                    int y_dtype) {
+    if (!shard_src || !x_gathered || !w || !y) return fail(SPTL_E_NULL, "%s: NULL pointer argument", fn);
+    if (seq_len < 0 || hidden <= 0 || n_local <= 0)
+        return fail(SPTL_E_SHAPE, "%s: bad sizes seq_len=%lld hidden=%lld n_local=%lld", fn, (long long)seq_len,
+                    (long long)hidden, (long long)n_local);
+    if (tp < 1 || tp > SPTL_MAX_TP) return fail(SPTL_E_RANGE, "%s: tp=%d not in [1, %d]", fn, tp, SPTL_MAX_TP);
+    if (n_chunks < 1 || n_chunks > SPTL_MAX_CHUNKS)
+        return fail(SPTL_E_RANGE, "%s: n_chunks=%d not in [1, %d]", fn, n_chunks, SPTL_MAX_CHUNKS);
+    if (rank < 0 || rank >= tp) return fail(SPTL_E_RANGE, "%s: rank=%d not in [0, %d)", fn, rank, tp);
+    if (n_chunks % tp) return fail(SPTL_E_DIVISIBILITY, "%s: n_chunks=%d not a multiple of tp=%d", fn, n_chunks, tp);
+    if (seq_len % n_chunks)
+        return fail(SPTL_E_DIVISIBILITY, "%s: seq_len=%lld not a multiple of n_chunks=%d", fn, (long long)seq_len,
+                    n_chunks);
+    if (y_dtype != SPTL_BF16 && y_dtype != SPTL_F32) return fail(SPTL_E_DTYPE, "%s: y_dtype=%d", fn, y_dtype);
+    if (int rc = check_gemm_dims(seq_len / n_chunks, hidden, n_local)) return rc;
+    for (int q = 0; q < tp; ++q) {
+        if (!shard_src[q]) return fail(SPTL_E_NULL, "%s: shard_src[%d] is NULL", fn, q);
+        if (!aligned16(shard_src[q])) return fail(SPTL_E_ALIGN, "%s: shard_src[%d] not 16-byte aligned", fn, q);
+    }
+    if (!aligned16(x_gathered) || !aligned16(w) || !aligned16(y))
+        return fail(SPTL_E_ALIGN, "%s: x_gathered, w and y must be 16-byte aligned", fn);
+    return SPTL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local, int tp,
                  int n_chunks, int rank, const void *const *shard_src, void *x_gathered,
                  const void *w, void *y, int y_dtype, void *compute, void *copy, int timing) {
     // ---- validation: nothing is enqueued on failure ------------------------------------
-    if (!shard_src || !x_gathered || !w || !y) return fail(SPTL_E_NULL, "agmm_chunked: NULL pointer argument");
-    if (seq_len < 0 || hidden <= 0 || n_local <= 0)
-        return fail(SPTL_E_SHAPE, "agmm_chunked: bad sizes seq_len=%lld hidden=%lld n_local=%lld",
-                    (long long)seq_len, (long long)hidden, (long long)n_local);
-    if (tp < 1 || tp > SPTL_MAX_TP) return fail(SPTL_E_RANGE, "agmm_chunked: tp=%d not in [1, %d]", tp, SPTL_MAX_TP);
-    if (n_chunks < 1 || n_chunks > SPTL_MAX_CHUNKS)
-        return fail(SPTL_E_RANGE, "agmm_chunked: n_chunks=%d not in [1, %d]", n_chunks, SPTL_MAX_CHUNKS);
-    if (rank < 0 || rank >= tp) return fail(SPTL_E_RANGE, "agmm_chunked: rank=%d not in [0, %d)", rank, tp);
-    if (n_chunks % tp) return fail(SPTL_E_DIVISIBILITY, "agmm_chunked: n_chunks=%d not a multiple of tp=%d", n_chunks, tp);
-    if (seq_len % n_chunks)
-        return fail(SPTL_E_DIVISIBILITY, "agmm_chunked: seq_len=%lld not a multiple of n_chunks=%d",
-                    (long long)seq_len, n_chunks);
-    if (y_dtype != SPTL_BF16 && y_dtype != SPTL_F32) return fail(SPTL_E_DTYPE, "agmm_chunked: y_dtype=%d", y_dtype);
+    if (int rc = check_agmm_args("agmm_chunked", seq_len, hidden, n_local, tp, n_chunks, rank, shard_src, x_gathered,
+                                 w, y, y_dtype))
+        return rc;
     if (timing != 0 && timing != 1) return fail(SPTL_E_RANGE, "agmm_chunked: timing=%d", timing);
-    if (int rc = check_gemm_dims(seq_len / n_chunks, hidden, n_local)) return rc;
-    for (int q = 0; q < tp; ++q) {
-        if (!shard_src[q]) return fail(SPTL_E_NULL, "agmm_chunked: shard_src[%d] is NULL", q);
-        if (!aligned16(shard_src[q])) return fail(SPTL_E_ALIGN, "agmm_chunked: shard_src[%d] not 16-byte aligned", q);
-    }
-    if (!aligned16(x_gathered) || !aligned16(w) || !aligned16(y))
-        return fail(SPTL_E_ALIGN, "agmm_chunked: x_gathered, w and y must be 16-byte aligned");
     if (seq_len == 0) return SPTL_OK;
     if (int rc = resolve_ctx(ctx)) return rc;
     DeviceGuard g(ctx->device);
@@ -526,6 +561,34 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
         ctx->t_chunks = n_chunks;
     }
     return SPTL_OK;
+}
+
+int agmm_chunked_noalloc(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local, int tp, int n_chunks,
+                         int rank, const void *const *shard_src, void *x_gathered, const void *w, void *y,
+                         int y_dtype, void *compute) {
+    static const char *fn = "agmm_chunked_noalloc";
+    if (!ctx) return fail(SPTL_E_NULL, "%s: ctx is NULL (its set-up happens in sptl_create)", fn);
+    if (int rc = check_agmm_args(fn, seq_len, hidden, n_local, tp, n_chunks, rank, shard_src, x_gathered, w, y,
+                                 y_dtype))
+        return rc;
+    if (n_chunks > sptl::kMaxPlanChunks)
+        return fail(SPTL_E_SHAPE, "%s: n_chunks=%d exceeds the %d chunks its device scratch holds", fn, n_chunks,
+                    sptl::kMaxPlanChunks);
+    if (!sptl::chunk_tile_rows(seq_len / n_chunks))
+        return fail(SPTL_E_UNSUPPORTED, "%s: rows per chunk (%lld) must be a multiple of 128", fn,
+                    (long long)(seq_len / n_chunks));
+    if (seq_len == 0) return SPTL_OK;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    if (!ctx->stager || sptl::stager_failed(ctx->stager))
+        return fail(SPTL_E_UNSUPPORTED, "%s: the context has no working copy engines (%s)", fn,
+                    ctx->staging_info.c_str());
+    sptl::NoallocScratch na;
+    if (!sptl::noalloc_scratch(ctx->device, &na))
+        return fail(SPTL_E_HIP, "%s: the device scratch was not set up", fn);
+    ctx->t_chunks = -1;
+    return agmm_staged(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, shard_src,
+                       static_cast<uint16_t *>(x_gathered), w, y, y_dtype, static_cast<hipStream_t>(compute), 0, &na);
 }
 
 int sptl_agmm_timeline(sptl_ctx *ctx, double *out, int n_chunks) {

@@ -127,11 +127,11 @@ __device__ __forceinline__ void wait_chunk(const ChunkPlan &plan, int chunk, int
     uint64_t *mine = plan.flags + (size_t)(bid % kFlagReplicas) * kFlagStride + chunk;
     const uint64_t t0 = wall_clock64();
     for (unsigned it = (unsigned)bid;; ++it) {
-        if (__hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == plan.epoch) break;
+        if (__hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == plan.flag_epoch) break;
         if (it % kSignalPollEvery == 0 && pieces_landed(words, n)) {
             __atomic_thread_fence(__ATOMIC_ACQ_REL);  // the flags are set after the landing was seen
             if (lane < kFlagReplicas)
-                __hip_atomic_store(plan.flags + (size_t)lane * kFlagStride + chunk, plan.epoch, __ATOMIC_RELAXED,
+                __hip_atomic_store(plan.flags + (size_t)lane * kFlagStride + chunk, plan.flag_epoch, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_SYSTEM);
             break;
         }
@@ -151,7 +151,7 @@ __device__ __forceinline__ bool chunk_ready_now(const ChunkPlan &plan, int chunk
     bool ok;
     if (plan.flags &&
         __hip_atomic_load(plan.flags + (size_t)(bid % kFlagReplicas) * kFlagStride + chunk, __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_SYSTEM) == plan.epoch) {
+                          __HIP_MEMORY_SCOPE_SYSTEM) == plan.flag_epoch) {
         ok = true;
     } else {
         ok = pieces_landed(words, n);
@@ -159,7 +159,7 @@ __device__ __forceinline__ bool chunk_ready_now(const ChunkPlan &plan, int chunk
             __atomic_thread_fence(__ATOMIC_ACQ_REL);
             const int lane = threadIdx.x & 63;
             if (lane < kFlagReplicas)
-                __hip_atomic_store(plan.flags + (size_t)lane * kFlagStride + chunk, plan.epoch, __ATOMIC_RELAXED,
+                __hip_atomic_store(plan.flags + (size_t)lane * kFlagStride + chunk, plan.flag_epoch, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }

@@ -42,7 +42,9 @@ struct ChunkPlan {
                                              // chunk order)
     int chunk_band;                          // tile rows per band inside a chunk (set by launch_gemm)
     uint64_t *flags;                         // landed flags (kFlagSetWords words), or nullptr
-    uint64_t epoch;                          // value a landed flag holds for this launch
+    uint64_t flag_epoch;                     // value a landed flag holds for this launch (unique
+                                             // among the launches that share the flags)
+    uint64_t epoch;                          // value the end words take for this launch
     uint64_t *finished;                      // pinned host word: epoch once the launch is done
     uint64_t *timedout;                      // pinned host word: epoch if a wait of the launch timed out
     uint64_t *wg_count;                      // end counters of the signal set (kEndCounters lines)
@@ -52,7 +54,7 @@ struct ChunkPlan {
 };
 // Waiting: a workgroup of chunk c polls its replica of c's landed flag about every
 // microsecond and, once every 16 polls (phase set by its index), c's completion words
-// themselves.  The first workgroup to see them all reach zero sets every replica to `epoch`.  Spreading
+// themselves.  The first workgroup to see them all reach zero sets every replica to `flag_epoch`.  Spreading
 // the polls over replicas keeps a few hundred waiting workgroups from hammering the one
 // memory line the copy engines update.
 // End: workgroup b counts itself in group counter b % kEndGroups (line g of wg_count, 256

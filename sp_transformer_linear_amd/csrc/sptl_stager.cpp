@@ -132,10 +132,17 @@ class SdmaStager {
     // Whether the last call begun on `set` may have left copies in flight: a wait of its
     // kernel timed out, or a submission failed (the failure path released its waiters).
     // Only meaningful once that kernel has reported its end.
-    bool tainted(int set) const {
+    bool tainted(int set) {
         const uint64_t e = sets[set].epoch;
-        return e && (__atomic_load_n(timedout(set), __ATOMIC_ACQUIRE) == e || failed.load());
+        const bool timed_out = e && __atomic_load_n(timedout(set), __ATOMIC_ACQUIRE) == e;
+        if (timed_out && timeout_noted[set] != e) {
+            timeout_noted[set] = e;
+            timeout_pending = true;
+        }
+        return e && (timed_out || failed.load());
     }
+    uint64_t timeout_noted[kSets] = {};  // per set: epoch of the last timed-out call noted
+    bool timeout_pending = false;        // a timed-out call was noted since the last report
 
     // Bounded wait until every copy of the last call on `set` is done: the worker has handled
     // its job (submitted every piece or given up) and every armed piece signal reads <= 0.
@@ -464,8 +471,17 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
     return out;
 }
 
+bool stager_take_timeouts(SdmaStager *s) {
+    for (int set = 0; set < kSets; ++set)
+        if (s->sets[set].epoch && __atomic_load_n(s->finished(set), __ATOMIC_ACQUIRE) == s->sets[set].epoch)
+            (void)s->tainted(set);
+    const bool r = s->timeout_pending;
+    s->timeout_pending = false;
+    return r;
+}
+
 int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t workgroups, StageCall *out,
-                 std::string *err) {
+                 std::string *err, uint64_t *fresh_counts) {
     int count[kMaxPlanChunks + 1] = {};
     for (const CopyPiece &p : pieces) {
         if (p.chunk < 0 || p.chunk > kMaxPlanChunks || p.piece != count[p.chunk] || p.piece >= kMaxPieces) {
@@ -510,18 +526,21 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
     out->fork = ss.fork;
     out->finished = const_cast<uint64_t *>(s->finished(set));
     out->timedout = const_cast<uint64_t *>(s->timedout(set));
-    out->wg_count = s->counts + (size_t)kSetCountWords * set;
+    // Cumulative counters of the set, or counters the caller zeroes before the launch.
+    out->wg_count = fresh_counts ? fresh_counts : s->counts + (size_t)kSetCountWords * set;
     int groups = 0;
     for (int g = 0; g < kEndGroups; ++g) {
         const int64_t n = workgroups > g ? (workgroups - g + kEndGroups - 1) / kEndGroups : 0;
+        const uint64_t base = fresh_counts ? 0 : ss.grp_total[g];
         out->grp_first[g] = ss.grp_total[g];
-        out->grp_last[g] = n ? ss.grp_total[g] + (uint64_t)n - 1 : ~0ull;
-        ss.grp_total[g] += (uint64_t)n;
+        out->grp_last[g] = n ? base + (uint64_t)n - 1 : ~0ull;
+        if (!fresh_counts) ss.grp_total[g] += (uint64_t)n;
         groups += n ? 1 : 0;
     }
+    const uint64_t all_base = fresh_counts ? 0 : ss.all_total;
     out->all_first = ss.all_total;
-    out->all_last = ss.all_total + (uint64_t)groups - 1;
-    ss.all_total += (uint64_t)groups;
+    out->all_last = all_base + (uint64_t)groups - 1;
+    if (!fresh_counts) ss.all_total += (uint64_t)groups;
     return 0;
 }
 

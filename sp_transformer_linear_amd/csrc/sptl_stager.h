@@ -72,9 +72,15 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
 // workgroups, and arms it with the number of pieces per chunk.  Blocks (bounded) while the
 // set's previous call is still running and, if a wait of that call timed out, until its copies
 // have completed.  Returns 0, -1 (the previous call did not finish; bad pieces) or -2 (the
-// copies of a timed-out call did not complete within the bound).
+// copies of a timed-out call did not complete within the bound).  fresh_counts: null to count
+// the kernel's workgroups in the set's own cumulative counters, or kEndCounters lines of
+// counters (kEndLine words apart) that the caller zeroes on the stream before the launch.
 int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t workgroups, StageCall *out,
-                 std::string *err);
+                 std::string *err, uint64_t *fresh_counts = nullptr);
+
+// Whether a call whose chunk wait timed out has been seen (on reuse of its set, on an idle wait or
+// now, for calls that have ended) since the last time this returned true.
+bool stager_take_timeouts(SdmaStager *s);
 
 // Queues the pieces; a worker thread submits them to the engines as soon as `call.fork`
 // has completed.

@@ -46,6 +46,7 @@ _SIGS = {
     "sptl_ctx_set_wait_timeout_us": ([_vp, _i64], _int),
     "agmm_chunked": ([_vp, _i64, _i64, _i64, _int, _int, _int, _ptrs, _vp, _vp, _vp, _int, _vp, _vp,
                       _int], _int),
+    "agmm_chunked_noalloc": ([_vp, _i64, _i64, _i64, _int, _int, _int, _ptrs, _vp, _vp, _vp, _int, _vp], _int),
     "sptl_agmm_timeline": ([_vp, ctypes.POINTER(ctypes.c_double), _int], _int),
     "gemm_partial": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp], _int),
     "reduce_residual_rmsnorm": ([_vp, _i64, _i64, _int, _ptrs, _vp, _vp, ctypes.c_float, _vp, _vp,
@@ -93,6 +94,12 @@ def raw_agmm_chunked(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, shard_sr
                      y, y_dtype, compute, copy, timing=0) -> int:
     return _lib.agmm_chunked(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, _ptr_array(shard_src),
                              x_gathered, w, y, y_dtype, compute, copy, timing)
+
+
+def raw_agmm_chunked_noalloc(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, shard_src, x_gathered, w,
+                             y, y_dtype, compute) -> int:
+    return _lib.agmm_chunked_noalloc(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, _ptr_array(shard_src),
+                                     x_gathered, w, y, y_dtype, compute)
 
 
 def raw_gemm_partial(ctx, seq_len, k_local, hidden, a, w, partial, out_dtype, stream) -> int:

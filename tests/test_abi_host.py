@@ -120,3 +120,17 @@ def test_create_rejects_null_out(sptl):
 
 def test_wait_timeout_option_rejects_null_ctx(sptl):
     assert sptl._lib.sptl_ctx_set_wait_timeout_us(None, 5) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ctx=None), 1),                                   # the set-up lives in the context
+    (dict(tp=0), 6), (dict(y_dtype=3), 5), (dict(w=A + 4), 4),
+    (dict(seq_len=128 * 128, n_chunks=128), 2),            # more chunks than the scratch holds
+    (dict(seq_len=256, n_chunks=4), 8),                    # 64 rows per chunk: no chunk tile fits
+])
+def test_agmm_noalloc_validation(sptl, kw, status):
+    d = dict(ctx=A, seq_len=512, hidden=256, n_local=512, tp=2, n_chunks=2, rank=0,
+             shard_src=[A, A + 0x100000], x_gathered=A, w=A, y=A, y_dtype=0, compute=None)
+    d.update(kw)
+    assert sptl.raw_agmm_chunked_noalloc(**d) == status, sptl.last_error()
+    assert "agmm_chunked_noalloc" in sptl.last_error()
