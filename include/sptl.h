@@ -255,6 +255,32 @@ int reduce_residual_rmsnorm(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int 
                             void *stream);
 
 /*
+ * (3+1) Sub-layer boundary overlap: reduce + residual + RMSNorm of this rank's rows fused with the
+ * next sub-layer's chunked all-gather + column GEMM.
+ *
+ * [AReaL "Potential Solution", sub-layer boundary overlap]: the norm reduces over the hidden
+ * dimension and the gather runs over the sequence, so gathering before the norm gives the same
+ * result and lets the gather start earlier.  Here the peers' rows (the other ranks' already
+ * normalised shards) start staging at the call's position, before this rank's boundary epilogue
+ * runs; the epilogue writes this rank's normalised rows straight into its slot of x_gathered, and
+ * the chunk-ordered GEMM follows on `compute`.  The results are bit for bit those of
+ *   reduce_residual_rmsnorm(rows = seq_len / tp, partials, residual, gamma, eps, residual_out,
+ *                           y = this rank's slot of x_gathered)
+ *   agmm_chunked(shard_src with entry `rank` = that slot, ..., copy = NULL, timing = 0)
+ * on the same stream; only the peers' copies start earlier (they overlap the epilogue).
+ *   n_partials, partials, residual, gamma, eps, residual_out: as reduce_residual_rmsnorm for the
+ *            seq_len / tp rows of this rank (hidden columns); residual_out may be NULL
+ *   seq_len .. y_dtype, compute: as agmm_chunked; shard_src[rank] is not used (may be NULL)
+ * Work on `compute` before the call must be done with x_gathered (the copies start at the call's
+ * position, as in agmm_chunked).  Without copy engines the pair runs unfused on `compute`.
+ */
+int reduce_norm_agmm_chunked(sptl_ctx *ctx, int n_partials, const void *const *partials,
+                             const void *residual, const void *gamma, float eps, void *residual_out,
+                             int64_t seq_len, int64_t hidden, int64_t n_local, int tp, int n_chunks,
+                             int rank, const void *const *shard_src, void *x_gathered,
+                             const void *w, void *y, int y_dtype, void *compute);
+
+/*
  * (4) Delayed tensor parallelism: residual update of module `module_idx`.
  *
  * [DTP abstract]: each device adds its own partial output to its residual stream at once

@@ -216,10 +216,13 @@ bool staged_path(sptl_ctx *ctx, int64_t rows_c, int n_chunks) {
 // engines, released at the fork point), and one GEMM launch processes the row tiles in
 // chunk order, each tile waiting for its chunk's completion signal.  Arguments validated.
 // na: null for the context's own state (landed flags, error word, the stager's cumulative end
-// counters), or the device scratch of agmm_chunked_noalloc (timing is then 0).
+// counters), or the device scratch of agmm_chunked_noalloc (timing is then 0).  pre: an epilogue
+// launched on cs between the fork point and the GEMM (the sub-layer boundary of
+// reduce_norm_agmm_chunked; it writes the own slot, which shard_src[rank] then aliases).
 int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local, int tp, int n_chunks,
                 int rank, const void *const *shard_src, uint16_t *xg, const void *w, void *y, int y_dtype,
-                hipStream_t cs, int timing, const sptl::NoallocScratch *na = nullptr) {
+                hipStream_t cs, int timing, const sptl::NoallocScratch *na = nullptr,
+                const sptl::EpilogueProblem *pre = nullptr) {
     const int cpr = n_chunks / tp;
     const int64_t rows_c = seq_len / n_chunks;
     const size_t chunk_elems = (size_t)rows_c * (size_t)hidden;
@@ -316,6 +319,7 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
         if (he == hipSuccess) he = sptl::launch_fill_u64(ctx->ts_dev + 2 * n, n + 1, 0ull, cs);
     }
     if (he == hipSuccess) he = hipEventRecord(call.fork, cs);
+    if (he == hipSuccess && pre) he = sptl::launch_epilogue(*pre, cs);  // the copies run meanwhile
     if (he == hipSuccess) he = sptl::launch_gemm(gp, cs);
     if (he != hipSuccess) {
         sptl::stager_cancel(ctx->stager, call);
@@ -684,37 +688,95 @@ int check_epilogue_common(const char *fn, int64_t seq_len, int64_t hidden, float
 
 extern "C" {
 
+}  // extern "C"
+
+namespace {
+
+// Validates the arguments of a reduce + residual + RMSNorm over `rows` rows and fills *ep
+// (everything but the launch).  fn names the calling entry point.
+int build_reduce(const char *fn, int64_t rows, int64_t hidden, int tp, const void *const *partials,
+                 const void *residual, const void *gamma, float eps, void *residual_out, void *y,
+                 sptl::EpilogueProblem *ep) {
+    if (!residual || !gamma || !y) return fail(SPTL_E_NULL, "%s: NULL pointer argument", fn);
+    if (tp < 0 || tp > SPTL_MAX_PARTIALS) return fail(SPTL_E_RANGE, "%s: tp=%d not in [0, %d]", fn, tp, SPTL_MAX_PARTIALS);
+    if (tp > 0 && !partials) return fail(SPTL_E_NULL, "%s: partials is NULL", fn);
+    if (int rc = check_epilogue_common(fn, rows, hidden, eps)) return rc;
+    *ep = sptl::EpilogueProblem{};
+    ep->in[0] = static_cast<const uint16_t *>(residual);
+    for (int p = 0; p < tp; ++p) {
+        if (!partials[p]) return fail(SPTL_E_NULL, "%s: partials[%d] is NULL", fn, p);
+        ep->in[1 + p] = static_cast<const uint16_t *>(partials[p]);
+    }
+    ep->n_in = 1 + tp;
+    for (int i = 0; i < ep->n_in; ++i)
+        if (!aligned16(ep->in[i])) return fail(SPTL_E_ALIGN, "%s: input %d not 16-byte aligned", fn, i);
+    if (!aligned16(gamma) || !aligned16(y) || !aligned16(residual_out))
+        return fail(SPTL_E_ALIGN, "%s: gamma, y, residual_out must be 16-byte aligned", fn);
+    ep->gamma = static_cast<const uint16_t *>(gamma);
+    ep->h_out = static_cast<uint16_t *>(residual_out);
+    ep->y_out = static_cast<uint16_t *>(y);
+    ep->rows = rows;
+    ep->hidden = hidden;
+    ep->eps = eps;
+    return SPTL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int reduce_residual_rmsnorm(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int tp,
                             const void *const *partials, const void *residual, const void *gamma,
                             float eps, void *residual_out, void *y, void *stream) {
-    if (!residual || !gamma || !y) return fail(SPTL_E_NULL, "reduce_residual_rmsnorm: NULL pointer argument");
-    if (tp < 0 || tp > SPTL_MAX_PARTIALS)
-        return fail(SPTL_E_RANGE, "reduce_residual_rmsnorm: tp=%d not in [0, %d]", tp, SPTL_MAX_PARTIALS);
-    if (tp > 0 && !partials) return fail(SPTL_E_NULL, "reduce_residual_rmsnorm: partials is NULL");
-    if (int rc = check_epilogue_common("reduce_residual_rmsnorm", seq_len, hidden, eps)) return rc;
-    sptl::EpilogueProblem ep{};
-    ep.in[0] = static_cast<const uint16_t *>(residual);
-    for (int p = 0; p < tp; ++p) {
-        if (!partials[p]) return fail(SPTL_E_NULL, "reduce_residual_rmsnorm: partials[%d] is NULL", p);
-        ep.in[1 + p] = static_cast<const uint16_t *>(partials[p]);
-    }
-    ep.n_in = 1 + tp;
-    for (int i = 0; i < ep.n_in; ++i)
-        if (!aligned16(ep.in[i])) return fail(SPTL_E_ALIGN, "reduce_residual_rmsnorm: input %d not 16-byte aligned", i);
-    if (!aligned16(gamma) || !aligned16(y) || !aligned16(residual_out))
-        return fail(SPTL_E_ALIGN, "reduce_residual_rmsnorm: gamma, y, residual_out must be 16-byte aligned");
+    sptl::EpilogueProblem ep;
+    if (int rc = build_reduce("reduce_residual_rmsnorm", seq_len, hidden, tp, partials, residual, gamma, eps,
+                              residual_out, y, &ep))
+        return rc;
     if (seq_len == 0) return SPTL_OK;
     if (int rc = resolve_ctx(ctx)) return rc;
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
-    ep.gamma = static_cast<const uint16_t *>(gamma);
-    ep.h_out = static_cast<uint16_t *>(residual_out);
-    ep.y_out = static_cast<uint16_t *>(y);
-    ep.rows = seq_len;
-    ep.hidden = hidden;
-    ep.eps = eps;
     SPTL_HIP(sptl::launch_epilogue(ep, static_cast<hipStream_t>(stream)));
     return SPTL_OK;
+}
+
+int reduce_norm_agmm_chunked(sptl_ctx *ctx, int n_partials, const void *const *partials, const void *residual,
+                             const void *gamma, float eps, void *residual_out, int64_t seq_len, int64_t hidden,
+                             int64_t n_local, int tp, int n_chunks, int rank, const void *const *shard_src,
+                             void *x_gathered, const void *w, void *y, int y_dtype, void *compute) {
+    static const char *fn = "reduce_norm_agmm_chunked";
+    if (!shard_src || !x_gathered) return fail(SPTL_E_NULL, "%s: NULL pointer argument", fn);
+    if (tp < 1 || tp > SPTL_MAX_TP) return fail(SPTL_E_RANGE, "%s: tp=%d not in [1, %d]", fn, tp, SPTL_MAX_TP);
+    if (rank < 0 || rank >= tp) return fail(SPTL_E_RANGE, "%s: rank=%d not in [0, %d)", fn, rank, tp);
+    if (seq_len < 0 || hidden <= 0)
+        return fail(SPTL_E_SHAPE, "%s: bad sizes seq_len=%lld hidden=%lld", fn, (long long)seq_len, (long long)hidden);
+    // the own rows' normalised output goes to this rank's slot of x_gathered, which the GEMM then
+    // reads in place (shard_src[rank] is not used)
+    const int64_t own_rows = seq_len / tp;
+    auto *own_slot = static_cast<uint16_t *>(x_gathered) + (size_t)rank * (size_t)own_rows * (size_t)hidden;
+    std::vector<const void *> src(shard_src, shard_src + tp);
+    src[(size_t)rank] = own_slot;
+    if (int rc = check_agmm_args(fn, seq_len, hidden, n_local, tp, n_chunks, rank, src.data(), x_gathered, w, y,
+                                 y_dtype))
+        return rc;
+    sptl::EpilogueProblem ep;
+    if (int rc = build_reduce(fn, own_rows, hidden, n_partials, partials, residual, gamma, eps, residual_out,
+                              own_slot, &ep))
+        return rc;
+    if (seq_len == 0) return SPTL_OK;
+    if (int rc = resolve_ctx(ctx)) return rc;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    hipStream_t cs = static_cast<hipStream_t>(compute);
+    if (staged_path(ctx, seq_len / n_chunks, n_chunks)) {
+        ctx->t_chunks = -1;
+        return agmm_staged(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, src.data(),
+                           static_cast<uint16_t *>(x_gathered), w, y, y_dtype, cs, 0, nullptr, &ep);
+    }
+    // no copy engines: the unfused pair (the copies start after the epilogue)
+    SPTL_HIP(sptl::launch_epilogue(ep, cs));
+    return agmm_chunked(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, src.data(), x_gathered, w, y, y_dtype,
+                        compute, nullptr, 0);
 }
 
 int dtp_accumulate(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int tp, int delta, int module_idx,

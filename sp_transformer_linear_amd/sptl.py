@@ -48,6 +48,8 @@ _SIGS = {
                       _int], _int),
     "agmm_chunked_noalloc": ([_vp, _i64, _i64, _i64, _int, _int, _int, _ptrs, _vp, _vp, _vp, _int, _vp], _int),
     "sptl_agmm_timeline": ([_vp, ctypes.POINTER(ctypes.c_double), _int], _int),
+    "reduce_norm_agmm_chunked": ([_vp, _int, _ptrs, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i64, _int, _int,
+                                  _int, _ptrs, _vp, _vp, _vp, _int, _vp], _int),
     "gemm_partial": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp], _int),
     "reduce_residual_rmsnorm": ([_vp, _i64, _i64, _int, _ptrs, _vp, _vp, ctypes.c_float, _vp, _vp,
                                  _vp], _int),
@@ -100,6 +102,13 @@ def raw_agmm_chunked_noalloc(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, 
                              y, y_dtype, compute) -> int:
     return _lib.agmm_chunked_noalloc(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, _ptr_array(shard_src),
                                      x_gathered, w, y, y_dtype, compute)
+
+
+def raw_reduce_norm_agmm_chunked(ctx, n_partials, partials, residual, gamma, eps, residual_out, seq_len, hidden,
+                                 n_local, tp, n_chunks, rank, shard_src, x_gathered, w, y, y_dtype, compute) -> int:
+    return _lib.reduce_norm_agmm_chunked(ctx, n_partials, _ptr_array(partials), residual, gamma, eps, residual_out,
+                                         seq_len, hidden, n_local, tp, n_chunks, rank, _ptr_array(shard_src),
+                                         x_gathered, w, y, y_dtype, compute)
 
 
 def raw_gemm_partial(ctx, seq_len, k_local, hidden, a, w, partial, out_dtype, stream) -> int:
@@ -221,6 +230,25 @@ def agmm_chunked(shards, x_gathered, w, y, *, n_chunks: int, rank: int = 0, comp
                             _dev_ptr(w, torch.bfloat16, "w", (K, N)),
                             _dev_ptr(y, y.dtype, "y", (M, N)), _out_dtype(y), _stream(compute),
                             None if copy is None else _stream(copy), int(bool(timing))))
+
+
+def reduce_norm_agmm_chunked(partials, residual, gamma, eps: float, shards, x_gathered, w, y, *, n_chunks: int,
+                             rank: int = 0, residual_out=None, compute=None, ctx: Optional[Context] = None) -> None:
+    """Boundary epilogue of this rank's rows into its slot of x_gathered, then agmm_chunked, with the
+    peers' staging started before the epilogue (see include/sptl.h).  shards[rank] is ignored."""
+    torch = _torch()
+    tp = len(shards)
+    M, K = x_gathered.shape
+    N = w.shape[1]
+    rows = M // tp if tp else 0
+    ps = [_dev_ptr(p, torch.bfloat16, f"partials[{i}]", (rows, K)) for i, p in enumerate(partials)]
+    src = [None if q == rank else _dev_ptr(s, torch.bfloat16, f"shards[{q}]", (rows, K)) for q, s in enumerate(shards)]
+    ro = None if residual_out is None else _dev_ptr(residual_out, torch.bfloat16, "residual_out", (rows, K))
+    _check(raw_reduce_norm_agmm_chunked(_h(ctx), len(ps), ps, _dev_ptr(residual, torch.bfloat16, "residual", (rows, K)),
+                                        _dev_ptr(gamma, torch.bfloat16, "gamma", (K,)), float(eps), ro, M, K, N, tp,
+                                        n_chunks, rank, src, _dev_ptr(x_gathered, torch.bfloat16, "x_gathered"),
+                                        _dev_ptr(w, torch.bfloat16, "w", (K, N)), _dev_ptr(y, y.dtype, "y", (M, N)),
+                                        _out_dtype(y), _stream(compute)))
 
 
 def gemm_partial(a, w, partial, *, stream=None, ctx: Optional[Context] = None) -> None:

@@ -134,3 +134,18 @@ def test_agmm_noalloc_validation(sptl, kw, status):
     d.update(kw)
     assert sptl.raw_agmm_chunked_noalloc(**d) == status, sptl.last_error()
     assert "agmm_chunked_noalloc" in sptl.last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(shard_src=None), 1), (dict(x_gathered=None), 1), (dict(residual=None), 1), (dict(gamma=None), 1),
+    (dict(tp=0), 6), (dict(rank=2), 6), (dict(n_partials=17), 6), (dict(partials=None), 1),
+    (dict(partials=[A, None]), 1), (dict(eps=-1.0), 6), (dict(residual=A + 2), 4), (dict(y_dtype=4), 5),
+    (dict(shard_src=[None, None]), 1),            # the peer's shard is required (own entry is not)
+    (dict(seq_len=301), 3),                       # not a multiple of n_chunks
+])
+def test_boundary_validation(sptl, kw, status):
+    d = dict(ctx=None, n_partials=2, partials=[A, A], residual=A, gamma=A, eps=1e-6, residual_out=None, seq_len=512,
+             hidden=256, n_local=512, tp=2, n_chunks=2, rank=0, shard_src=[None, A + 0x100000], x_gathered=A, w=A,
+             y=A, y_dtype=0, compute=None)
+    d.update(kw)
+    assert sptl.raw_reduce_norm_agmm_chunked(**d) == status, sptl.last_error()

@@ -19,6 +19,7 @@ def bf16_tol(oracle: np.ndarray) -> np.ndarray:
 
 def assert_within(got: np.ndarray, want: np.ndarray, tol: np.ndarray, what: str = "") -> None:
     err = np.abs(got - want)
+    tol = np.broadcast_to(tol, err.shape)
     bad = err > tol
     if bad.any():
         i = np.argwhere(bad)[0]
