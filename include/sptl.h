@@ -232,6 +232,34 @@ int gemm_partial(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden
                  const void *a, const void *w, void *partial, int out_dtype, void *stream);
 
 /*
+ * (2') Row-parallel GEMM with the reduce-scatter's sends overlapped: the mirror of agmm_chunked.
+ *
+ * [AReaL "Potential Solution"]: the partial sums of a row-parallel linear are reduce-scattered
+ * at the end of the sub-layer (each rank keeps the sum over ranks of its own sequence slice);
+ * [MLM "Scope"] leaves that half of the overlap out.  Here the partial is computed slice by
+ * slice in send order (the slices of ranks rank+1, ..., rank+tp-1, then this rank's own), and
+ * each peer's slice is copied out by the SDMA copy engines (striped over all of them) as soon as
+ * its rows are written, while the following slices are computed.
+ *   seq_len, k_local, hidden, a, w: as gemm_partial; seq_len % tp == 0; slice q is rows
+ *            [q seq_len/tp, (q+1) seq_len/tp) of partial
+ *   partial  [seq_len, hidden] bf16: this rank's whole partial sum, the same bits as gemm_partial
+ *   dst      host array [tp] of device pointers: dst[q] ([seq_len/tp, hidden] bf16) receives slice q
+ *            for q != rank (it stands in for rank q's receive buffer); dst[rank] is not used and
+ *            may be NULL.  A dst[q] that is slice q of partial itself is left as is.
+ *   tp in [1, 64].  One GEMM launch on `compute`; the launch ends after every copy has landed, so
+ *   later work on `compute` sees partial and every dst complete.  The copies are released by the
+ *   context's worker thread as the kernel reports each slice done.  Slices of a height that fits
+ *   no chunk tile (a multiple of 128 rows), or a context without copy engines: the GEMM, then
+ *   the copies, on `compute`.
+ * Errors: SPTL_E_NULL (a, w, partial, dst or a peer's dst[q] NULL), SPTL_E_RANGE (tp, rank),
+ * SPTL_E_SHAPE / SPTL_E_DIVISIBILITY (sizes, seq_len % tp), SPTL_E_ALIGN (any pointer not 16-byte
+ * aligned), SPTL_E_ASYNC (an earlier call's copies timed out and are still draining); nothing is
+ * launched then.  The kernel's bounded wait for the copies reports through sptl_ctx_check.
+ */
+int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden, int tp, int rank,
+                    const void *a, const void *w, void *partial, void *const *dst, void *compute);
+
+/*
  * (3) Fused reduce + residual + RMSNorm at a sub-layer boundary.
  *
  * [AReaL "Potential Solution", sub-layer boundary overlap]: between a sub-layer's

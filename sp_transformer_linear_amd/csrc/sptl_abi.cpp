@@ -670,6 +670,104 @@ int gemm_partial(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden
     return SPTL_OK;
 }
 
+int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden, int tp, int rank,
+                    const void *a, const void *w, void *partial, void *const *dst, void *compute) {
+    static const char *fn = "gemm_rs_chunked";
+    if (!a || !w || !partial || !dst) return fail(SPTL_E_NULL, "%s: NULL pointer argument", fn);
+    if (tp < 1 || tp > sptl::kMaxPlanChunks)
+        return fail(SPTL_E_RANGE, "%s: tp=%d not in [1, %d]", fn, tp, sptl::kMaxPlanChunks);
+    if (rank < 0 || rank >= tp) return fail(SPTL_E_RANGE, "%s: rank=%d not in [0, %d)", fn, rank, tp);
+    if (seq_len < 0) return fail(SPTL_E_SHAPE, "%s: seq_len=%lld", fn, (long long)seq_len);
+    if (seq_len % tp) return fail(SPTL_E_DIVISIBILITY, "%s: seq_len=%lld not a multiple of tp=%d", fn, (long long)seq_len, tp);
+    const int64_t R = seq_len / tp;
+    if (int rc = check_gemm_dims(R, k_local, hidden)) return rc;
+    for (int q = 0; q < tp; ++q) {
+        if (q != rank && !dst[q]) return fail(SPTL_E_NULL, "%s: dst[%d] is NULL", fn, q);
+        if (dst[q] && !aligned16(dst[q])) return fail(SPTL_E_ALIGN, "%s: dst[%d] not 16-byte aligned", fn, q);
+    }
+    if (!aligned16(a) || !aligned16(w) || !aligned16(partial))
+        return fail(SPTL_E_ALIGN, "%s: a, w and partial must be 16-byte aligned", fn);
+    if (seq_len == 0) return SPTL_OK;
+    if (int rc = resolve_ctx(ctx)) return rc;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    hipStream_t cs = static_cast<hipStream_t>(compute);
+    auto *pb = static_cast<uint16_t *>(partial);
+    const size_t slice_elems = (size_t)R * (size_t)hidden;
+    const size_t slice_bytes = slice_elems * 2;
+    sptl::GemmProblem gp{};
+    gp.a = static_cast<const uint16_t *>(a);
+    gp.b = static_cast<const uint16_t *>(w);
+    gp.c = partial;
+    gp.m = seq_len;
+    gp.n = hidden;
+    gp.k = k_local;
+    gp.lda = k_local;
+    gp.ldb = hidden;
+    gp.ldc = hidden;
+    gp.c_f32 = false;
+    if (!staged_path(ctx, R, tp)) {
+        // no copy engines (or slices of no chunk-tile height): the GEMM, then the copies
+        SPTL_HIP(sptl::launch_gemm(gp, cs));
+        for (int q = 0; q < tp; ++q)
+            if (q != rank && dst[q] != pb + (size_t)q * slice_elems)
+                SPTL_HIP(hipMemcpyAsync(dst[q], pb + (size_t)q * slice_elems, slice_bytes, hipMemcpyDeviceToDeviceNoCU, cs));
+        return SPTL_OK;
+    }
+    // slices in send order: the peers' r + 1, r + 2, ... (copied out while later slices compute),
+    // this rank's own last
+    std::vector<sptl::CopyPiece> copies;
+    sptl::ChunkPlan &plan = gp.plan;
+    int64_t slice_tiles[sptl::kMaxPlanChunks] = {};
+    for (int d = 1; d <= tp; ++d) {
+        const int q = (rank + d) % tp;
+        plan.order[d - 1] = q;
+        if (q == rank || dst[q] == pb + (size_t)q * slice_elems) continue;  // stays in place
+        copies.push_back({dst[q], pb + (size_t)q * slice_elems, slice_bytes, q});
+    }
+    plan.chunk_rows = (int)R;
+    plan.n_chunks = tp;
+    plan.own_first = 0;
+    plan.own_count = 0;
+    plan.own_a = gp.a;
+    plan.err = ctx->err_dev;
+    plan.timeout_ticks = (uint64_t)ctx->wallclock_khz * ctx->wait_timeout_us / 1000u;
+    plan.copy_out = true;
+    std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies, 1, 1);
+    const int64_t wgs = sptl::gemm_workgroups(gp);  // the chunk-ordered launch: equal tiles per slice
+    for (const sptl::CopyPiece &pc : pieces) slice_tiles[pc.chunk] = wgs / tp;
+    sptl::StageCall call;
+    std::string why;
+    if (int rc = sptl::stager_begin(ctx->stager, pieces, wgs, &call, &why, nullptr, slice_tiles))
+        return fail(rc == -2 ? SPTL_E_ASYNC : SPTL_E_HIP, "%s: %s", fn, why.c_str());
+    for (int c = 0; c < tp; ++c) {
+        plan.ready[c] = call.ready[c];  // copy-out: the slice's outgoing copies
+        plan.ready_n[c] = call.ready_n[c];
+        plan.slice_last[c] = call.slice_last[c];
+    }
+    plan.slice_ready = call.slice_ready;
+    plan.slice_count = call.slice_count;
+    plan.join = nullptr;
+    plan.join_n = 0;
+    plan.flags = nullptr;
+    plan.epoch = call.epoch;
+    plan.flag_epoch = call.epoch;
+    plan.finished = call.finished;
+    plan.timedout = call.timedout;
+    plan.wg_count = call.wg_count;
+    for (int gi = 0; gi < sptl::kEndGroups; ++gi) plan.grp_last[gi] = call.grp_last[gi];
+    plan.all_last = call.all_last;
+    hipError_t he = hipEventRecord(call.fork, cs);
+    if (he == hipSuccess) he = sptl::launch_gemm(gp, cs);
+    if (he != hipSuccess) {
+        sptl::stager_cancel(ctx->stager, call);
+        return hip_fail(he, "gemm_rs_chunked: kernel launch");
+    }
+    if (sptl::stager_submit(ctx->stager, call, std::move(pieces), &why, true))
+        return fail(SPTL_E_HIP, "%s: %s", fn, why.c_str());
+    return SPTL_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -683,14 +781,6 @@ int check_epilogue_common(const char *fn, int64_t seq_len, int64_t hidden, float
     if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(SPTL_E_RANGE, "%s: eps must be finite and >= 0", fn);
     return SPTL_OK;
 }
-
-}  // namespace
-
-extern "C" {
-
-}  // extern "C"
-
-namespace {
 
 // Validates the arguments of a reduce + residual + RMSNorm over `rows` rows and fills *ep
 // (everything but the launch).  fn names the calling entry point.

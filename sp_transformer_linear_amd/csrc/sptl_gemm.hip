@@ -120,7 +120,7 @@ static_assert(kFlagReplicas <= 64, "one lane per flag replica");
 
 __device__ __forceinline__ void wait_chunk(const ChunkPlan &plan, int chunk, int bid) {
     const int64_t *const *words = plan.ready[chunk];
-    if (!words) return;
+    if (!words || plan.copy_out) return;
     const int n = plan.ready_n[chunk];
     if (!plan.flags) return wait_ready(words, n, plan);
     const int lane = threadIdx.x & 63;
@@ -146,7 +146,7 @@ __device__ __forceinline__ void wait_chunk(const ChunkPlan &plan, int chunk, int
 // copied rows are visible to the workgroup's later loads (after a barrier).
 __device__ __forceinline__ bool chunk_ready_now(const ChunkPlan &plan, int chunk, int bid) {
     const int64_t *const *words = plan.ready[chunk];
-    if (!words) return true;
+    if (!words || plan.copy_out) return true;
     const int n = plan.ready_n[chunk];
     bool ok;
     if (plan.flags &&
@@ -298,6 +298,23 @@ __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin 
 // tile.
 template <bool CHUNKED>
 __device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrigin &o, int bid) {
+    if (CHUNKED && p.plan.copy_out && p.plan.ready[o.chunk]) {
+        // A slice that is copied out: every wave waits until its stores of the tile have reached
+        // the L2 (vmcnt 0: the barrier's workgroup-scope fence does not wait for them), then
+        // after the barrier the first thread writes the XCD's L2 back (system-scope release: the
+        // copy engines read memory, not the L2) and counts the tile; the slice's last tile
+        // releases its copies.
+        const ChunkPlan &plan = p.plan;
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0); expcnt, lgkmcnt not waited
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            __atomic_thread_fence(__ATOMIC_RELEASE);
+            if (__hip_atomic_fetch_add(plan.slice_count + (size_t)o.chunk * kEndLine, 1ull, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == plan.slice_last[o.chunk])
+                __hip_atomic_store(plan.slice_ready + 16 * (size_t)o.chunk, plan.epoch, __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
     if (CHUNKED && threadIdx.x < 64) {
         const ChunkPlan &plan = p.plan;
         const int chunk = o.chunk;
@@ -321,6 +338,8 @@ __device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrig
         }
         if (__shfl(last, 0, 64)) {
             wait_ready(plan.join, plan.join_n, plan);
+            if (plan.copy_out)
+                for (int c = 0; c < plan.n_chunks; ++c) wait_ready(plan.ready[c], plan.ready_n[c], plan);
             if (threadIdx.x == 0)
                 __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
         }

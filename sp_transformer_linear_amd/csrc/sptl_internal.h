@@ -51,6 +51,16 @@ struct ChunkPlan {
     uint64_t grp_last[kEndGroups];           // group counter value seen by a group's last workgroup
     uint64_t all_last;                       // final counter value seen by the last group
     uint64_t *ts;                            // optional per-chunk timestamps (see below)
+    // Copy-out mode (the reduce-scatter mirror): the chunks are output slices and no tile waits
+    // for input.  ready[c] then lists the completion words of slice c's outgoing copies (null: the
+    // slice stays): the slice's tiles count themselves in slice_count (line c, kEndLine words),
+    // each after making its rows visible to the copy engines, and the last of them (it sees
+    // slice_last[c]) stores epoch to slice_ready[16 c] (pinned host memory, where the copies are
+    // released from); the launch's last workgroup waits for every copy before reporting the end.
+    bool copy_out;
+    uint64_t *slice_ready;
+    uint64_t *slice_count;
+    uint64_t slice_last[kMaxPlanChunks];
 };
 // Waiting: a workgroup of chunk c polls its replica of c's landed flag about every
 // microsecond and, once every 16 polls (phase set by its index), c's completion words

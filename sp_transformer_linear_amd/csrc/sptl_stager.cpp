@@ -73,6 +73,9 @@ constexpr int kCountWords = kSetCountWords * kStageSets;
 constexpr double kReuseWaitSeconds = 30.0;  // longest a call waits for a set to come free
 
 constexpr int kSetSignals = (kMaxPlanChunks + 1) * kMaxPieces;
+// slice-ready words (16 apart) and slice counters (kEndLine apart) of copy-out calls, per set
+constexpr int kSliceSetWords = kMaxPlanChunks * (kEndLine > 16 ? kEndLine : 16);
+constexpr int kSliceWords = kSliceSetWords * kStageSets;
 
 struct SignalSet {
     hsa_signal_t sig[kMaxPlanChunks + 1][kMaxPieces] = {};
@@ -80,6 +83,7 @@ struct SignalSet {
     hipEvent_t fork = nullptr;
     uint64_t epoch = 0;       // of the last call begun on the set (0: never used)
     int armed[kMaxPlanChunks + 1] = {};   // pieces per chunk armed by that call
+    uint64_t slice_total[kMaxPlanChunks] = {};  // copy-out tiles counted per slice, all calls
     std::atomic<uint64_t> handled{0};     // epoch of the last job the worker has handled
     uint64_t grp_total[kEndGroups] = {};  // workgroups counted per group, all calls on the set
     uint64_t all_total = 0;               // groups counted, all calls on the set
@@ -90,7 +94,9 @@ struct Job {
     uint64_t epoch;
     hipEvent_t fork;
     std::vector<CopyPiece> pieces;
+    const volatile uint64_t *gates = nullptr;  // copy-out: chunk c's pieces wait for gates[16 c] == epoch
 };
+constexpr double kGateWaitSeconds = 10.0;
 
 // Spins (with pauses, yielding now and then) until *word == value; false after `seconds`.
 bool spin_until(const volatile uint64_t *word, uint64_t value, double seconds) {
@@ -125,6 +131,8 @@ class SdmaStager {
     void *scratch = nullptr;        // 8 KB for the engine checks
     uint64_t *host_words = nullptr; // pinned, kHostWords
     uint64_t *counts = nullptr;     // device, kCountWords
+    uint64_t *slice_words = nullptr;   // pinned: per set, kMaxPlanChunks slice-ready words 16 apart
+    uint64_t *slice_counts = nullptr;  // device: per set, kMaxPlanChunks slice counters kEndLine apart
 
     volatile uint64_t *finished(int set) const { return host_words + 16 * set; }
     volatile uint64_t *timedout(int set) const { return host_words + 16 * set + 8; }
@@ -218,12 +226,16 @@ class SdmaStager {
         const auto tf = std::chrono::steady_clock::now();
         int last_chunk = -2;
         for (const CopyPiece &pc : job.pieces) {
-            if (trace && pc.chunk != last_chunk) {
+            if (ok && job.gates && pc.chunk != last_chunk) {
+                // copy-out: the slice's rows are written and visible once the kernel says so
+                const volatile uint64_t *g = job.gates + 16 * (size_t)pc.chunk;
+                ok = spin_until(g, job.epoch, kGateWaitSeconds);
+            }
+            if (trace && pc.chunk != last_chunk)
                 fprintf(stderr, "[stager] chunk %d submit at +%.1f us after fork (fork wait %.1f us)\n", pc.chunk,
                         std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - tf).count(),
                         std::chrono::duration<double, std::micro>(tf - tq).count());
-                last_chunk = pc.chunk;
-            }
+            last_chunk = pc.chunk;
             const uint32_t eng = engines[(size_t)pc.engine % engines.size()];
             if (ok)
                 ok = hsa_amd_memory_async_copy_on_engine(pc.dst, agent, pc.src, agent, pc.bytes, 0, nullptr,
@@ -288,6 +300,10 @@ SdmaStager *stager_create(int device, std::string *err) {
         hipMemset(s->counts, 0, kCountWords * sizeof(uint64_t)) != hipSuccess ||
         hipHostMalloc(&s->host_words, kHostWords * sizeof(uint64_t), hipHostMallocMapped | hipHostMallocCoherent) !=
             hipSuccess ||
+        hipHostMalloc(&s->slice_words, kSliceWords * sizeof(uint64_t), hipHostMallocMapped | hipHostMallocCoherent) !=
+            hipSuccess ||
+        hipMalloc(&s->slice_counts, kSliceWords * sizeof(uint64_t)) != hipSuccess ||
+        hipMemset(s->slice_counts, 0, kSliceWords * sizeof(uint64_t)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         *err = "cannot allocate the engine-check buffer, counters or pinned progress words";
         (void)hipGetLastError();
@@ -330,10 +346,12 @@ SdmaStager *stager_create(int device, std::string *err) {
     bool ok = true;
     std::string why;
     for (int i = 0; i < kHostWords; ++i) s->host_words[i] = 0;
+    for (int i = 0; i < kSliceWords; ++i) s->slice_words[i] = 0;
     {
         // the kernels write these words through the device address of the pinned block
-        void *dp = nullptr;
-        if (hipHostGetDevicePointer(&dp, s->host_words, 0) != hipSuccess || dp != (void *)s->host_words) {
+        void *dp = nullptr, *dq = nullptr;
+        if (hipHostGetDevicePointer(&dp, s->host_words, 0) != hipSuccess || dp != (void *)s->host_words ||
+            hipHostGetDevicePointer(&dq, s->slice_words, 0) != hipSuccess || dq != (void *)s->slice_words) {
             *err = "pinned progress words have no identical device address";
             (void)hipGetLastError();
             stager_destroy(s);
@@ -419,6 +437,8 @@ void stager_destroy(SdmaStager *s) {
         if (s->scratch) (void)hipFree(s->scratch);
         if (s->counts) (void)hipFree(s->counts);
         if (s->host_words) (void)hipHostFree(s->host_words);
+        if (s->slice_words) (void)hipHostFree(s->slice_words);
+        if (s->slice_counts) (void)hipFree(s->slice_counts);
         delete s;
         hsa_shut_down();
     }
@@ -442,7 +462,7 @@ int stager_wait_idle(SdmaStager *s) {
     return 0;
 }
 
-std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies, int lead) {
+std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies, int lead, int group_in) {
     // tuning knob: SPTL_SDMA_SPLIT=p stripes a chunk into up to p pieces per engine
     static const size_t split = [] {
         const char *e = getenv("SPTL_SDMA_SPLIT");
@@ -459,7 +479,9 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
     pc.reserve(copies.size());
     for (const CopyPiece &c : copies) pc.push_back({c.bytes, c.chunk});
     const int engines = (int)s->engines.size();
-    const int group = forced_group ? forced_group : later_group(engines, copies.empty() ? 0 : copies[0].bytes);
+    const int group = group_in > 0     ? group_in
+                      : forced_group ? forced_group
+                                     : later_group(engines, copies.empty() ? 0 : copies[0].bytes);
     std::vector<CopyPiece> out;
     for (const PlanPiece &q : plan_pieces(pc, lead, engines, split, group)) {
         const CopyPiece &c = copies[(size_t)q.copy];
@@ -481,7 +503,7 @@ bool stager_take_timeouts(SdmaStager *s) {
 }
 
 int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t workgroups, StageCall *out,
-                 std::string *err, uint64_t *fresh_counts) {
+                 std::string *err, uint64_t *fresh_counts, const int64_t *slice_tiles) {
     int count[kMaxPlanChunks + 1] = {};
     for (const CopyPiece &p : pieces) {
         if (p.chunk < 0 || p.chunk > kMaxPlanChunks || p.piece != count[p.chunk] || p.piece >= kMaxPieces) {
@@ -541,14 +563,24 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
     out->all_first = ss.all_total;
     out->all_last = all_base + (uint64_t)groups - 1;
     if (!fresh_counts) ss.all_total += (uint64_t)groups;
+    // copy-out slices: cumulative tile counts of the set, like the end counters
+    out->slice_ready = s->slice_words + (size_t)kSliceSetWords * set;
+    out->slice_count = s->slice_counts + (size_t)kSliceSetWords * set;
+    for (int c = 0; c < kMaxPlanChunks; ++c) {
+        const int64_t t = slice_tiles ? slice_tiles[c] : 0;
+        out->slice_first[c] = ss.slice_total[c];
+        out->slice_last[c] = t > 0 ? ss.slice_total[c] + (uint64_t)t - 1 : ~0ull;
+        ss.slice_total[c] += (uint64_t)(t > 0 ? t : 0);
+    }
     return 0;
 }
 
-int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> pieces, std::string *err) {
+int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> pieces, std::string *err,
+                  bool gated) {
     (void)err;
     {
         std::lock_guard<std::mutex> lk(s->mu);
-        s->queue.push_back(Job{call.set, call.epoch, call.fork, std::move(pieces)});
+        s->queue.push_back(Job{call.set, call.epoch, call.fork, std::move(pieces), gated ? call.slice_ready : nullptr});
         s->queued.fetch_add(1, std::memory_order_release);
     }
     s->cv.notify_one();
@@ -561,6 +593,7 @@ void stager_cancel(SdmaStager *s, const StageCall &call) {
     SignalSet &ss = s->sets[call.set];
     for (int g = 0; g < kEndGroups; ++g) ss.grp_total[g] = call.grp_first[g];
     ss.all_total = call.all_first;
+    for (int c = 0; c < kMaxPlanChunks; ++c) ss.slice_total[c] = call.slice_first[c];
     for (int c = 0; c <= kMaxPlanChunks; ++c) ss.armed[c] = 0;
     ss.handled.store(call.epoch, std::memory_order_release);
     __atomic_store_n(s->host_words + 16 * call.set, call.epoch, __ATOMIC_RELEASE);

@@ -54,6 +54,11 @@ struct StageCall {
     uint64_t all_last = 0;
     uint64_t grp_first[kEndGroups] = {};  // the set's totals before this call (for a cancel)
     uint64_t all_first = 0;
+    // copy-out calls (slice_tiles given to stager_begin): see ChunkPlan
+    uint64_t *slice_ready = nullptr;
+    uint64_t *slice_count = nullptr;
+    uint64_t slice_last[kMaxPlanChunks] = {};
+    uint64_t slice_first[kMaxPlanChunks] = {};
 };
 
 class SdmaStager;
@@ -66,25 +71,31 @@ int stager_engine_count(const SdmaStager *s);
 // Splits the chunk copies into pieces with an engine each (plan_pieces, sptl_plan.h) and returns
 // them in submission order with their chunk and piece ids, which is what stager_begin and
 // stager_submit expect; each engine takes its pieces in submission order.
-std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies, int lead = 1);
+// group > 0 overrides the grouping of the later copies (1: each striped over all engines).
+std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies, int lead = 1,
+                                   int group = 0);
 
 // Reserves a completion-signal set for one call whose consuming kernel has `workgroups`
-// workgroups, and arms it with the number of pieces per chunk.  Blocks (bounded) while the
+// workgroups, and arms it with the number of pieces per chunk.  slice_tiles (copy-out calls):
+// per chunk, the tiles of the slice whose copies the kernel releases (0: not copied).  Blocks (bounded) while the
 // set's previous call is still running and, if a wait of that call timed out, until its copies
 // have completed.  Returns 0, -1 (the previous call did not finish; bad pieces) or -2 (the
 // copies of a timed-out call did not complete within the bound).  fresh_counts: null to count
 // the kernel's workgroups in the set's own cumulative counters, or kEndCounters lines of
 // counters (kEndLine words apart) that the caller zeroes on the stream before the launch.
 int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t workgroups, StageCall *out,
-                 std::string *err, uint64_t *fresh_counts = nullptr);
+                 std::string *err, uint64_t *fresh_counts = nullptr, const int64_t *slice_tiles = nullptr);
 
 // Whether a call whose chunk wait timed out has been seen (on reuse of its set, on an idle wait or
 // now, for calls that have ended) since the last time this returned true.
 bool stager_take_timeouts(SdmaStager *s);
 
 // Queues the pieces; a worker thread submits them to the engines as soon as `call.fork`
-// has completed.
-int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> pieces, std::string *err);
+// has completed.  gated: a copy-out call, whose pieces of chunk c are submitted only once the
+// kernel has stored the call's epoch to call.slice_ready[16 c] (bounded wait: after 10 s the
+// stager fails and releases the call's waiters).
+int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> pieces, std::string *err,
+                  bool gated = false);
 
 // Gives back a set reserved by stager_begin whose kernel was never launched.
 void stager_cancel(SdmaStager *s, const StageCall &call);

@@ -51,6 +51,7 @@ _SIGS = {
     "reduce_norm_agmm_chunked": ([_vp, _int, _ptrs, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i64, _int, _int,
                                   _int, _ptrs, _vp, _vp, _vp, _int, _vp], _int),
     "gemm_partial": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp], _int),
+    "gemm_rs_chunked": ([_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _ptrs, _vp], _int),
     "reduce_residual_rmsnorm": ([_vp, _i64, _i64, _int, _ptrs, _vp, _vp, ctypes.c_float, _vp, _vp,
                                  _vp], _int),
     "dtp_accumulate": ([_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _ptrs, _vp, ctypes.c_float, _vp,
@@ -102,6 +103,10 @@ def raw_agmm_chunked_noalloc(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, 
                              y, y_dtype, compute) -> int:
     return _lib.agmm_chunked_noalloc(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, _ptr_array(shard_src),
                                      x_gathered, w, y, y_dtype, compute)
+
+
+def raw_gemm_rs_chunked(ctx, seq_len, k_local, hidden, tp, rank, a, w, partial, dst, compute) -> int:
+    return _lib.gemm_rs_chunked(ctx, seq_len, k_local, hidden, tp, rank, a, w, partial, _ptr_array(dst), compute)
 
 
 def raw_reduce_norm_agmm_chunked(ctx, n_partials, partials, residual, gamma, eps, residual_out, seq_len, hidden,
@@ -249,6 +254,21 @@ def reduce_norm_agmm_chunked(partials, residual, gamma, eps: float, shards, x_ga
                                         n_chunks, rank, src, _dev_ptr(x_gathered, torch.bfloat16, "x_gathered"),
                                         _dev_ptr(w, torch.bfloat16, "w", (K, N)), _dev_ptr(y, y.dtype, "y", (M, N)),
                                         _out_dtype(y), _stream(compute)))
+
+
+def gemm_rs_chunked(a, w, partial, dst, *, rank: int = 0, stream=None, ctx: Optional[Context] = None) -> None:
+    """partial = a @ w, slice by slice in send order, each peer slice q copied to dst[q] by the copy
+    engines while later slices compute (dst[rank] is ignored; see include/sptl.h)."""
+    torch = _torch()
+    M, K = a.shape
+    H = w.shape[1]
+    tp = len(dst)
+    rows = M // tp if tp else 0
+    d = [None if (q == rank or t is None) else _dev_ptr(t, torch.bfloat16, f"dst[{q}]", (rows, H))
+         for q, t in enumerate(dst)]
+    _check(raw_gemm_rs_chunked(_h(ctx), M, K, H, tp, rank, _dev_ptr(a, torch.bfloat16, "a"),
+                               _dev_ptr(w, torch.bfloat16, "w", (K, H)),
+                               _dev_ptr(partial, torch.bfloat16, "partial", (M, H)), d, _stream(stream)))
 
 
 def gemm_partial(a, w, partial, *, stream=None, ctx: Optional[Context] = None) -> None:

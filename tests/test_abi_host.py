@@ -149,3 +149,15 @@ def test_boundary_validation(sptl, kw, status):
              y=A, y_dtype=0, compute=None)
     d.update(kw)
     assert sptl.raw_reduce_norm_agmm_chunked(**d) == status, sptl.last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=None), 1), (dict(w=None), 1), (dict(partial=None), 1), (dict(dst=None), 1),
+    (dict(dst=[None, None]), 1), (dict(tp=0), 6), (dict(tp=65), 6), (dict(rank=2), 6), (dict(seq_len=-2), 2),
+    (dict(seq_len=513), 3), (dict(hidden=12), 3), (dict(partial=A + 4), 4), (dict(dst=[None, A + 8]), 4),
+])
+def test_gemm_rs_validation(sptl, kw, status):
+    d = dict(ctx=None, seq_len=512, k_local=256, hidden=256, tp=2, rank=0, a=A, w=A, partial=A, dst=[None, A],
+             compute=None)
+    d.update(kw)
+    assert sptl.raw_gemm_rs_chunked(**d) == status, sptl.last_error()
