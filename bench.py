@@ -309,9 +309,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def agmm(T, w, y, timing=False, n_chunks=None, shards=None):
+    def agmm(T, w, y, timing=False, n_chunks=None, shards=None, c=None):
         sptl.agmm_chunked(shards or T.shards, T.xg, w, y, n_chunks=n_chunks or T.n_chunks, rank=0, compute=cs,
-                          timing=timing, ctx=ctx)
+                          timing=timing, ctx=c or ctx)
 
     L.n_chunks = wl.n_chunks
 
@@ -532,6 +532,151 @@ def main():
                     "bitwise_equal": same}
         del y_own, h_own, y_alias, y_fused, xg_fused
 
+    # Reduce-scatter mirror: the row GEMM with each finished peer slice copied out by the copy
+    # engines under the later slices (gemm_rs_chunked), against the plain GEMM and against the
+    # GEMM followed by the same copies (a second context in the serial copy mode, which runs them
+    # after the GEMM on the stream).  Timed in triples so all three see the same clock; the
+    # copies' hidden share is 1 - (T_rs - T_gemm) / (T_serial - T_gemm), per triple.
+    ctx_serial = sptl.Context(0)
+    ctx_serial.set_copy_mode("serial")
+
+    def reduce_scatter(T, reps):
+        M_, H_ = T.own.shape
+        tp_ = len(T.shards)
+        R_ = M_ // tp_
+        dst = [None] + [torch.empty((R_, H_), dtype=torch.bfloat16, device=dev) for _ in range(tp_ - 1)]
+        part = torch.empty_like(T.own)
+
+        def rs(c):
+            sptl.gemm_rs_chunked(T.a_row, T.w_row, part, dst, rank=0, stream=cs, ctx=c)
+
+        for _ in range(3):
+            rs(ctx)
+            rs(ctx_serial)
+        trip = []
+        for _ in range(3 * reps):
+            e = [ev() for _ in range(4)]
+            e[0].record(cs)
+            rs(ctx)
+            e[1].record(cs)
+            gemm_p(T)
+            e[2].record(cs)
+            rs(ctx_serial)
+            e[3].record(cs)
+            trip.append(e)
+        torch.cuda.synchronize()
+        ctx.check()
+        ctx_serial.check()
+        d = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in trip])
+        rs(ctx)
+        torch.cuda.synchronize()
+        ctx.check()
+        same = bool(torch.equal(part.view(torch.int16), T.own.view(torch.int16)) and all(
+            torch.equal(dst[q].view(torch.int16), part[q * R_:(q + 1) * R_].view(torch.int16)) for q in range(1, tp_)))
+        t_rs, t_g, t_ser = (float(np.median(d[:, i])) for i in range(3))
+        t_copy = float(np.median(d[:, 2] - d[:, 1]))
+        exposed = max(0.0, float(np.median(d[:, 0] - d[:, 1])))
+        nbytes = (tp_ - 1) * R_ * H_ * 2
+        fl = 2.0 * M_ * T.a_row.shape[1] * H_
+        del dst, part
+        return {"ms_rs": round(t_rs, 4), "ms_gemm_partial": round(t_g, 4), "ms_gemm_then_copies": round(t_ser, 4),
+                "rs_tflops": round(fl / (t_rs * 1e-3) / 1e12, 2),
+                "copy_bytes": nbytes, "copy_alone_ms": round(t_copy, 4),
+                "copy_alone_GBps": None if t_copy <= 0 else round(nbytes / (t_copy * 1e-3) / 1e9, 1),
+                "copy_exposed_ms": round(exposed, 4),
+                "copy_hidden_frac": None if t_copy <= 0 else round(max(0.0, 1.0 - exposed / t_copy), 4),
+                "bitwise_equal_gemm_partial": same}
+
+    rs_main = reduce_scatter(L, reps) if L.a_row.shape[0] % wl.tp == 0 else None
+
+    # Copy modes ("Add forward all-gather overlap", "Observations": a gather on the compute units
+    # contends with the GEMM; the copy-engine gather does not).  The same agmm call with its
+    # copies as per-chunk SDMA copies, as copy kernels on the compute units (a grid sized to the
+    # copy, and 48 workgroups, about the share of the chip a ring gather's CTAs take), and with no
+    # overlap at all; each timed in pairs with the GEMM on pre-gathered rows, like the staged call.
+    # exposed = median(T_call - T_gemm); hidden share = 1 - exposed / (T_serial - T_gemm).
+    def copy_mode_study(T, w, reps, n_chunks):
+        M_, K_ = T.xg.shape
+        N_ = w.shape[1]
+        y_tmp = torch.empty((M_, N_), dtype=torch.bfloat16, device=dev)
+        fl = 2.0 * M_ * K_ * N_
+        modes = [("staged", 0, ctx), ("events", 0, ctx_serial), ("blit", 0, ctx_serial), ("blit", 48, ctx_serial),
+                 ("serial", 0, ctx_serial)]
+        d = {}
+        for m, wg, c in modes:
+            if c is ctx_serial:
+                c.set_copy_mode(m, wg)
+            for _ in range(3):
+                agmm(T, w, T.y_col, n_chunks=n_chunks, c=c)
+            pairs = []
+            for _ in range(2 * reps):
+                e = [ev() for _ in range(3)]
+                e[0].record(cs)
+                agmm(T, w, T.y_col, n_chunks=n_chunks, c=c)
+                e[1].record(cs)
+                sptl.gemm_partial(T.xg, w, y_tmp, stream=cs, ctx=ctx)
+                e[2].record(cs)
+                pairs.append(e)
+            torch.cuda.synchronize()
+            c.check()
+            d[(m, wg)] = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in pairs])
+        ctx_serial.set_copy_mode("serial")
+        del y_tmp
+        t_copy = float(np.median(d[("serial", 0)][:, 0] - d[("serial", 0)][:, 1]))
+        out_ = {"copy_serial_ms": round(t_copy, 4)}
+        for (m, wg), a in d.items():
+            ex = max(0.0, float(np.median(a[:, 0] - a[:, 1])))
+            key = m if not wg else f"{m}_{wg}wg"
+            out_[key] = {"ms": round(float(np.median(a[:, 0])), 4),
+                         "tflops": round(fl / (float(np.median(a[:, 0])) * 1e-3) / 1e12, 2),
+                         "exposed_ms": round(ex, 4),
+                         "hidden_frac_vs_serial_copy": None if t_copy <= 0 or m == "serial"
+                         else round(max(0.0, 1.0 - ex / t_copy), 4)}
+        return out_
+
+    copy_modes = copy_mode_study(L, L.w_col, reps, wl.n_chunks)
+
+    # Launch gaps: one step captured in a HIP graph (on a stream under capture the agmm call takes
+    # the per-chunk event path, whose copies, events and launches a graph holds), replayed, against
+    # the same step run eagerly on the event path and on the default staged path (the timed
+    # region above).  The column GEMM's output must come out with the same bits.
+    y_staged = L.y_col.clone()
+    ctx.set_copy_mode("events")
+    step()  # also creates the context's copy stream before the capture
+    torch.cuda.synchronize()
+    n_l = max(5, args.steps)
+    t0, t1 = ev(), ev()
+    t0.record(cs)
+    for _ in range(n_l):
+        step()
+    t1.record(cs)
+    torch.cuda.synchronize()
+    ctx.check()
+    ms_events = t0.elapsed_time(t1) / n_l
+    ctx.set_copy_mode("staged")
+    cs_eager = cs
+    cap_stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    cs = cap_stream  # the step's calls go to the capturing stream
+    with torch.cuda.graph(graph, stream=cap_stream):
+        step()
+    cs = cs_eager
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0.record(cs)
+    for _ in range(n_l):
+        graph.replay()
+    t1.record(cs)
+    torch.cuda.synchronize()
+    ctx.check()
+    ms_graph = t0.elapsed_time(t1) / n_l
+    launch = {"ms_step_staged_eager": round(ms_step, 4), "ms_step_events_eager": round(ms_events, 4),
+              "ms_step_events_graph": round(ms_graph, 4), "steps": n_l,
+              "y_bitwise_equal": bool(torch.equal(L.y_col.view(torch.int16), y_staged.view(torch.int16)))}
+    del graph, y_staged
+
     def gbs(nbytes, ms):
         return nbytes / (ms * 1e-3) / 1e9
 
@@ -579,9 +724,12 @@ def main():
             **ov,
             "staging_check": staging_check,
             "boundary": boundary,
+            "copy_modes": copy_modes,
+            "launch": launch,
         },
         "gemm_partial": {"tflops": round(gemmp_tflops, 2), "frac_peak": round(gemmp_tflops / PEAK_BF16_TFLOPS, 4),
-                         "ms": round(float(gemmp_ms.mean()), 4), "ms_median": round(float(np.median(gemmp_ms)), 4)},
+                         "ms": round(float(gemmp_ms.mean()), 4), "ms_median": round(float(np.median(gemmp_ms)), 4),
+                         "reduce_scatter": rs_main},
         "reduce_residual_rmsnorm": {
             "GBps": round(gbs(red_bytes, red_ms.mean()), 1), "frac_hbm": round(gbs(red_bytes, red_ms.mean()) / PEAK_HBM_GBS, 4),
             "ms": round(float(red_ms.mean()), 4), "ms_median": round(float(np.median(red_ms)), 4),
@@ -641,6 +789,7 @@ def main():
             "gemm_partial_frac_peak": round(gfl / (ms[1] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "reduce_GBps": round(gbs(rb, ms[2]), 1), "reduce_frac_hbm": round(gbs(rb, ms[2]) / PEAK_HBM_GBS, 4),
             "reduce_GBps_cold": round(gbs(rb, rc), 1), "reduce_frac_hbm_cold": round(gbs(rb, rc) / PEAK_HBM_GBS, 4),
+            "reduce_scatter": reduce_scatter(T, reps) if wo.M % wo.tp == 0 else None,
         }
         del T, fns
         torch.cuda.empty_cache()
@@ -650,6 +799,7 @@ def main():
 
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    ctx_serial.close()
     ctx.close()
     print(json.dumps(out), flush=True)
     return 0

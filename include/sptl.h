@@ -110,6 +110,27 @@ int sptl_ctx_check(sptl_ctx *ctx);
  * early error over a long stall.  SPTL_E_NULL for a NULL ctx, SPTL_E_RANGE otherwise. */
 int sptl_ctx_set_wait_timeout_us(sptl_ctx *ctx, int64_t us);
 
+/* How the staging copies of agmm_chunked (copy == NULL), reduce_norm_agmm_chunked and
+ * gemm_rs_chunked run on ctx.  [MLM "Observations"]: a gather that runs on the compute units
+ * (the ring all-gather's CTAs) contends with the GEMM, while the copy-engine gather does not;
+ * the modes other than the default exist to measure that and to give a capturable path.
+ *   SPTL_COPY_STAGED  the default: the copy engines driven by the context's worker thread,
+ *                     one chunk-ordered GEMM launch that waits for each chunk on the GPU.
+ *                     Falls back to SPTL_COPY_EVENTS where it does not apply (no copy engines,
+ *                     chunk heights that fit no chunk tile, a stream under graph capture).
+ *   SPTL_COPY_EVENTS  one SDMA-class hipMemcpyAsync per chunk on the context's copy stream with
+ *                     an event each, one GEMM launch per chunk after its event.  Under graph
+ *                     capture the copies are recorded as device-to-device copy nodes.
+ *   SPTL_COPY_BLIT    as SPTL_COPY_EVENTS, but each copy is a copy kernel on the compute units
+ *                     (blit_workgroups workgroups of 256 threads; 0 = sized to the copy).
+ *   SPTL_COPY_SERIAL  no overlap: every copy on the compute stream, then one GEMM launch over
+ *                     all rows (agmm_chunked), or the GEMM then the copies (gemm_rs_chunked).
+ * Every mode gives bit-identical outputs.  agmm_chunked_noalloc always stages (the mode does not
+ * apply to it).  SPTL_E_NULL for a NULL ctx; SPTL_E_RANGE for a mode outside the enum or
+ * blit_workgroups outside [0, 65535]. */
+typedef enum { SPTL_COPY_STAGED = 0, SPTL_COPY_EVENTS = 1, SPTL_COPY_BLIT = 2, SPTL_COPY_SERIAL = 3 } sptl_copy_mode;
+int sptl_ctx_set_copy_mode(sptl_ctx *ctx, int mode, int blit_workgroups);
+
 /* Short text naming how agmm_chunked stages chunks on ctx with copy == NULL (copy engines
  * driven directly with a chunk-ordered GEMM, or one copy and one GEMM launch per chunk) and,
  * for the latter, why.  Owned by ctx; valid until ctx is destroyed.  Diagnostic only. */
@@ -146,10 +167,12 @@ const char *sptl_ctx_info(sptl_ctx *ctx);
  *            and later work on it sees x_gathered and y complete.
  *   copy     NULL: staged path (below).  Otherwise a stream for the per-chunk path.
  *   timing   0: no timing; 1: record per-chunk landing and GEMM timestamps, read
- *            afterwards with sptl_agmm_timeline().
- * Staged path (copy == NULL, the default; used when the device's SDMA engines can be driven
- * through HSA, seq_len / n_chunks is a multiple of 128 and n_chunks <= 64; else the
- * per-chunk path runs on the context's own copy stream):
+ *            afterwards with sptl_agmm_timeline().  SPTL_E_UNSUPPORTED with the serial copy
+ *            mode and on a stream under graph capture.
+ * Staged path (copy == NULL and the context's copy mode is SPTL_COPY_STAGED, the default;
+ * used when the device's SDMA engines can be driven through HSA, seq_len / n_chunks is a
+ * multiple of 128, n_chunks <= 64 and `compute` is not under graph capture; else the per-chunk
+ * path runs on the context's own copy stream, see sptl_ctx_set_copy_mode):
  *   - Every peer chunk is split into pieces for the SDMA copy engines.  The peer chunks that
  *     the GEMM's first round of tiles needs (one tile per compute unit, the round sized for
  *     an output at least `hidden` wide) are split together, one piece per engine, so that

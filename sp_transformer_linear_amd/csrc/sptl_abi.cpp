@@ -22,7 +22,9 @@ struct sptl_ctx {
     // SDMA stager (chunk-ordered path); created on first use, null if unavailable
     sptl::SdmaStager *stager = nullptr;
     bool stager_tried = false;
-    bool events_only = false;           // SPTL_STAGING=events: always use the per-chunk event path
+    bool events_only = false;           // SPTL_STAGING=events: no stager, copy mode SPTL_COPY_EVENTS
+    int copy_mode = SPTL_COPY_STAGED;   // sptl_ctx_set_copy_mode
+    int blit_wgs = 0;                   // workgroups of a blit-mode copy (0: sized to the copy)
     std::string staging_info;           // how agmm_chunked stages chunks, and why
     int *err_dev = nullptr;             // device flag set by a timed-out staging wait
     uint64_t *ts_dev = nullptr;         // [3 * kMaxPlanChunks + 1] chunk timestamps
@@ -145,6 +147,7 @@ int create_ctx(sptl_ctx **out, int device) {
             c->cus = cus;
         const char *e = getenv("SPTL_STAGING");
         c->events_only = e && !strcmp(e, "events");
+        if (c->events_only) c->copy_mode = SPTL_COPY_EVENTS;
         // SPTL_WAIT_TIMEOUT_US shortens the bound on a chunk wait (failure-path tests)
         if (const char *t = getenv("SPTL_WAIT_TIMEOUT_US")) {
             const long long us = strtoll(t, nullptr, 10);
@@ -206,10 +209,27 @@ int check_gemm_dims(int64_t m, int64_t k, int64_t n) {
     return SPTL_OK;
 }
 
-// Whether the chunk-ordered path (SDMA stager + one chunk-ordered GEMM) can serve this call.
-bool staged_path(sptl_ctx *ctx, int64_t rows_c, int n_chunks) {
-    if (ctx->events_only || n_chunks > sptl::kMaxPlanChunks || !sptl::chunk_tile_rows(rows_c)) return false;
-    return ctx->stager && !sptl::stager_failed(ctx->stager);
+// Whether stream s is being captured into a graph (a failed query counts as captured: the
+// per-chunk path is correct either way, the staged one needs its worker thread at run time).
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone;
+}
+
+// Whether the chunk-ordered path (SDMA stager + one chunk-ordered GEMM) can serve this call on
+// compute stream cs.
+bool staged_path(sptl_ctx *ctx, int64_t rows_c, int n_chunks, hipStream_t cs) {
+    if (ctx->copy_mode != SPTL_COPY_STAGED || n_chunks > sptl::kMaxPlanChunks || !sptl::chunk_tile_rows(rows_c))
+        return false;
+    return ctx->stager && !sptl::stager_failed(ctx->stager) && !capturing(cs);
+}
+
+// One staging copy of the per-chunk and serial paths on stream s: a copy-engine (SDMA-class)
+// copy, recorded as a plain device-to-device copy node under graph capture, or in blit mode a
+// copy kernel on the compute units.
+hipError_t stage_copy(const sptl_ctx *ctx, void *dst, const void *src, size_t bytes, hipStream_t s, bool cap) {
+    if (ctx->copy_mode == SPTL_COPY_BLIT) return sptl::launch_blit(dst, src, bytes, ctx->blit_wgs, s);
+    return hipMemcpyAsync(dst, src, bytes, cap ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU, s);
 }
 
 // Chunk-ordered agmm: all staging copies go to the SDMA stager (striped over the copy
@@ -347,6 +367,9 @@ int sptl_version(void) { return 100; }
 const char *sptl_ctx_info(sptl_ctx *ctx) {
     if (resolve_ctx(ctx)) return "";
     if (ctx->events_only) return "per-chunk events (forced by SPTL_STAGING=events)";
+    if (ctx->copy_mode == SPTL_COPY_EVENTS) return "per-chunk events (copy mode)";
+    if (ctx->copy_mode == SPTL_COPY_BLIT) return "per-chunk events with copy kernels (blit copy mode)";
+    if (ctx->copy_mode == SPTL_COPY_SERIAL) return "copies, then the GEMM (serial copy mode)";
     if (!ctx->stager_tried) return "no copy engines set up";
     return ctx->staging_info.c_str();
 }
@@ -381,6 +404,17 @@ int sptl_ctx_set_wait_timeout_us(sptl_ctx *ctx, int64_t us) {
     if (us < 0 || us > 10000000)
         return fail(SPTL_E_RANGE, "sptl_ctx_set_wait_timeout_us: us=%lld not in [0, 10000000]", (long long)us);
     ctx->wait_timeout_us = us ? (uint64_t)us : kDefaultWaitUs;
+    return SPTL_OK;
+}
+
+int sptl_ctx_set_copy_mode(sptl_ctx *ctx, int mode, int blit_workgroups) {
+    if (!ctx) return fail(SPTL_E_NULL, "sptl_ctx_set_copy_mode: ctx is NULL");
+    if (mode < SPTL_COPY_STAGED || mode > SPTL_COPY_SERIAL)
+        return fail(SPTL_E_RANGE, "sptl_ctx_set_copy_mode: mode=%d", mode);
+    if (blit_workgroups < 0 || blit_workgroups > 65535)
+        return fail(SPTL_E_RANGE, "sptl_ctx_set_copy_mode: blit_workgroups=%d not in [0, 65535]", blit_workgroups);
+    ctx->copy_mode = mode;
+    ctx->blit_wgs = blit_workgroups;
     return SPTL_OK;
 }
 
@@ -463,12 +497,43 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
 
     hipStream_t cs = static_cast<hipStream_t>(compute);
-    if (!copy && staged_path(ctx, seq_len / n_chunks, n_chunks)) {
+    const bool cap = capturing(cs);
+    const bool serial = !copy && ctx->copy_mode == SPTL_COPY_SERIAL;
+    if (timing && (cap || serial))
+        return fail(SPTL_E_UNSUPPORTED, "agmm_chunked: timing with %s", cap ? "a stream under graph capture"
+                                                                              : "the serial copy mode");
+    if (!copy && staged_path(ctx, seq_len / n_chunks, n_chunks, cs)) {
         ctx->t_chunks = -1;
         return agmm_staged(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, shard_src,
                            static_cast<uint16_t *>(x_gathered), w, y, y_dtype, cs, timing);
     }
-    // ---- event path: one SDMA copy per chunk on a copy stream, one GEMM launch per chunk ----
+    if (serial) {
+        // no overlap (the baseline the overlap is measured against): every copy on `compute`,
+        // then one GEMM over all gathered rows
+        if (int rc = check_gemm_dims(seq_len, hidden, n_local)) return rc;
+        ctx->t_chunks = -1;
+        auto *xg = static_cast<uint16_t *>(x_gathered);
+        const size_t shard_elems = (size_t)(seq_len / tp) * (size_t)hidden;
+        for (int d = 1; d <= tp; ++d) {
+            const int q = (rank + d) % tp;
+            if (shard_src[q] != xg + (size_t)q * shard_elems)
+                SPTL_HIP(stage_copy(ctx, xg + (size_t)q * shard_elems, shard_src[q], shard_elems * 2, cs, cap));
+        }
+        sptl::GemmProblem gp{};
+        gp.a = xg;
+        gp.b = static_cast<const uint16_t *>(w);
+        gp.c = y;
+        gp.m = seq_len;
+        gp.n = n_local;
+        gp.k = hidden;
+        gp.lda = hidden;
+        gp.ldb = n_local;
+        gp.ldc = n_local;
+        gp.c_f32 = y_dtype == SPTL_F32;
+        SPTL_HIP(sptl::launch_gemm(gp, cs));
+        return SPTL_OK;
+    }
+    // ---- event path: one copy per chunk on a copy stream, one GEMM launch per chunk ----
     hipStream_t ps = static_cast<hipStream_t>(copy);
     if (!ps)
         if (int rc = copy_stream_of(ctx, &ps)) return rc;
@@ -498,7 +563,8 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
     // ---- copy stream: every staging copy is enqueued before any GEMM ------------------
     // Peers in ring order rank+1, rank+2, ... so the order matches arrival in a real ring.
     // hipMemcpyDeviceToDeviceNoCU keeps the copies on the SDMA engines (a plain
-    // device-to-device copy would run as a copy kernel on the compute units).
+    // device-to-device copy may run as a copy kernel on the compute units); the blit mode
+    // runs them as a copy kernel on purpose.
     for (int d = 1; d < tp; ++d) {
         const int q = (rank + d) % tp;
         for (int s = 0; s < cpr; ++s) {
@@ -507,8 +573,7 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
                 SPTL_HIP(hipEventRecord(ctx->t_copy_start[c], ps));
                 ctx->t_has_copy[c] = 1;
             }
-            SPTL_HIP(hipMemcpyAsync(xg + (size_t)c * chunk_elems, src_chunk(q, s), chunk_bytes,
-                                    hipMemcpyDeviceToDeviceNoCU, ps));
+            SPTL_HIP(stage_copy(ctx, xg + (size_t)c * chunk_elems, src_chunk(q, s), chunk_bytes, ps, cap));
             SPTL_HIP(hipEventRecord(ctx->ready[c], ps));
         }
     }
@@ -519,8 +584,7 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
             SPTL_HIP(hipEventRecord(ctx->t_copy_start[c0], ps));
             for (int s = 0; s < cpr; ++s) ctx->t_has_copy[c0 + s] = 1;
         }
-        SPTL_HIP(hipMemcpyAsync(xg + (size_t)c0 * chunk_elems, shard_src[rank], chunk_bytes * cpr,
-                                hipMemcpyDeviceToDeviceNoCU, ps));
+        SPTL_HIP(stage_copy(ctx, xg + (size_t)c0 * chunk_elems, shard_src[rank], chunk_bytes * cpr, ps, cap));
         SPTL_HIP(hipEventRecord(ctx->ready[c0], ps));
         for (int s = 1; s < cpr; ++s) {
             if (timing) SPTL_HIP(hipEventRecord(ctx->t_copy_start[c0 + s], ps));
@@ -587,6 +651,8 @@ int agmm_chunked_noalloc(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t
     if (!ctx->stager || sptl::stager_failed(ctx->stager))
         return fail(SPTL_E_UNSUPPORTED, "%s: the context has no working copy engines (%s)", fn,
                     ctx->staging_info.c_str());
+    if (capturing(static_cast<hipStream_t>(compute)))
+        return fail(SPTL_E_UNSUPPORTED, "%s: the staged copies cannot be captured into a graph", fn);
     sptl::NoallocScratch na;
     if (!sptl::noalloc_scratch(ctx->device, &na))
         return fail(SPTL_E_HIP, "%s: the device scratch was not set up", fn);
@@ -706,12 +772,43 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
     gp.ldb = hidden;
     gp.ldc = hidden;
     gp.c_f32 = false;
-    if (!staged_path(ctx, R, tp)) {
-        // no copy engines (or slices of no chunk-tile height): the GEMM, then the copies
+    auto in_place = [&](int q) { return q == rank || dst[q] == pb + (size_t)q * slice_elems; };
+    if (ctx->copy_mode == SPTL_COPY_SERIAL) {
+        // no overlap (the baseline the overlap is measured against): the GEMM, then the copies
+        const bool cap = capturing(cs);
         SPTL_HIP(sptl::launch_gemm(gp, cs));
-        for (int q = 0; q < tp; ++q)
-            if (q != rank && dst[q] != pb + (size_t)q * slice_elems)
-                SPTL_HIP(hipMemcpyAsync(dst[q], pb + (size_t)q * slice_elems, slice_bytes, hipMemcpyDeviceToDeviceNoCU, cs));
+        for (int d = 1; d < tp; ++d) {
+            const int q = (rank + d) % tp;
+            if (!in_place(q)) SPTL_HIP(stage_copy(ctx, dst[q], pb + (size_t)q * slice_elems, slice_bytes, cs, cap));
+        }
+        return SPTL_OK;
+    }
+    if (!staged_path(ctx, R, tp, cs)) {
+        // per-slice events: one GEMM launch per slice on `compute` in send order, each peer slice
+        // then copied on the copy stream after its event while the next slices compute
+        const bool cap = capturing(cs);
+        hipStream_t ps;
+        if (int rc = copy_stream_of(ctx, &ps)) return rc;
+        if (int rc = grow_events(ctx->ready, tp)) return rc;
+        sptl::GemmProblem sp = gp;
+        sp.m = R;
+        bool copied = false;
+        for (int d = 1; d <= tp; ++d) {
+            const int q = (rank + d) % tp;
+            sp.a = gp.a + (size_t)q * (size_t)R * (size_t)k_local;
+            sp.c = pb + (size_t)q * slice_elems;
+            SPTL_HIP(sptl::launch_gemm(sp, cs));
+            if (in_place(q)) continue;
+            SPTL_HIP(hipEventRecord(ctx->ready[q], cs));
+            SPTL_HIP(hipStreamWaitEvent(ps, ctx->ready[q], 0));
+            SPTL_HIP(stage_copy(ctx, dst[q], pb + (size_t)q * slice_elems, slice_bytes, ps, cap));
+            copied = true;
+        }
+        if (copied) {
+            // later work on `compute` sees every destination complete
+            SPTL_HIP(hipEventRecord(ctx->join, ps));
+            SPTL_HIP(hipStreamWaitEvent(cs, ctx->join, 0));
+        }
         return SPTL_OK;
     }
     // slices in send order: the peers' r + 1, r + 2, ... (copied out while later slices compute),
@@ -858,12 +955,12 @@ int reduce_norm_agmm_chunked(sptl_ctx *ctx, int n_partials, const void *const *p
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
     hipStream_t cs = static_cast<hipStream_t>(compute);
-    if (staged_path(ctx, seq_len / n_chunks, n_chunks)) {
+    if (staged_path(ctx, seq_len / n_chunks, n_chunks, cs)) {
         ctx->t_chunks = -1;
         return agmm_staged(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, src.data(),
                            static_cast<uint16_t *>(x_gathered), w, y, y_dtype, cs, 0, nullptr, &ep);
     }
-    // no copy engines: the unfused pair (the copies start after the epilogue)
+    // not staged (see sptl_ctx_set_copy_mode): the unfused pair (the copies start after the epilogue)
     SPTL_HIP(sptl::launch_epilogue(ep, cs));
     return agmm_chunked(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, src.data(), x_gathered, w, y, y_dtype,
                         compute, nullptr, 0);

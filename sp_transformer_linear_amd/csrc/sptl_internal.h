@@ -106,6 +106,10 @@ int chunk_tile_rows(int64_t chunk_rows);
 // Fills n 64-bit words with v on `stream` (a kernel, so it is safe inside graph capture).
 hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t stream);
 
+// Copies `bytes` (a multiple of 16; both pointers 16-byte aligned) with a kernel on the compute
+// units: `workgroups` workgroups of 256 threads, or a grid sized to the copy when 0 (sptl_copy.hip).
+hipError_t launch_blit(void *dst, const void *src, size_t bytes, int workgroups, hipStream_t stream);
+
 constexpr int kMaxEpilogueInputs = 17;  // residual + 16 partials
 
 // h = in[0] + in[1] + ... + in[n_in - 1] (fp32, in this order); y = RMSNorm(h) * gamma.

@@ -30,6 +30,8 @@ STATUS = {0: "SPTL_OK", 1: "SPTL_E_NULL", 2: "SPTL_E_SHAPE", 3: "SPTL_E_DIVISIBI
           8: "SPTL_E_UNSUPPORTED", 9: "SPTL_E_ASYNC"}
 MAX_PARTIALS, MAX_TP, MAX_CHUNKS = 16, 64, 512
 MAX_K, MAX_N = 2097152, 8388608
+COPY_STAGED, COPY_EVENTS, COPY_BLIT, COPY_SERIAL = 0, 1, 2, 3
+COPY_MODES = {"staged": COPY_STAGED, "events": COPY_EVENTS, "blit": COPY_BLIT, "serial": COPY_SERIAL}
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -44,6 +46,7 @@ _SIGS = {
     "sptl_ctx_check": ([_vp], _int),
     "sptl_ctx_info": ([_vp], ctypes.c_char_p),
     "sptl_ctx_set_wait_timeout_us": ([_vp, _i64], _int),
+    "sptl_ctx_set_copy_mode": ([_vp, _int, _int], _int),
     "agmm_chunked": ([_vp, _i64, _i64, _i64, _int, _int, _int, _ptrs, _vp, _vp, _vp, _int, _vp, _vp,
                       _int], _int),
     "agmm_chunked_noalloc": ([_vp, _i64, _i64, _i64, _int, _int, _int, _ptrs, _vp, _vp, _vp, _int, _vp], _int),
@@ -163,6 +166,12 @@ class Context:
     def set_wait_timeout_us(self, us: int) -> None:
         """Bound on one chunk wait of later staged calls, in microseconds (0: the default 10 s)."""
         _check(_lib.sptl_ctx_set_wait_timeout_us(self.handle, int(us)))
+
+    def set_copy_mode(self, mode, blit_workgroups: int = 0) -> None:
+        """How later calls on this context stage their copies: "staged", "events", "blit" or
+        "serial" (or the COPY_* value); blit_workgroups sizes the blit mode's copy kernels."""
+        m = COPY_MODES[mode] if isinstance(mode, str) else int(mode)
+        _check(_lib.sptl_ctx_set_copy_mode(self.handle, m, int(blit_workgroups)))
 
     def info(self) -> str:
         """How agmm_chunked stages chunks on this context (diagnostic)."""

@@ -122,6 +122,11 @@ def test_wait_timeout_option_rejects_null_ctx(sptl):
     assert sptl._lib.sptl_ctx_set_wait_timeout_us(None, 5) == 1
 
 
+def test_copy_mode_option_rejects_null_ctx(sptl):
+    assert sptl._lib.sptl_ctx_set_copy_mode(None, sptl.COPY_EVENTS, 0) == 1
+    assert set(sptl.COPY_MODES.values()) == {0, 1, 2, 3}
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(ctx=None), 1),                                   # the set-up lives in the context
     (dict(tp=0), 6), (dict(y_dtype=3), 5), (dict(w=A + 4), 4),
