@@ -15,8 +15,8 @@ Sources (web pages; section named, no line numbers):
   [AReaL] "[Feature] Async Tensor Parallelism for Archon Engine" (AReaL issue), sections
           "TP Communication Is on Activations, Not Weights" and "Potential Solution".
   [DTP]   "Affinity-Aware Sharding for Delayed Tensor Parallelism" (arXiv abstract).
-  [MLM]   "Add forward all-gather overlap" (Megatron-LM pull request #5513), "Summary" and
-          "Observations".
+  [MLM]   "Add forward all-gather overlap" (Megatron-LM pull request #5513), "Summary",
+          "Scope" and "Observations".
 
 Readings taken where the pages are silent (each is listed, with the reason, in the design
 notes of the repository):
@@ -43,6 +43,7 @@ __all__ = [
     "f64_to_bf16_bits",
     "all_gather_sequence",
     "agmm",
+    "agmm_backward",
     "gemm_partial",
     "rmsnorm",
     "reduce_residual_rmsnorm",
@@ -121,6 +122,23 @@ def agmm(shards: Sequence, w) -> tuple[np.ndarray, np.ndarray]:
     """
     x = all_gather_sequence(shards)
     return x, x @ _as_f64(w)
+
+
+def agmm_backward(shards: Sequence, w, dy) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Backward of Y = gather(shards) @ W for an upstream gradient dY: returns (X, dX, dW).
+
+    The backward pass all-gathers the activation again [MLM, "Scope": backward all-gathers
+    are present, not yet overlapped], because the weight gradient needs every token while each
+    rank keeps only its shard.  The gradients are those of any linear map Y = X W:
+        dX = dY W^T   (this rank's partial sum of the input gradient, since W is its shard of
+                       the columns; its sequence slices are reduce-scattered over the ranks)
+        dW = X^T dY   (the gradient of this rank's weight shard)
+    stated here unchunked and in float64.
+    """
+    x = all_gather_sequence(shards)
+    g = _as_f64(dy)
+    wt = _as_f64(w).T
+    return x, g @ wt, x.T @ g
 
 
 # ---------------------------------------------------------------------------------------

@@ -202,6 +202,70 @@ def check_tp_identity(impl):
     assert np.allclose(sum(parts), impl.gemm_partial(a, w), rtol=1e-12, atol=1e-300)
 
 
+def _int_bits(rng, shape, lo=-3, hi=4):
+    """bf16 bits of small integers: sums of their products are exact in float64."""
+    return bits(rng.integers(lo, hi, shape).astype(np.float64))
+
+
+def check_backward_is_the_gradient(impl):
+    """dX and dW are the derivatives of L = <dY, Y> with Y the forward agmm: with integer
+    inputs, a unit step of one element of a shard (or of W) changes L by exactly that element
+    of dX (or dW).  Pins the backward to the forward and to the definition of a gradient, not
+    to a formula (a transposed or misplaced operand fails it)."""
+    rng = np.random.default_rng(21)
+    for tp, rows, k, n in ((2, 2, 3, 4), (3, 1, 4, 4), (2, 3, 5, 2)):
+        shards = [_int_bits(rng, (rows, k)) for _ in range(tp)]
+        w = _int_bits(rng, (k, n))
+        dy = _int_bits(rng, (tp * rows, n))
+        g = O.bf16_bits_to_f64(dy)
+        x, dx, dw = impl.agmm_backward(shards, w, dy)
+        assert np.array_equal(x, impl.agmm(shards, w)[0])
+        loss = lambda sh, ww: float(np.sum(g * impl.agmm(sh, ww)[1]))  # noqa: E731
+        base = loss(shards, w)
+        for q in range(tp):
+            for i in range(rows):
+                for j in range(k):
+                    v = O.bf16_bits_to_f64(shards[q]).copy()
+                    v[i, j] += 1.0
+                    step = [bits(v) if p == q else shards[p] for p in range(tp)]
+                    assert loss(step, w) - base == dx[q * rows + i, j]
+        for i in range(k):
+            for j in range(n):
+                v = O.bf16_bits_to_f64(w).copy()
+                v[i, j] += 1.0
+                assert loss(shards, bits(v)) - base == dw[i, j]
+
+
+def check_backward_brute(impl):
+    rng = np.random.default_rng(22)
+    for tp, rows, k, n in ((2, 2, 3, 5), (4, 1, 2, 3)):
+        shards = [rand_bits(rng, (rows, k)) for _ in range(tp)]
+        w = rand_bits(rng, (k, n), 0.5)
+        dy = rand_bits(rng, (tp * rows, n), 0.3)
+        x, dx, dw = impl.agmm_backward(shards, w, dy)
+        bx = brute.gather([brute.matrix(s) for s in shards])
+        bw, bdy = brute.matrix(w), brute.matrix(dy)
+        tr = lambda m: [list(r) for r in zip(*m)]  # noqa: E731
+        f = lambda m: np.array([[float(v) for v in r] for r in m])  # noqa: E731
+        assert np.allclose(dx, f(brute.matmul(bdy, tr(bw))), rtol=1e-13, atol=0)
+        assert np.allclose(dw, f(brute.matmul(tr(bx), bdy)), rtol=1e-13, atol=0)
+
+
+def check_backward_special(impl):
+    rng = np.random.default_rng(23)
+    k = 8
+    shards = [rand_bits(rng, (3, k)) for _ in range(2)]
+    dy = rand_bits(rng, (6, k))
+    x, dx, dw = impl.agmm_backward(shards, bits(np.eye(k)), dy)
+    assert np.array_equal(dx, O.bf16_bits_to_f64(dy))       # W = I: the gradient passes through
+    one = np.zeros((6, 5))
+    one[4, 2] = 1.0                                          # one token, one output feature
+    x, dx, dw = impl.agmm_backward(shards, rand_bits(rng, (k, 5)), bits(one))
+    want = np.zeros((k, 5))
+    want[:, 2] = x[4]
+    assert np.array_equal(dw, want)
+
+
 def check_rmsnorm_golden(impl):
     g = load_golden("rmsnorm_worked.txt")
     for case, nparts in (("a", 0), ("b", 2), ("c", 0)):
@@ -336,7 +400,7 @@ CHECKS = [check_bf16_decode, check_round_to_bf16, check_f64_to_bf16_bits, check_
           check_tp_identity, check_rmsnorm_golden, check_rmsnorm_closed_forms,
           check_rmsnorm_brute, check_norm_commutes_with_gather,
           check_reduce_uses_each_partial_once, check_dtp_golden, check_dtp_invariants,
-          check_dtp_store_bf16]
+          check_dtp_store_bf16, check_backward_is_the_gradient, check_backward_brute, check_backward_special]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
@@ -458,6 +522,25 @@ def _round_trunc(x):
     return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
 
 
+def _bwd_dx_untransposed(shards, w, dy):   # input gradient through W instead of W^T
+    x = O.all_gather_sequence(shards)
+    wv, g = O._as_f64(w), O._as_f64(dy)
+    dx = g @ wv if wv.shape[0] == wv.shape[1] else g @ wv[::-1].T
+    return x, dx, x.T @ g
+
+
+def _bwd_dw_tokens_misaligned(shards, w, dy):  # weight gradient pairs the wrong tokens
+    x = O.all_gather_sequence(shards)
+    g = O._as_f64(dy)
+    return x, g @ O._as_f64(w).T, x.T @ g[::-1]
+
+
+def _bwd_gather_reversed(shards, w, dy):
+    x = _gather_reversed(shards)
+    g = O._as_f64(dy)
+    return x, g @ O._as_f64(w).T, x.T @ g
+
+
 MUTANTS = {
     "rmsnorm_sum_not_mean": dict(rmsnorm=_rms_sum),
     "rmsnorm_eps_outside_sqrt": dict(rmsnorm=_rms_eps_outside),
@@ -472,6 +555,9 @@ MUTANTS = {
     "decode_wrong_exponent": dict(bf16_bits_to_f64=_decode_wrong_bias),
     "round_truncates": dict(round_to_bf16=_round_trunc),
     "encode_double_rounding": dict(f64_to_bf16_bits=_encode_via_binary32),
+    "backward_dx_untransposed": dict(agmm_backward=_bwd_dx_untransposed),
+    "backward_dw_tokens_misaligned": dict(agmm_backward=_bwd_dw_tokens_misaligned),
+    "backward_gather_reversed": dict(agmm_backward=_bwd_gather_reversed),
 }
 
 
