@@ -636,6 +636,55 @@ def main():
 
     copy_modes = copy_mode_study(L, L.w_col, reps, wl.n_chunks)
 
+    # Backward ("Add forward all-gather overlap", "Scope": the backward gathers again): the
+    # re-gather on the copy engines under the input-gradient GEMM, then the weight-gradient GEMM;
+    # against the same call with every shard already in place (the two GEMMs alone) and the
+    # serial mode (copies, then the GEMMs), timed in triples.  dy is the forward's output.
+    def backward_study(T, w, reps):
+        M_, K_ = T.xg.shape
+        N_ = w.shape[1]
+        tp_ = len(T.shards)
+        R_ = M_ // tp_
+        dy = T.y_col
+        dx = torch.empty((M_, K_), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((K_, N_), dtype=torch.float32, device=dev)
+        in_place = [T.xg[q * R_:(q + 1) * R_] for q in range(tp_)]
+
+        def bwd(c, shards):
+            sptl.agmm_backward(shards, T.xg, w, dy, dx, dw, rank=0, compute=cs, ctx=c)
+
+        for _ in range(3):
+            bwd(ctx, T.shards)
+            bwd(ctx, in_place)
+            bwd(ctx_serial, T.shards)
+        trip = []
+        for _ in range(2 * reps):
+            e = [ev() for _ in range(4)]
+            e[0].record(cs)
+            bwd(ctx, T.shards)
+            e[1].record(cs)
+            bwd(ctx, in_place)
+            e[2].record(cs)
+            bwd(ctx_serial, T.shards)
+            e[3].record(cs)
+            trip.append(e)
+        torch.cuda.synchronize()
+        ctx.check()
+        ctx_serial.check()
+        d = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in trip])
+        t_b, t_g, t_s = (float(np.median(d[:, i])) for i in range(3))
+        t_copy = float(np.median(d[:, 2] - d[:, 1]))
+        exposed = max(0.0, float(np.median(d[:, 0] - d[:, 1])))
+        fl = 4.0 * M_ * K_ * N_
+        del dx, dw
+        return {"ms": round(t_b, 4), "tflops": round(fl / (t_b * 1e-3) / 1e12, 2),
+                "frac_peak": round(fl / (t_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "ms_gemms_only": round(t_g, 4), "gemms_tflops": round(fl / (t_g * 1e-3) / 1e12, 2),
+                "ms_serial": round(t_s, 4), "copy_serial_ms": round(t_copy, 4), "copy_exposed_ms": round(exposed, 4),
+                "copy_hidden_frac": None if t_copy <= 0 else round(max(0.0, 1.0 - exposed / t_copy), 4)}
+
+    backward = backward_study(L, L.w_col, reps)
+
     # Launch gaps: one step captured in a HIP graph (on a stream under capture the agmm call takes
     # the per-chunk event path, whose copies, events and launches a graph holds), replayed, against
     # the same step run eagerly on the event path and on the default staged path (the timed
@@ -726,6 +775,7 @@ def main():
             "boundary": boundary,
             "copy_modes": copy_modes,
             "launch": launch,
+            "backward": backward,
         },
         "gemm_partial": {"tflops": round(gemmp_tflops, 2), "frac_peak": round(gemmp_tflops / PEAK_BF16_TFLOPS, 4),
                          "ms": round(float(gemmp_ms.mean()), 4), "ms_median": round(float(np.median(gemmp_ms)), 4),

@@ -283,6 +283,34 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
                     const void *a, const void *w, void *partial, void *const *dst, void *compute);
 
 /*
+ * (1') Backward of the chunked all-gather + column-parallel GEMM, with the re-gather overlapped.
+ *
+ * [MLM "Scope"]: the backward pass gathers again (the weight gradient needs the gathered
+ * activation, of which each rank keeps only its shard), and that gather was left without
+ * overlap.  Here it runs on the copy engines while the input-gradient GEMM, which does not read
+ * the activation, computes; the weight-gradient GEMM follows.  For y = x_gathered @ w (agmm_chunked):
+ *   x_gathered = rank-major concatenation of the shards (as agmm_chunked)
+ *   dx = dy @ w^T   [seq_len, hidden] bf16: this rank's partial sum of the input gradient (its
+ *                   sequence slices are reduce-scattered over the ranks, as gemm_rs_chunked does)
+ *   dw = x_gathered^T @ dy   [hidden, n_local], dw_dtype SPTL_F32 or SPTL_BF16
+ * Both GEMMs accumulate in fp32, over n_local ascending (dx) and seq_len ascending (dw).
+ *   seq_len, hidden, n_local, tp, rank, shard_src, x_gathered, w: as agmm_chunked
+ *            (seq_len % tp == 0; hidden and n_local multiples of 8; tp <= 64)
+ *   dy       [seq_len, n_local] bf16, the gradient of y
+ *   compute  stream; the call is ordered after earlier work on it, and later work on it sees
+ *            x_gathered, dx and dw complete.
+ * Staged (the context's copy mode SPTL_COPY_STAGED, copy engines available, no graph capture):
+ * every copy goes to the SDMA engines at the call's position on `compute`; the dx GEMM, a
+ * one-wave kernel that waits (bounded, as the chunk waits of agmm_chunked) for every copy, and
+ * the dw GEMM follow on `compute`.  Otherwise the copies run on the context's copy stream
+ * (events mode, blit mode or graph capture) or on `compute` before the GEMMs (serial mode).
+ * Every path gives the same bits.  Errors as agmm_chunked (SPTL_E_DTYPE for dw_dtype).
+ */
+int agmm_backward(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local, int tp, int rank,
+                  const void *const *shard_src, void *x_gathered, const void *w, const void *dy,
+                  void *dx, void *dw, int dw_dtype, void *compute);
+
+/*
  * (3) Fused reduce + residual + RMSNorm at a sub-layer boundary.
  *
  * [AReaL "Potential Solution", sub-layer boundary overlap]: between a sub-layer's

@@ -209,6 +209,16 @@ int check_gemm_dims(int64_t m, int64_t k, int64_t n) {
     return SPTL_OK;
 }
 
+// SPTL_POLL_SLEEP=0..64: extra s_sleep 127 per poll of a bounded wait (measurement aid).
+int poll_sleep_setting() {
+    static const int v = [] {
+        const char *e = getenv("SPTL_POLL_SLEEP");
+        const long x = e ? strtol(e, nullptr, 10) : 0;
+        return (int)(x >= 0 && x <= 64 ? x : 0);
+    }();
+    return v;
+}
+
 // Whether stream s is being captured into a graph (a failed query counts as captured: the
 // per-chunk path is correct either way, the staged one needs its worker thread at run time).
 bool capturing(hipStream_t s) {
@@ -286,12 +296,7 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     plan.own_a = static_cast<const uint16_t *>(shard_src[rank]);
     plan.err = na ? na->err : ctx->err_dev;
     plan.timeout_ticks = (uint64_t)ctx->wallclock_khz * ctx->wait_timeout_us / 1000u;
-    static const int poll_sleep = [] {
-        const char *e = getenv("SPTL_POLL_SLEEP");
-        const long v = e ? strtol(e, nullptr, 10) : 0;
-        return (int)(v >= 0 && v <= 64 ? v : 0);
-    }();
-    plan.poll_sleep = poll_sleep;
+    plan.poll_sleep = poll_sleep_setting();
     // SPTL_CHUNK_XCDS=g (1, 2, 4 or 8) spreads every chunk's tiles over g XCDs (measurement aid)
     static const int xcd_group = [] {
         const char *e = getenv("SPTL_CHUNK_XCDS");
@@ -862,6 +867,132 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
     }
     if (sptl::stager_submit(ctx->stager, call, std::move(pieces), &why, true))
         return fail(SPTL_E_HIP, "%s: %s", fn, why.c_str());
+    return SPTL_OK;
+}
+
+int agmm_backward(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local, int tp, int rank,
+                  const void *const *shard_src, void *x_gathered, const void *w, const void *dy, void *dx, void *dw,
+                  int dw_dtype, void *compute) {
+    static const char *fn = "agmm_backward";
+    if (!shard_src || !x_gathered || !w || !dy || !dx || !dw) return fail(SPTL_E_NULL, "%s: NULL pointer argument", fn);
+    if (seq_len < 0 || hidden <= 0 || n_local <= 0)
+        return fail(SPTL_E_SHAPE, "%s: bad sizes seq_len=%lld hidden=%lld n_local=%lld", fn, (long long)seq_len,
+                    (long long)hidden, (long long)n_local);
+    if (tp < 1 || tp > sptl::kMaxPlanChunks)
+        return fail(SPTL_E_RANGE, "%s: tp=%d not in [1, %d]", fn, tp, sptl::kMaxPlanChunks);
+    if (rank < 0 || rank >= tp) return fail(SPTL_E_RANGE, "%s: rank=%d not in [0, %d)", fn, rank, tp);
+    if (seq_len % tp)
+        return fail(SPTL_E_DIVISIBILITY, "%s: seq_len=%lld not a multiple of tp=%d", fn, (long long)seq_len, tp);
+    if (dw_dtype != SPTL_BF16 && dw_dtype != SPTL_F32) return fail(SPTL_E_DTYPE, "%s: dw_dtype=%d", fn, dw_dtype);
+    // dx = dy w^T: m = seq_len, k = n_local, n = hidden; dw = x^T dy: m = hidden, k = seq_len (the row
+    // index of both operands, so any length), n = n_local
+    if (int rc = check_gemm_dims(seq_len, n_local, hidden)) return rc;
+    if (int rc = check_gemm_dims(hidden, 8, n_local)) return rc;
+    for (int q = 0; q < tp; ++q) {
+        if (!shard_src[q]) return fail(SPTL_E_NULL, "%s: shard_src[%d] is NULL", fn, q);
+        if (!aligned16(shard_src[q])) return fail(SPTL_E_ALIGN, "%s: shard_src[%d] not 16-byte aligned", fn, q);
+    }
+    if (!aligned16(x_gathered) || !aligned16(w) || !aligned16(dy) || !aligned16(dx) || !aligned16(dw))
+        return fail(SPTL_E_ALIGN, "%s: x_gathered, w, dy, dx and dw must be 16-byte aligned", fn);
+    if (seq_len == 0) return SPTL_OK;
+    if (int rc = resolve_ctx(ctx)) return rc;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    hipStream_t cs = static_cast<hipStream_t>(compute);
+    auto *xg = static_cast<uint16_t *>(x_gathered);
+    const size_t shard_elems = (size_t)(seq_len / tp) * (size_t)hidden;
+    sptl::GemmProblem gx{}, gw{};
+    gx.a = static_cast<const uint16_t *>(dy);  // dx[m, k] = sum_j dy[m, j] w[k, j]
+    gx.b = static_cast<const uint16_t *>(w);
+    gx.c = dx;
+    gx.m = seq_len;
+    gx.n = hidden;
+    gx.k = n_local;
+    gx.lda = n_local;
+    gx.ldb = n_local;
+    gx.ldc = hidden;
+    gx.c_f32 = false;
+    gx.layout = sptl::kLayoutBNMajor;
+    gw.a = xg;  // dw[k, j] = sum_m x[m, k] dy[m, j]
+    gw.b = static_cast<const uint16_t *>(dy);
+    gw.c = dw;
+    gw.m = hidden;
+    gw.n = n_local;
+    gw.k = seq_len;
+    gw.lda = hidden;
+    gw.ldb = n_local;
+    gw.ldc = n_local;
+    gw.c_f32 = dw_dtype == SPTL_F32;
+    gw.layout = sptl::kLayoutAKMajor;
+    // the copies, peers in arrival order (rank+1, rank+2, ...) then the own slot unless aliased
+    std::vector<sptl::CopyPiece> copies;
+    for (int d = 1; d <= tp; ++d) {
+        const int q = (rank + d) % tp;
+        if (shard_src[q] != xg + (size_t)q * shard_elems)
+            copies.push_back({xg + (size_t)q * shard_elems, shard_src[q], shard_elems * 2, q});
+    }
+    const bool cap = capturing(cs);
+    if (ctx->copy_mode == SPTL_COPY_SERIAL) {
+        for (const sptl::CopyPiece &c : copies) SPTL_HIP(stage_copy(ctx, c.dst, c.src, c.bytes, cs, cap));
+        SPTL_HIP(sptl::launch_gemm(gx, cs));
+        SPTL_HIP(sptl::launch_gemm(gw, cs));
+        return SPTL_OK;
+    }
+    if (copies.empty()) {
+        SPTL_HIP(sptl::launch_gemm(gx, cs));
+        SPTL_HIP(sptl::launch_gemm(gw, cs));
+        return SPTL_OK;
+    }
+    const bool staged = ctx->copy_mode == SPTL_COPY_STAGED && ctx->stager && !sptl::stager_failed(ctx->stager) && !cap;
+    if (!staged) {
+        // per-copy events on the context's copy stream; dw waits for all of them
+        hipStream_t ps;
+        if (int rc = copy_stream_of(ctx, &ps)) return rc;
+        SPTL_HIP(hipEventRecord(ctx->fork, cs));
+        SPTL_HIP(hipStreamWaitEvent(ps, ctx->fork, 0));
+        for (const sptl::CopyPiece &c : copies) SPTL_HIP(stage_copy(ctx, c.dst, c.src, c.bytes, ps, cap));
+        SPTL_HIP(hipEventRecord(ctx->join, ps));
+        SPTL_HIP(sptl::launch_gemm(gx, cs));
+        SPTL_HIP(hipStreamWaitEvent(cs, ctx->join, 0));
+        SPTL_HIP(sptl::launch_gemm(gw, cs));
+        return SPTL_OK;
+    }
+    // staged: the copy engines take the re-gather at the fork point, dx's GEMM runs meanwhile (it
+    // does not read x), a one-wave kernel then waits for every piece, and dw's GEMM follows it
+    std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies, 1, 1);
+    sptl::StageCall call;
+    std::string why;
+    if (int rc = sptl::stager_begin(ctx->stager, pieces, 1, &call, &why))
+        return fail(rc == -2 ? SPTL_E_ASYNC : SPTL_E_HIP, "%s: %s", fn, why.c_str());
+    sptl::ChunkPlan jp{};
+    jp.n_chunks = tp;
+    for (int c = 0; c < tp; ++c) {
+        jp.ready[c] = call.ready[c];
+        jp.ready_n[c] = call.ready_n[c];
+    }
+    jp.join = call.join;
+    jp.join_n = call.join_n;
+    jp.err = ctx->err_dev;
+    jp.timeout_ticks = (uint64_t)ctx->wallclock_khz * ctx->wait_timeout_us / 1000u;
+    jp.poll_sleep = poll_sleep_setting();
+    jp.epoch = call.epoch;
+    jp.flag_epoch = call.epoch;
+    jp.finished = call.finished;
+    jp.timedout = call.timedout;
+    jp.wg_count = call.wg_count;
+    for (int gi = 0; gi < sptl::kEndGroups; ++gi) jp.grp_last[gi] = call.grp_last[gi];
+    jp.all_last = call.all_last;
+    hipError_t he = hipEventRecord(call.fork, cs);
+    if (he == hipSuccess) he = sptl::launch_gemm(gx, cs);
+    if (he == hipSuccess) he = sptl::launch_stage_join(jp, cs);
+    if (he != hipSuccess) {
+        sptl::stager_cancel(ctx->stager, call);
+        return hip_fail(he, "agmm_backward: kernel launch");
+    }
+    he = sptl::launch_gemm(gw, cs);
+    if (sptl::stager_submit(ctx->stager, call, std::move(pieces), &why))
+        return fail(SPTL_E_HIP, "%s: %s", fn, why.c_str());
+    if (he != hipSuccess) return hip_fail(he, "agmm_backward: dw kernel launch");
     return SPTL_OK;
 }
 

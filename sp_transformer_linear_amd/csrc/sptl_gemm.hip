@@ -742,10 +742,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 //           (the transposing reads of a fragment take rows 8 g .. 8 g + 3 in lane group g; bit 3
 //           of k keeps groups 0 and 1, which the LDS serves together, on different banks).
 // Same K order as every other configuration.
-template <int WGM, int WGN, int SLOTS, bool OUT_F32, bool CHUNKED>
+//
+// Operand layouts (LAYOUT, GemmProblem::layout): kLayoutRowMajor as above; kLayoutAKMajor, A
+// stored k-major (element (i, k) at a[k lda + i], the transposed activation of a weight
+// gradient): its stage is staged and read exactly like B's (32 k rows of 256 values, transposing
+// fragment reads); kLayoutBNMajor, B stored n-major (element (k, j) at b[j ldb + k], the
+// transposed weight of an input gradient): its stage is staged and read like A's (256 rows of 32
+// k, one ds_read_b128 per fragment).  The MFMA sees the same fragments either way, so the K
+// order, and every product and sum, are those of the row-major form.
+template <int WGM, int WGN, int SLOTS, bool OUT_F32, bool CHUNKED, int LAYOUT = kLayoutRowMajor>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
+    constexpr bool A_KM = LAYOUT == kLayoutAKMajor, B_NM = LAYOUT == kLayoutBNMajor;
+    static_assert(!CHUNKED || LAYOUT == kLayoutRowMajor, "chunk-ordered launches are row-major");
     constexpr int BM = 256, BN = 256, TM = BM / WGM / 16, TN = BN / WGN / 16;  // 16 x 16 blocks per wave
     constexpr int NBLK = 16 / (WGM * WGN);   // 1 KB blocks per operand per wave per stage
     constexpr bool kFour = WGM * WGN == 4;   // the four-wave form (AGPR accumulators)
@@ -766,31 +776,61 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     const int nt = tiles_m * tiles_n;
     const int nk = (int)((p.k + kDmaBK - 1) / kDmaBK);
 
-    // Per-lane offsets of this wave's NBLK A blocks (16 rows each) and NBLK B blocks (2 k-rows
-    // each) of a stage, relative to a tile's origin.
-    int a_off[NBLK], a_kc[NBLK];
+    // Per-lane offsets of this wave's NBLK row-form blocks (16 rows of 32 k each) of a stage,
+    // relative to the operand tile's origin (A, or with B_NM the n-major B); the k-major form's
+    // blocks (2 k-rows each) are addressed in load_kmajor.
+    int a_off[NBLK], b_off[B_NM ? NBLK : 1], r_kc[NBLK];
 #pragma unroll
     for (int t = 0; t < NBLK; ++t) {
         const int blk = wave * NBLK + t;
         const int row = blk * 16 + (lane >> 2);
         const int c = (lane & 3) ^ ((row >> 2) & 3);
-        a_kc[t] = c * 8;
+        r_kc[t] = c * 8;
         a_off[t] = (int)((row * p.lda + c * 8) * 2);
+        if constexpr (B_NM) b_off[t] = (int)((row * p.ldb + c * 8) * 2);
     }
     const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * NBLK) * 1024;  // this wave's first block
-    // Load t of a stage's A blocks and of its B blocks, into the slot at la / lb.
-    auto load_a = [&](const u32x4_t &ar, uint32_t la, int t, bool k_tail, int64_t k0) __attribute__((always_inline)) {
-        const int off = (k_tail && k0 + a_kc[t] >= p.k) ? kOutOfRange : a_off[t];
-        load_to_lds(ar, la + t * 1024, off);
+    // Load t of a stage's row-form blocks (16 rows, one 16-byte piece of k per lane).
+    auto load_rows = [&](const u32x4_t &r, uint32_t l, int t, bool k_tail, int64_t k0, const int *off)
+        __attribute__((always_inline)) {
+        load_to_lds(r, l + t * 1024, (k_tail && k0 + r_kc[t] >= p.k) ? kOutOfRange : off[t]);
     };
-    auto load_b = [&](const u32x4_t &br, uint32_t lb, int t, int64_t n0) __attribute__((always_inline)) {
-        // B block: k-rows 2 blk, 2 blk + 1 (lane / 32); lanes q, q + 1 read the two halves of the
-        // swizzled 32-byte unit (q / 2) of that row (recomputed here rather than kept in
-        // registers across the tiles)
+    // Load t of a stage's k-major blocks: k-rows 2 blk, 2 blk + 1 (lane / 32); lanes q, q + 1
+    // read the two halves of the swizzled 32-byte unit (q / 2) of that row (recomputed here
+    // rather than kept in registers across the tiles).  x0: the tile's first column (of B, or
+    // with A_KM the tile's first row of the output), x_end: the operand's column count, ld: its
+    // row stride.
+    auto load_kmajor = [&](const u32x4_t &r, uint32_t l, int t, int64_t x0, int64_t x_end, int64_t ld)
+        __attribute__((always_inline)) {
         const int krow = (wave * NBLK + t) * 2 + (lane >> 5);
         const int q = lane & 31;
-        const int64_t n = n0 + (((q >> 1) ^ (((krow & 3) << 1) | ((krow >> 3) & 1))) * 16 + (q & 1) * 8);
-        load_to_lds(br, lb + t * 1024, n < p.n ? (int)((krow * p.ldb + n) * 2) : kOutOfRange);
+        const int64_t x = x0 + (((q >> 1) ^ (((krow & 3) << 1) | ((krow >> 3) & 1))) * 16 + (q & 1) * 8);
+        load_to_lds(r, l + t * 1024, x < x_end ? (int)((krow * ld + x) * 2) : kOutOfRange);
+    };
+    auto load_a = [&](const u32x4_t &ar, uint32_t la, int t, bool k_tail, int64_t k0, const TileOrigin &o)
+        __attribute__((always_inline)) {
+        if constexpr (A_KM) load_kmajor(ar, la, t, o.m0, p.m, p.lda);
+        else load_rows(ar, la, t, k_tail, k0, a_off);
+    };
+    auto load_b = [&](const u32x4_t &br, uint32_t lb, int t, bool k_tail, int64_t k0, const TileOrigin &o)
+        __attribute__((always_inline)) {
+        if constexpr (B_NM) load_rows(br, lb, t, k_tail, k0, b_off);
+        else load_kmajor(br, lb, t, o.n0, p.n, p.ldb);
+    };
+    // Buffer ranges of stage k0 (k_rows of its 32 k exist; 0 for an empty stage).  Row form:
+    // from the tile's first row at k0 to the end of its last valid row (rows and k past the end
+    // read zeros).  k-major form: the stage's k_rows rows of the whole operand.
+    auto a_desc = [&](const TileOrigin &o, bool live, int64_t k0, int64_t k_rows) __attribute__((always_inline)) {
+        if constexpr (A_KM) return buffer_desc(p.a + k0 * p.lda, (uint32_t)(k_rows * p.lda * 2));
+        else return buffer_desc(o.a_tile + k0, (uint32_t)(live ? ((int64_t)o.rows_valid * p.lda - k0) * 2 : 0));
+    };
+    auto b_desc = [&](const TileOrigin &o, bool live, int64_t k0, int64_t k_rows) __attribute__((always_inline)) {
+        if constexpr (B_NM) {
+            const int64_t cols = (p.n - o.n0) < BN ? (p.n - o.n0) : BN;
+            return buffer_desc(p.b + o.n0 * p.ldb + k0, (uint32_t)(live ? (cols * p.ldb - k0) * 2 : 0));
+        } else {
+            return buffer_desc(p.b + k0 * p.ldb, (uint32_t)(k_rows * p.ldb * 2));
+        }
     };
 
     // Stage kt of the tile at `o` into ring slot `slot`; live = false (or kt >= nk) reads an
@@ -799,16 +839,15 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     auto issue = [&](const TileOrigin &o, bool live_tile, int kt, int slot) {
         const bool live = live_tile && kt < nk;
         const int64_t k0 = live ? (int64_t)kt * kDmaBK : 0;
-        const int64_t a_bytes = live ? ((int64_t)o.rows_valid * p.lda - k0) * 2 : 0;
-        const u32x4_t ar = buffer_desc(o.a_tile + k0, (uint32_t)a_bytes);
         const bool k_tail = k0 + kDmaBK > p.k;
         const int64_t k_rows = !live ? 0 : (p.k - k0) < kDmaBK ? (p.k - k0) : kDmaBK;
-        const u32x4_t br = buffer_desc(p.b + k0 * p.ldb, (uint32_t)(k_rows * p.ldb * 2));
+        const u32x4_t ar = a_desc(o, live, k0, k_rows);
+        const u32x4_t br = b_desc(o, live, k0, k_rows);
         const uint32_t la = lds0 + (uint32_t)(slot * SLOT), lb = la + kDmaSlotBytes;
 #pragma unroll
-        for (int t = 0; t < NBLK; ++t) load_a(ar, la, t, k_tail, k0);
+        for (int t = 0; t < NBLK; ++t) load_a(ar, la, t, k_tail, k0, o);
 #pragma unroll
-        for (int t = 0; t < NBLK; ++t) load_b(br, lb, t, o.n0);
+        for (int t = 0; t < NBLK; ++t) load_b(br, lb, t, k_tail, k0, o);
     };
 
     // Fragment read addresses within a slot.  A block i (16 rows): lane l reads row
@@ -816,33 +855,50 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     // l holds column wn0 + 16 j + l % 16, k 8 (l / 16) .. + 7, from two transposing reads; per 16
     // lanes source lane s supplies row kb + s / 4 at columns nb + 4 (s % 4) and result lane i
     // gets B[kb .. kb + 3][nb + i], with kb = 8 (l / 16) and 8 (l / 16) + 4.
-    int a_addr[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int r = wm0 + i * 16 + (lane & 15);
-        a_addr[i] = r * (kDmaBK * 2) + (((lane >> 4) ^ ((r >> 2) & 3)) << 4);
-    }
+    // Row form, block x of the slot half at `half`: lane l reads row x0 + l % 16 (x0 = the
+    // block's first row) at k 8 (l / 16) .. + 7.  k-major form: lane l holds column x0 + l % 16
+    // from two transposing reads.
     const int rr = lane & 15;
     const int b_k0 = 8 * (lane >> 4) + (rr >> 2);
     const int b_sw = ((b_k0 & 3) << 1) | ((b_k0 >> 3) & 1);
-    int b_addr[TN];
+    auto row_addr = [&](int half, int x0) {
+        const int r = x0 + (lane & 15);
+        return half + r * (kDmaBK * 2) + (((lane >> 4) ^ ((r >> 2) & 3)) << 4);
+    };
+    auto kmajor_addr = [&](int half, int x0) {
+        const int x = x0 + 4 * (rr & 3);
+        return half + b_k0 * B_ROW + (((x >> 4) ^ b_sw) << 5) + (x & 15) * 2;
+    };
+    int a_addr[TM], b_addr[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int n = wn0 + j * 16 + 4 * (rr & 3);
-        b_addr[j] = kDmaSlotBytes + b_k0 * B_ROW + (((n >> 4) ^ b_sw) << 5) + (n & 15) * 2;
-    }
+    for (int i = 0; i < TM; ++i) a_addr[i] = A_KM ? kmajor_addr(0, wm0 + i * 16) : row_addr(0, wm0 + i * 16);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+        b_addr[j] = B_NM ? row_addr(kDmaSlotBytes, wn0 + j * 16) : kmajor_addr(kDmaSlotBytes, wn0 + j * 16);
+    auto read_rows = [&](const char *at) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8_t *>(at);
+    };
+    auto read_kmajor = [&](const char *at) __attribute__((always_inline)) {
+        bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(at));
+        bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(at + 4 * B_ROW));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto read_a = [&](const char *slot, int i) __attribute__((always_inline)) {
+        if constexpr (A_KM) return read_kmajor(slot + a_addr[i]);
+        else return read_rows(slot + a_addr[i]);
+    };
+    auto read_b = [&](const char *slot, int j) __attribute__((always_inline)) {
+        if constexpr (B_NM) return read_rows(slot + b_addr[j]);
+        else return read_kmajor(slot + b_addr[j]);
+    };
+    constexpr int kReadsA = A_KM ? 2 : 1, kReadsB = B_NM ? 1 : 2;  // LDS reads per fragment
 
     f32x4_t acc[TM][TN];
     auto load_frags = [&](const char *slot, bf16x8_t *af, bf16x8_t *bfr) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(slot + a_addr[i]);
+        for (int i = 0; i < TM; ++i) af[i] = read_a(slot, i);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const char *base = slot + b_addr[j];
-            bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
-            bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * B_ROW));
-            bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+        for (int j = 0; j < TN; ++j) bfr[j] = read_b(slot, j);
     };
     constexpr int kMf = TM * TN;
     // Column block major: B fragment j of the stage is dead after its TM MFMAs, so the next
@@ -862,9 +918,9 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #pragma unroll
         for (int m = 0; m < kMf; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (m < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (m < TM) __builtin_amdgcn_sched_group_barrier(0x100, kReadsA, 0);
             if (m % TM == TM - 1) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, kReadsB, 0);
                 if (m / TM < 2 * NBLK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         }
@@ -916,11 +972,10 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
             const int g = kt + SLOTS - 1;
             const bool live = g < nk;
             const int64_t k0 = live ? (int64_t)g * kDmaBK : 0;
-            const int64_t a_bytes = live ? ((int64_t)o.rows_valid * p.lda - k0) * 2 : 0;
-            const u32x4_t ar = buffer_desc(o.a_tile + k0, (uint32_t)a_bytes);
             const bool k_tail = k0 + kDmaBK > p.k;
             const int64_t k_rows = !live ? 0 : (p.k - k0) < kDmaBK ? (p.k - k0) : kDmaBK;
-            const u32x4_t br = buffer_desc(p.b + k0 * p.ldb, (uint32_t)(k_rows * p.ldb * 2));
+            const u32x4_t ar = a_desc(o, live, k0, k_rows);
+            const u32x4_t br = b_desc(o, live, k0, k_rows);
             const uint32_t la = lds0 + (uint32_t)(fslot * SLOT), lb = la + kDmaSlotBytes;
             const char *ns = smem + nslot * SLOT;
 #pragma unroll
@@ -935,16 +990,13 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
                     wait_vmcnt<2 * NBLK * (SLOTS - 3)>();  // SLOTS - 3 later stages may stay in flight
                     __syncthreads();
                 }
-                if (j < NBLK) load_a(ar, la, j, k_tail, k0);
-                else load_b(br, lb, j - NBLK, o.n0);
+                if (j < NBLK) load_a(ar, la, j, k_tail, k0, o);
+                else load_b(br, lb, j - NBLK, k_tail, k0, o);
                 if (2 * j < TM) {
-                    fa[S1][2 * j] = *reinterpret_cast<const bf16x8_t *>(ns + a_addr[2 * j]);
-                    fa[S1][2 * j + 1] = *reinterpret_cast<const bf16x8_t *>(ns + a_addr[2 * j + 1]);
+                    fa[S1][2 * j] = read_a(ns, 2 * j);
+                    fa[S1][2 * j + 1] = read_a(ns, 2 * j + 1);
                 }
-                const char *base = ns + b_addr[j];
-                bf16x4_t blo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
-                bf16x4_t bhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * B_ROW));
-                fb[S1][j] = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
+                fb[S1][j] = read_b(ns, j);
                 asm volatile("" ::: "memory");
             }
         };
@@ -993,6 +1045,25 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     // no load may still be writing this workgroup's LDS when it exits
     wait_vmcnt<0>();
 #endif
+}
+
+// Closes a staged call whose copies no GEMM tile waits for (the re-gather of agmm_backward,
+// consumed by a later launch on the stream): one wave, counted in the call's end counters like a
+// GEMM's only workgroup, waits for every piece of the call, then reports the call done.  The
+// launches after it on the stream see the copied rows (their start invalidates the caches).
+__global__ void __launch_bounds__(64) stage_join_kernel(ChunkPlan plan) {
+    int last = 0;
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(plan.wg_count, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   plan.grp_last[0] &&
+               __hip_atomic_fetch_add(plan.wg_count + kEndGroups * kEndLine, 1ull, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == plan.all_last;
+    if (__shfl(last, 0, 64)) {
+        for (int c = 0; c < plan.n_chunks; ++c) wait_ready(plan.ready[c], plan.ready_n[c], plan);
+        wait_ready(plan.join, plan.join_n, plan);
+        if (threadIdx.x == 0)
+            __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
 }
 
 __global__ void fill_u64_kernel(uint64_t *p, int64_t n, uint64_t v) {
@@ -1054,6 +1125,23 @@ hipError_t launch_ring(const GemmProblem &p, hipStream_t stream) {
     // one workgroup per CU, each taking several tiles; the four-wave form one workgroup per tile
     const int64_t g = WGM * WGN == 4 ? nt : persistent_grid();
     const dim3 grid((unsigned)(nt < g ? nt : g)), block(64 * WGM * WGN);
+    if (p.layout != kLayoutRowMajor) {
+        if (p.plan.chunk_rows != 0) return hipErrorInvalidValue;
+#define SPTL_RING_LAYOUT(L)                                                                                         \
+    do {                                                                                                            \
+        if (p.c_f32)                                                                                                \
+            hipLaunchKernelGGL((gemm_ring_kernel<WGM, WGN, SLOTS, true, false, L>), grid, block, 0, stream, p,      \
+                               (int)tm, (int)tn);                                                                   \
+        else                                                                                                        \
+            hipLaunchKernelGGL((gemm_ring_kernel<WGM, WGN, SLOTS, false, false, L>), grid, block, 0, stream, p,     \
+                               (int)tm, (int)tn);                                                                   \
+    } while (0)
+        if (p.layout == kLayoutAKMajor) SPTL_RING_LAYOUT(kLayoutAKMajor);
+        else if (p.layout == kLayoutBNMajor) SPTL_RING_LAYOUT(kLayoutBNMajor);
+        else return hipErrorInvalidValue;
+#undef SPTL_RING_LAYOUT
+        return hipGetLastError();
+    }
     const bool chunked = p.plan.chunk_rows != 0;
     if (p.c_f32 && chunked)
         hipLaunchKernelGGL((gemm_ring_kernel<WGM, WGN, SLOTS, true, true>), grid, block, 0, stream, p, (int)tm, (int)tn);
@@ -1116,6 +1204,8 @@ int forced_config() {
 }
 
 int resolve(const GemmProblem &p, GemmTile t) {
+    if (p.layout != kLayoutRowMajor)  // the other layouts exist on the ring kernels only
+        return p.k >= kFourWaveMinK ? k256x256ring4 : k256x256ring;
     if (p.plan.chunk_rows) {  // chunk-ordered: the tile height must divide the chunk
         if (forced_config() >= 0 && p.plan.chunk_rows % config_rows(forced_config()) == 0)
             return forced_config();
@@ -1143,6 +1233,11 @@ int chunk_tile_rows(int64_t chunk_rows) {
     if (chunk_rows > 0 && chunk_rows % 256 == 0) return 256;
     if (chunk_rows > 0 && chunk_rows % 128 == 0) return 128;
     return 0;
+}
+
+hipError_t launch_stage_join(const ChunkPlan &plan, hipStream_t stream) {
+    hipLaunchKernelGGL(stage_join_kernel, dim3(1), dim3(64), 0, stream, plan);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t stream) {

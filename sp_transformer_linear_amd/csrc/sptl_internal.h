@@ -81,6 +81,13 @@ struct ChunkPlan {
 // Row-major with leading dimensions lda, ldb, ldc (elements).  K and N multiples of 8,
 // pointers 16-byte aligned.  Every tile configuration uses the same MFMA instruction and
 // the same ascending K order, so the result bits do not depend on the tiling.
+// Operand layouts of a GEMM C[m, n] = sum_k A(i, k) B(k, j):
+//   kLayoutRowMajor  A(i, k) = a[i lda + k], B(k, j) = b[k ldb + j]
+//   kLayoutAKMajor   A(i, k) = a[k lda + i] (a weight gradient's transposed activation)
+//   kLayoutBNMajor   B(k, j) = b[j ldb + k] (an input gradient's transposed weight)
+// The layouts other than row-major run on the 256 x 256 ring kernels only, never chunk-ordered.
+constexpr int kLayoutRowMajor = 0, kLayoutAKMajor = 1, kLayoutBNMajor = 2;
+
 struct GemmProblem {
     const uint16_t *a;
     const uint16_t *b;
@@ -89,6 +96,7 @@ struct GemmProblem {
     int64_t lda, ldb, ldc;
     bool c_f32;
     ChunkPlan plan;   // plan.chunk_rows == 0: plain GEMM
+    int layout = kLayoutRowMajor;
 };
 
 enum class GemmTile { T256x256, T128x128, Auto };
@@ -105,6 +113,10 @@ int chunk_tile_rows(int64_t chunk_rows);
 
 // Fills n 64-bit words with v on `stream` (a kernel, so it is safe inside graph capture).
 hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t stream);
+
+// Launches the one-wave kernel that waits for every copy of a staged call (plan: n_chunks, ready,
+// join, the end counters and words of the call) and then reports the call done.
+hipError_t launch_stage_join(const ChunkPlan &plan, hipStream_t stream);
 
 // Copies `bytes` (a multiple of 16; both pointers 16-byte aligned) with a kernel on the compute
 // units: `workgroups` workgroups of 256 threads, or a grid sized to the copy when 0 (sptl_copy.hip).

@@ -55,6 +55,7 @@ _SIGS = {
                                   _int, _ptrs, _vp, _vp, _vp, _int, _vp], _int),
     "gemm_partial": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp], _int),
     "gemm_rs_chunked": ([_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _ptrs, _vp], _int),
+    "agmm_backward": ([_vp, _i64, _i64, _i64, _int, _int, _ptrs, _vp, _vp, _vp, _vp, _vp, _int, _vp], _int),
     "reduce_residual_rmsnorm": ([_vp, _i64, _i64, _int, _ptrs, _vp, _vp, ctypes.c_float, _vp, _vp,
                                  _vp], _int),
     "dtp_accumulate": ([_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _ptrs, _vp, ctypes.c_float, _vp,
@@ -106,6 +107,12 @@ def raw_agmm_chunked_noalloc(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, 
                              y, y_dtype, compute) -> int:
     return _lib.agmm_chunked_noalloc(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, _ptr_array(shard_src),
                                      x_gathered, w, y, y_dtype, compute)
+
+
+def raw_agmm_backward(ctx, seq_len, hidden, n_local, tp, rank, shard_src, x_gathered, w, dy, dx, dw, dw_dtype,
+                      compute) -> int:
+    return _lib.agmm_backward(ctx, seq_len, hidden, n_local, tp, rank, _ptr_array(shard_src), x_gathered, w, dy, dx,
+                              dw, dw_dtype, compute)
 
 
 def raw_gemm_rs_chunked(ctx, seq_len, k_local, hidden, tp, rank, a, w, partial, dst, compute) -> int:
@@ -263,6 +270,22 @@ def reduce_norm_agmm_chunked(partials, residual, gamma, eps: float, shards, x_ga
                                         n_chunks, rank, src, _dev_ptr(x_gathered, torch.bfloat16, "x_gathered"),
                                         _dev_ptr(w, torch.bfloat16, "w", (K, N)), _dev_ptr(y, y.dtype, "y", (M, N)),
                                         _out_dtype(y), _stream(compute)))
+
+
+def agmm_backward(shards, x_gathered, w, dy, dx, dw, *, rank: int = 0, compute=None,
+                  ctx: Optional[Context] = None) -> None:
+    """Backward of agmm_chunked: x_gathered = concat(shards) (re-gathered under the dx GEMM),
+    dx = dy @ w^T, dw = x_gathered^T @ dy (see include/sptl.h)."""
+    torch = _torch()
+    tp = len(shards)
+    M, K = x_gathered.shape
+    N = w.shape[1]
+    rows = M // tp if tp else 0
+    src = [_dev_ptr(s, torch.bfloat16, f"shards[{q}]", (rows, K)) for q, s in enumerate(shards)]
+    _check(raw_agmm_backward(_h(ctx), M, K, N, tp, rank, src, _dev_ptr(x_gathered, torch.bfloat16, "x_gathered"),
+                             _dev_ptr(w, torch.bfloat16, "w", (K, N)), _dev_ptr(dy, torch.bfloat16, "dy", (M, N)),
+                             _dev_ptr(dx, torch.bfloat16, "dx", (M, K)), _dev_ptr(dw, dw.dtype, "dw", (K, N)),
+                             _out_dtype(dw), _stream(compute)))
 
 
 def gemm_rs_chunked(a, w, partial, dst, *, rank: int = 0, stream=None, ctx: Optional[Context] = None) -> None:

@@ -166,3 +166,16 @@ def test_gemm_rs_validation(sptl, kw, status):
              compute=None)
     d.update(kw)
     assert sptl.raw_gemm_rs_chunked(**d) == status, sptl.last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dy=None), 1), (dict(dx=None), 1), (dict(dw=None), 1), (dict(shard_src=[A, None]), 1),
+    (dict(tp=0), 6), (dict(tp=65), 6), (dict(rank=2), 6), (dict(hidden=0), 2), (dict(seq_len=-1), 2),
+    (dict(seq_len=257), 3), (dict(n_local=12), 3), (dict(hidden=20), 3), (dict(dw_dtype=2), 5),
+    (dict(dx=A + 2), 4), (dict(shard_src=[A, A + 8]), 4),
+])
+def test_agmm_backward_validation(sptl, kw, status):
+    d = dict(ctx=None, seq_len=256, hidden=128, n_local=64, tp=2, rank=0, shard_src=[A, A], x_gathered=A, w=A,
+             dy=A, dx=A, dw=A, dw_dtype=1, compute=None)
+    d.update(kw)
+    assert sptl.raw_agmm_backward(**d) == status, sptl.last_error()
