@@ -49,6 +49,12 @@ __all__ = [
     "reduce_residual_rmsnorm",
     "dtp_accumulate",
     "dtp_sequence",
+    "colocated_affinity",
+    "balanced_neuron_assignment",
+    "best_head_layout",
+    "affinity_layout",
+    "layout_permutation",
+    "permute",
 ]
 
 
@@ -247,3 +253,92 @@ def dtp_sequence(x0, owns: Sequence, peers: Sequence[Sequence], delta: int, gamm
         for p in peers[l]:
             x_imm = x_imm + _as_f64(p)
     return steps, x, x_imm
+
+
+# ---------------------------------------------------------------------------------------
+# (5) affinity-aware sharding for delayed TP                        [DTP abstract]
+# ---------------------------------------------------------------------------------------
+
+def colocated_affinity(affinity, head_device, neuron_device) -> float:
+    """Co-located affinity of a layout: the sum of affinity[h, j] over every KV head h and FFN
+    neuron j placed on the same device [DTP abstract: "maximising the affinity between the KV
+    heads and the FFN neurons co-located on a device"]."""
+    a = np.asarray(affinity, dtype=np.float64)
+    hd = np.asarray(head_device)
+    nd = np.asarray(neuron_device)
+    return float(np.sum(a * (hd[:, None] == nd[None, :])))
+
+
+def balanced_neuron_assignment(affinity, head_device, tp: int) -> np.ndarray:
+    """For fixed heads, the neuron layout with n_neurons / tp neurons per device of largest
+    co-located affinity [DTP abstract: "an exact balanced assignment of neurons"].
+
+    Neuron j placed on device d contributes the sum of its affinities to the heads on d.  The
+    balanced assignment is a linear assignment of neurons to device slots (each device repeated
+    n_neurons / tp times), solved exactly by scipy's linear_sum_assignment (a library step)."""
+    from scipy.optimize import linear_sum_assignment
+    a = np.asarray(affinity, dtype=np.float64)
+    hd = np.asarray(head_device)
+    n = a.shape[1]
+    value = np.stack([a[hd == d].sum(axis=0) for d in range(tp)])   # [tp, n_neurons]
+    slot_device = np.repeat(np.arange(tp), n // tp)                  # [n_neurons] slots
+    rows, cols = linear_sum_assignment(value[slot_device].T, maximize=True)
+    out = np.empty(n, dtype=np.int64)
+    out[rows] = slot_device[cols]
+    return out
+
+
+def best_head_layout(affinity, neuron_device, tp: int) -> np.ndarray:
+    """For fixed neurons, the head layout with n_heads / tp heads per device of largest
+    co-located affinity, by trying every one [DTP abstract: "an exhaustive search over the KV
+    head partitions"].  Devices are told apart by the neurons they hold, so layouts are
+    assignments of heads to devices.  They are tried in lexicographic order of (device of head
+    0, device of head 1, ...) and the first best one is kept."""
+    import itertools
+    a = np.asarray(affinity, dtype=np.float64)
+    nd = np.asarray(neuron_device)
+    n_heads = a.shape[0]
+    t = np.stack([a[:, nd == d].sum(axis=1) for d in range(tp)], axis=1)  # [n_heads, tp]
+    best, best_s = None, -np.inf
+    for cand in itertools.product(range(tp), repeat=n_heads):
+        if any(cand.count(d) != n_heads // tp for d in range(tp)):
+            continue
+        s = sum(t[h, d] for h, d in enumerate(cand))
+        if s > best_s:
+            best, best_s = cand, s
+    return np.array(best, dtype=np.int64)
+
+
+def affinity_layout(affinity, tp: int, head_device, max_rounds: int = 100):
+    """Coordinate ascent on the co-located affinity [DTP abstract: "a coordinate-ascent optimiser
+    that alternates an exact balanced assignment of neurons with an exhaustive search over the
+    KV head partitions"], from the head layout given: each round assigns the neurons for the
+    current heads, then searches the heads for those neurons; it stops after a round that does
+    not raise the score (or after max_rounds).  Returns (heads, neurons, score, rounds)."""
+    hd = np.asarray(head_device, dtype=np.int64)
+    prev = -np.inf
+    rounds = 0
+    while rounds < max_rounds:
+        nd = balanced_neuron_assignment(affinity, hd, tp)
+        hd = best_head_layout(affinity, nd, tp)
+        s = colocated_affinity(affinity, hd, nd)
+        rounds += 1
+        if not s > prev:
+            break
+        prev = s
+    return hd, nd, s, rounds
+
+
+def layout_permutation(layout, tp: int, group: int = 1) -> np.ndarray:
+    """Index order that shards a layout: device 0's items ascending, then device 1's, ...; item
+    i stands for the group indices i*group .. i*group + group - 1 [DTP abstract: "permuting the
+    dense model before sharding"]."""
+    lay = np.asarray(layout)
+    items = np.concatenate([np.flatnonzero(lay == d) for d in range(tp)])
+    return (items[:, None] * group + np.arange(group)[None, :]).reshape(-1)
+
+
+def permute(x, perm, dim: int) -> np.ndarray:
+    """x with its rows (dim 0) or columns (dim 1) taken in the order perm."""
+    return np.take(np.asarray(x), np.asarray(perm), axis=dim)
+

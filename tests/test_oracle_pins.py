@@ -266,6 +266,109 @@ def check_backward_special(impl):
     assert np.array_equal(dw, want)
 
 
+def _balanced_layouts(n, tp):
+    import itertools
+    for cand in itertools.product(range(tp), repeat=n):
+        if all(cand.count(d) == n // tp for d in range(tp)):
+            yield np.array(cand)
+
+
+def check_affinity_golden(impl):
+    g = load_golden("affinity_worked_tp2.txt")
+    a = g["affinity"]
+    hd, nd = g["heads"][0].astype(int), g["neurons"][0].astype(int)
+    assert impl.colocated_affinity(a, hd, nd) == g["score"][0, 0]
+    best_nd = impl.balanced_neuron_assignment(a, hd, 2)
+    assert np.bincount(best_nd, minlength=2).tolist() == [2, 2]
+    assert impl.colocated_affinity(a, hd, best_nd) == g["best_neuron_score"][0, 0]
+    best_hd = impl.best_head_layout(a, nd, 2)
+    assert np.array_equal(best_hd, g["best_heads"][0].astype(int))
+    assert impl.colocated_affinity(a, best_hd, nd) == g["best_head_score"][0, 0]
+
+
+def check_balanced_assignment_brute(impl):
+    """The neuron step against every balanced neuron layout of tiny instances."""
+    rng = np.random.default_rng(31)
+    for n_heads, n, tp in ((2, 6, 2), (3, 6, 3), (4, 8, 4), (2, 8, 2)):
+        a = rng.standard_normal((n_heads, n))
+        hd = np.arange(n_heads) % tp
+        got = impl.balanced_neuron_assignment(a, hd, tp)
+        assert np.bincount(got, minlength=tp).tolist() == [n // tp] * tp
+        best = max(O.colocated_affinity(a, hd, nd) for nd in _balanced_layouts(n, tp))
+        assert abs(impl.colocated_affinity(a, hd, got) - best) <= 1e-12 * (1 + abs(best))
+
+
+def check_head_step_is_an_assignment(impl):
+    """The head step is itself a balanced assignment of heads to device slots: its optimum must
+    match an independent linear-assignment solve (scipy), at head counts past the tiny ones."""
+    from scipy.optimize import linear_sum_assignment
+    rng = np.random.default_rng(32)
+    for n_heads, n, tp in ((8, 40, 4), (6, 30, 3), (8, 16, 2)):
+        a = rng.standard_normal((n_heads, n))
+        nd = np.arange(n) % tp
+        got = impl.best_head_layout(a, nd, tp)
+        assert np.bincount(got, minlength=tp).tolist() == [n_heads // tp] * tp
+        t = np.stack([a[:, nd == d].sum(axis=1) for d in range(tp)], axis=1)
+        slots = np.repeat(np.arange(tp), n_heads // tp)
+        r, c = linear_sum_assignment(t[:, slots], maximize=True)
+        assert abs(impl.colocated_affinity(a, got, nd) - t[:, slots][r, c].sum()) <= 1e-12 * (1 + abs(t).sum())
+
+
+def check_affinity_planted(impl):
+    """Planted groups (affinity 1 inside a group, 0 across): from the planted head layout the
+    ascent reaches the planted layout, whose score (every same-group pair co-located) is the
+    largest any layout can have."""
+    rng = np.random.default_rng(33)
+    n_heads, n, tp = 8, 64, 4
+    gh = rng.permutation(np.arange(n_heads) % tp)
+    gn = rng.permutation(np.arange(n) % tp)
+    a = (gh[:, None] == gn[None, :]).astype(np.float64)
+    hd, nd, score, rounds = impl.affinity_layout(a, tp, gh)
+    assert score == a.sum()
+    assert np.array_equal(nd, gn) and np.array_equal(hd, gh)
+
+
+def check_affinity_ascent(impl):
+    """The ascent ends at a layout that neither step improves, its score is the layout's, and it
+    runs until a round brings nothing (this instance needs three rounds)."""
+    rng = np.random.default_rng(11)
+    a = rng.random((6, 24))
+    hd, nd, score, rounds = impl.affinity_layout(a, 3, np.arange(6) // 2)
+    assert rounds == 3
+    assert score == O.colocated_affinity(a, hd, nd)
+    assert O.colocated_affinity(a, hd, impl.balanced_neuron_assignment(a, hd, 3)) <= score + 1e-12
+    assert O.colocated_affinity(a, impl.best_head_layout(a, nd, 3), nd) <= score + 1e-12
+    # every round's score is at least the last one's
+    h = np.arange(6) // 2
+    last = -np.inf
+    for _ in range(rounds):
+        n_ = impl.balanced_neuron_assignment(a, h, 3)
+        h = impl.best_head_layout(a, n_, 3)
+        s_ = O.colocated_affinity(a, h, n_)
+        assert s_ >= last
+        last = s_
+
+
+def check_layout_permutation(impl):
+    rng = np.random.default_rng(34)
+    lay = rng.permutation(np.arange(12) % 3)
+    for group in (1, 4):
+        p = impl.layout_permutation(lay, 3, group)
+        assert np.array_equal(np.sort(p), np.arange(12 * group))           # a permutation
+        blocks = p.reshape(3, -1)
+        for d in range(3):                                                  # block d: device d's items
+            items = blocks[d].reshape(-1, group)[:, 0] // group
+            assert np.all(lay[items] == d) and np.all(np.diff(items) > 0)
+            assert np.array_equal(blocks[d].reshape(-1, group), items[:, None] * group + np.arange(group))
+    x = rng.standard_normal((5, 12))
+    p = rng.permutation(12)
+    inv = np.argsort(p)
+    assert np.array_equal(impl.permute(impl.permute(x, p, 1), inv, 1), x)
+    assert np.array_equal(impl.permute(x, p, 1), impl.permute(x.T, p, 0).T)
+    assert np.array_equal(impl.permute(x, np.arange(5), 0), x)
+    assert np.array_equal(impl.permute(x, p, 1)[:, 3], x[:, p[3]])
+
+
 def check_rmsnorm_golden(impl):
     g = load_golden("rmsnorm_worked.txt")
     for case, nparts in (("a", 0), ("b", 2), ("c", 0)):
@@ -400,7 +503,9 @@ CHECKS = [check_bf16_decode, check_round_to_bf16, check_f64_to_bf16_bits, check_
           check_tp_identity, check_rmsnorm_golden, check_rmsnorm_closed_forms,
           check_rmsnorm_brute, check_norm_commutes_with_gather,
           check_reduce_uses_each_partial_once, check_dtp_golden, check_dtp_invariants,
-          check_dtp_store_bf16, check_backward_is_the_gradient, check_backward_brute, check_backward_special]
+          check_dtp_store_bf16, check_backward_is_the_gradient, check_backward_brute, check_backward_special,
+          check_affinity_golden, check_balanced_assignment_brute, check_head_step_is_an_assignment,
+          check_affinity_planted, check_affinity_ascent, check_layout_permutation]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
@@ -541,6 +646,33 @@ def _bwd_gather_reversed(shards, w, dy):
     return x, g @ O._as_f64(w).T, x.T @ g
 
 
+def _affinity_cross(affinity, head_device, neuron_device):   # counts pairs on different devices
+    a = np.asarray(affinity, dtype=np.float64)
+    return float(np.sum(a * (np.asarray(head_device)[:, None] != np.asarray(neuron_device)[None, :])))
+
+
+def _neurons_unbalanced(affinity, head_device, tp):   # each neuron to its best device, no capacity
+    a = np.asarray(affinity, dtype=np.float64)
+    hd = np.asarray(head_device)
+    value = np.stack([a[hd == d].sum(axis=0) for d in range(tp)])
+    return np.argmax(value, axis=0)
+
+
+def _heads_not_searched(affinity, neuron_device, tp):   # keeps the contiguous head layout
+    n_heads = np.asarray(affinity).shape[0]
+    return np.arange(n_heads) // (n_heads // tp)
+
+
+def _ascent_one_round(affinity, tp, head_device, max_rounds=100):
+    return O.affinity_layout(affinity, tp, head_device, 1)
+
+
+def _permutation_interleaved(layout, tp, group=1):     # items in index order, not grouped by device
+    lay = np.asarray(layout)
+    items = np.argsort(lay, kind="stable")[::-1]
+    return (items[:, None] * group + np.arange(group)[None, :]).reshape(-1)
+
+
 MUTANTS = {
     "rmsnorm_sum_not_mean": dict(rmsnorm=_rms_sum),
     "rmsnorm_eps_outside_sqrt": dict(rmsnorm=_rms_eps_outside),
@@ -558,6 +690,11 @@ MUTANTS = {
     "backward_dx_untransposed": dict(agmm_backward=_bwd_dx_untransposed),
     "backward_dw_tokens_misaligned": dict(agmm_backward=_bwd_dw_tokens_misaligned),
     "backward_gather_reversed": dict(agmm_backward=_bwd_gather_reversed),
+    "affinity_counts_cross_device_pairs": dict(colocated_affinity=_affinity_cross),
+    "neuron_step_ignores_balance": dict(balanced_neuron_assignment=_neurons_unbalanced),
+    "head_step_does_not_search": dict(best_head_layout=_heads_not_searched),
+    "ascent_stops_after_one_round": dict(affinity_layout=_ascent_one_round),
+    "permutation_blocks_reversed": dict(layout_permutation=_permutation_interleaved),
 }
 
 
