@@ -801,6 +801,71 @@ def main():
         "input_gen_s": round(t_gen, 2),
     }
 
+    # ---- delayed-TP sharding of a Qwen3-0.6B-shaped model (the delayed-TP workload's model) ----
+    # ("Affinity-Aware Sharding for Delayed Tensor Parallelism", abstract.)  28 layers of 8 KV
+    # heads (128 wide, 2 query heads each) and 3072 FFN neurons over tp devices, synthetic
+    # affinities (synth.synthetic_affinity).  Per layer the optimiser runs from the contiguous
+    # head layout and from 4 seeded random ones and keeps the best; then every layer's weights
+    # are permuted on the GPU (permute_bf16), which is what the layout costs at load time.
+    def dtp_sharding(tp_, layers=28, n_kv=8, q_per_kv=2, hd_dim=128, hidden=1024, ffn=3072, seeds=4):
+        t0 = time.perf_counter()
+        contiguous, best_scores, rounds = [], [], []
+        layouts = []
+        for layer in range(layers):
+            a = synth.synthetic_affinity(1000 + layer, n_kv, ffn, tp_)
+            starts = [np.arange(n_kv) // (n_kv // tp_)] + [
+                np.random.default_rng((layer, s_)).permutation(np.arange(n_kv) // (n_kv // tp_)) for s_ in range(seeds)]
+            best = None
+            for st in starts:
+                r = sptl.dtp_affinity_layout(a, tp_, st)
+                rounds.append(r[3])
+                if best is None or r[2] > best[2]:
+                    best = r
+            contiguous.append(sptl.dtp_colocated_affinity(a, tp_, starts[0], np.arange(ffn) // (ffn // tp_)))
+            best_scores.append(best[2])
+            layouts.append(best)
+        t_opt = time.perf_counter() - t0
+        # the layer's weights, [in, out]: W_q, W_k, W_v, W_o, W_gate, W_up, W_down
+        shapes = [((hidden, n_kv * q_per_kv * hd_dim), 1, q_per_kv * hd_dim), ((hidden, n_kv * hd_dim), 1, hd_dim),
+                  ((hidden, n_kv * hd_dim), 1, hd_dim), ((n_kv * q_per_kv * hd_dim, hidden), 0, q_per_kv * hd_dim),
+                  ((hidden, ffn), 1, 0), ((hidden, ffn), 1, 0), ((ffn, hidden), 0, 0)]
+        srcs = [torch.empty(sh, dtype=torch.bfloat16, device=dev).normal_() for sh, _, _ in shapes]
+        dsts = [torch.empty_like(x) for x in srcs]
+        perms = []
+        for hd_l, nd_l, _, _ in layouts:
+            pl = []
+            for (sh, dim, group) in shapes:
+                p_ = (sptl.dtp_layout_permutation(hd_l, tp_, group) if group else sptl.dtp_layout_permutation(nd_l, tp_))
+                pl.append(torch.from_numpy(p_).to(dev))
+            perms.append(pl)
+        nbytes = layers * sum(2 * 2 * x.numel() for x in srcs)
+        for _ in range(2):
+            for pl in perms:
+                for x, y_, p_, (sh, dim, _) in zip(srcs, dsts, pl, shapes):
+                    sptl.permute_bf16(x, y_, p_, dim=dim, stream=cs, ctx=ctx)
+        torch.cuda.synchronize()
+        a_, b_ = ev(), ev()
+        a_.record(cs)
+        for pl in perms:
+            for x, y_, p_, (sh, dim, _) in zip(srcs, dsts, pl, shapes):
+                sptl.permute_bf16(x, y_, p_, dim=dim, stream=cs, ctx=ctx)
+        b_.record(cs)
+        torch.cuda.synchronize()
+        ctx.check()
+        ms_perm = a_.elapsed_time(b_)
+        del srcs, dsts, perms
+        gain = np.array(best_scores) / np.array(contiguous)
+        return {"model": "Qwen3-0.6B-shaped (28 layers, 8 KV heads x 128, 16 query heads, FFN 3072, hidden 1024)",
+                "affinity": "synthetic (exp(N(0,1)), x3 within hidden groups)", "tp": tp_,
+                "starts_per_layer": seeds + 1, "optimizer_s": round(t_opt, 3),
+                "rounds_max": int(max(rounds)), "rounds_mean": round(float(np.mean(rounds)), 2),
+                "score_vs_contiguous_mean": round(float(gain.mean()), 4),
+                "score_vs_contiguous_min": round(float(gain.min()), 4),
+                "permute_ms": round(ms_perm, 4), "permute_bytes": nbytes,
+                "permute_GBps": round(nbytes / (ms_perm * 1e-3) / 1e9, 1)}
+
+    out["dtp_sharding"] = dtp_sharding(wd.tp)
+
     # ---- other workloads, after the timed region: the same calls, fewer steps ---------------
     del L, D
     torch.cuda.empty_cache()

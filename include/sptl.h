@@ -72,6 +72,7 @@ typedef enum {
 #define SPTL_MAX_CHUNKS 512    /* chunk count of agmm_chunked                            */
 #define SPTL_MAX_K 2097152     /* GEMM reduction size (hidden of agmm_chunked, k_local)  */
 #define SPTL_MAX_N 8388608     /* GEMM output width (n_local, hidden of gemm_partial)    */
+#define SPTL_MAX_HEAD_LAYOUTS 67108864LL /* head layouts dtp_affinity_layout tries per round */
 
 /* Create a context on HIP device `device`: events, small device buffers and the SDMA stager
  * are created now (the copy stream of the per-chunk path on its first use), together with the
@@ -383,6 +384,51 @@ int dtp_accumulate(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int tp, int d
                    int module_idx, void *residual, const void *own_partial,
                    const void *const *delayed_peers, const void *gamma, float eps,
                    void *y, void *stream);
+
+/*
+ * (5) Affinity-aware sharding for delayed TP: the layout of KV heads and FFN neurons over the
+ * devices, and the permutation of the dense weights before sharding.
+ *
+ * [DTP abstract]: delayed TP breaks the permutation symmetry of FFN neurons and of KV heads, so
+ * which heads and neurons share a device matters.  The layout maximises the co-located affinity
+ *     score = sum over devices d, heads h on d, neurons j on d of affinity[h][j]
+ * (affinity[h][j]: how much neuron j's output depends on head h, a first-order estimate the
+ * caller computes from a trained model), with n_heads / tp heads and n_neurons / tp neurons per
+ * device, by coordinate ascent: each round assigns the neurons exactly for the current heads (a
+ * balanced assignment), then tries every head layout for those neurons and keeps the best;
+ * it stops after a round that does not raise the score.  Host code; no GPU is used.
+ *   affinity      HOST [n_heads, n_neurons] float64, row-major, finite
+ *   head_device   HOST [n_heads] int: in, the starting layout (n_heads / tp heads per device, e.g.
+ *                 the contiguous one or a seeded random one); out, the optimised one
+ *   neuron_device HOST [n_neurons] int, out
+ *   score         out: the co-located affinity of the result;  rounds: out, may be NULL
+ *   n_heads % tp == 0, n_neurons % tp == 0, 1 <= tp <= 64, max_rounds >= 1.  Ties go to the
+ *   first layout in the order the search takes (lower device numbers for lower indices).
+ * SPTL_E_UNSUPPORTED when a round would try more than SPTL_MAX_HEAD_LAYOUTS head layouts
+ * (n_heads! / ((n_heads / tp)!)^tp); SPTL_E_RANGE for a starting layout that is not balanced.
+ */
+int dtp_affinity_layout(const double *affinity, int n_heads, int n_neurons, int tp, int max_rounds,
+                        int *head_device, int *neuron_device, double *score, int *rounds);
+
+/* The co-located affinity of a given layout (definition above).  Every device index must lie
+ * in [0, tp); the layout need not be balanced. */
+int dtp_colocated_affinity(const double *affinity, int n_heads, int n_neurons, int tp,
+                           const int *head_device, const int *neuron_device, double *score);
+
+/* The permutation that shards a layout: perm lists the items of device 0 in ascending order,
+ * then those of device 1, and so on, each item i expanded to the `group` consecutive indices
+ * i*group .. i*group + group - 1 (e.g. a KV head's head_dim columns).  HOST arrays: layout [n],
+ * perm [n * group] (out).  Device d's shard is then the d-th block of the permuted tensor when
+ * the layout is balanced. */
+int dtp_layout_permutation(const int *layout, int n, int tp, int group, int32_t *perm);
+
+/* [DTP abstract] "permuting the dense model before sharding": dst = src with its rows (dim 0:
+ * dst[i, :] = src[perm[i], :]) or its columns (dim 1: dst[:, j] = src[:, perm[j]]) permuted.
+ *   src, dst [rows, cols] bf16, distinct, 16-byte aligned; cols % 8 == 0
+ *   perm     DEVICE int32 array [rows] (dim 0) or [cols] (dim 1), 4-byte aligned
+ * An index out of range gives zeros in its place; sptl_ctx_check then reports SPTL_E_ASYNC. */
+int permute_bf16(sptl_ctx *ctx, const void *src, void *dst, int64_t rows, int64_t cols, int dim,
+                 const int32_t *perm, void *stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsptl.so")
 ARCH = "gfx950"
 
-SOURCES = ["sptl_abi.cpp", "sptl_stager.cpp", "sptl_gemm.hip", "sptl_epilogue.hip", "sptl_noalloc.hip", "sptl_copy.hip"]
+SOURCES = ["sptl_abi.cpp", "sptl_stager.cpp", "sptl_gemm.hip", "sptl_epilogue.hip", "sptl_noalloc.hip", "sptl_copy.hip", "sptl_affinity.cpp"]
 
 # packed-fp32 instructions are disabled for all device code (the compiler would otherwise
 # form them from ordinary float code).

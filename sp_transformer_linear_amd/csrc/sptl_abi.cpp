@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -13,6 +14,7 @@
 #include <vector>
 
 #include "sptl.h"
+#include "sptl_affinity.h"
 #include "sptl_internal.h"
 #include "sptl_noalloc.h"
 #include "sptl_stager.h"
@@ -388,10 +390,11 @@ int sptl_ctx_check(sptl_ctx *ctx) {
             return fail(rc == -2 ? SPTL_E_ASYNC : SPTL_E_HIP,
                         rc == -2 ? "sptl_ctx_check: the copies of a timed-out call did not complete"
                                  : "sptl_ctx_check: waiting for staged calls failed");
-    int flag = 0;
-    SPTL_HIP(hipMemcpy(&flag, ctx->err_dev, sizeof flag, hipMemcpyDeviceToHost));
-    if (flag) {
-        SPTL_HIP(hipMemset(ctx->err_dev, 0, sizeof flag));
+    int flag[2] = {0, 0};  // [0]: a staging wait timed out; [1]: a permutation index was out of range
+    SPTL_HIP(hipMemcpy(flag, ctx->err_dev, sizeof flag, hipMemcpyDeviceToHost));
+    if (flag[0] || flag[1]) SPTL_HIP(hipMemset(ctx->err_dev, 0, sizeof flag));
+    if (flag[1]) return fail(SPTL_E_ASYNC, "permute_bf16: an index was out of range (zeros written there)");
+    if (flag[0]) {
         if (ctx->stager) (void)sptl::stager_take_timeouts(ctx->stager);  // the same report
         return fail(SPTL_E_ASYNC, "a staging wait timed out; the affected agmm_chunked results are invalid");
     }
@@ -993,6 +996,84 @@ int agmm_backward(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_loca
     if (sptl::stager_submit(ctx->stager, call, std::move(pieces), &why))
         return fail(SPTL_E_HIP, "%s: %s", fn, why.c_str());
     if (he != hipSuccess) return hip_fail(he, "agmm_backward: dw kernel launch");
+    return SPTL_OK;
+}
+
+int dtp_colocated_affinity(const double *affinity, int n_heads, int n_neurons, int tp, const int *head_device,
+                           const int *neuron_device, double *score) {
+    static const char *fn = "dtp_colocated_affinity";
+    if (!affinity || !head_device || !neuron_device || !score) return fail(SPTL_E_NULL, "%s: NULL pointer argument", fn);
+    if (n_heads <= 0 || n_neurons <= 0) return fail(SPTL_E_SHAPE, "%s: n_heads=%d n_neurons=%d", fn, n_heads, n_neurons);
+    if (tp < 1) return fail(SPTL_E_RANGE, "%s: tp=%d", fn, tp);
+    for (int h = 0; h < n_heads; ++h)
+        if (head_device[h] < 0 || head_device[h] >= tp) return fail(SPTL_E_RANGE, "%s: head_device[%d]", fn, h);
+    for (int j = 0; j < n_neurons; ++j)
+        if (neuron_device[j] < 0 || neuron_device[j] >= tp) return fail(SPTL_E_RANGE, "%s: neuron_device[%d]", fn, j);
+    *score = sptl::colocated_affinity(affinity, n_heads, n_neurons, head_device, neuron_device);
+    return SPTL_OK;
+}
+
+int dtp_affinity_layout(const double *affinity, int n_heads, int n_neurons, int tp, int max_rounds, int *head_device,
+                        int *neuron_device, double *score, int *rounds) {
+    static const char *fn = "dtp_affinity_layout";
+    if (!affinity || !head_device || !neuron_device || !score) return fail(SPTL_E_NULL, "%s: NULL pointer argument", fn);
+    if (n_heads <= 0 || n_neurons <= 0) return fail(SPTL_E_SHAPE, "%s: n_heads=%d n_neurons=%d", fn, n_heads, n_neurons);
+    if (tp < 1 || tp > 64) return fail(SPTL_E_RANGE, "%s: tp=%d not in [1, 64]", fn, tp);
+    if (n_heads % tp || n_neurons % tp)
+        return fail(SPTL_E_DIVISIBILITY, "%s: n_heads=%d and n_neurons=%d must be multiples of tp=%d", fn, n_heads,
+                    n_neurons, tp);
+    if (max_rounds < 1) return fail(SPTL_E_RANGE, "%s: max_rounds=%d", fn, max_rounds);
+    if (sptl::head_layout_count(n_heads, tp) > SPTL_MAX_HEAD_LAYOUTS)
+        return fail(SPTL_E_UNSUPPORTED, "%s: %d heads over %d devices have more than %lld layouts to search", fn,
+                    n_heads, tp, (long long)SPTL_MAX_HEAD_LAYOUTS);
+    std::vector<int> per(tp, 0);
+    for (int h = 0; h < n_heads; ++h) {
+        if (head_device[h] < 0 || head_device[h] >= tp) return fail(SPTL_E_RANGE, "%s: head_device[%d]", fn, h);
+        per[head_device[h]]++;
+    }
+    for (int d = 0; d < tp; ++d)
+        if (per[d] != n_heads / tp)
+            return fail(SPTL_E_RANGE, "%s: the starting head layout puts %d heads on device %d (not %d)", fn, per[d], d,
+                        n_heads / tp);
+    for (int64_t i = 0; i < (int64_t)n_heads * n_neurons; ++i)
+        if (!std::isfinite(affinity[i])) return fail(SPTL_E_RANGE, "%s: affinity[%lld] is not finite", fn, (long long)i);
+    const int r = sptl::affinity_layout(affinity, n_heads, n_neurons, tp, max_rounds, head_device, neuron_device, score);
+    if (rounds) *rounds = r;
+    return SPTL_OK;
+}
+
+int dtp_layout_permutation(const int *layout, int n, int tp, int group, int32_t *perm) {
+    static const char *fn = "dtp_layout_permutation";
+    if (!layout || !perm) return fail(SPTL_E_NULL, "%s: NULL pointer argument", fn);
+    if (n <= 0 || group <= 0 || (int64_t)n * group > 0x7fffffff)
+        return fail(SPTL_E_SHAPE, "%s: n=%d group=%d", fn, n, group);
+    if (tp < 1) return fail(SPTL_E_RANGE, "%s: tp=%d", fn, tp);
+    for (int i = 0; i < n; ++i)
+        if (layout[i] < 0 || layout[i] >= tp) return fail(SPTL_E_RANGE, "%s: layout[%d]=%d", fn, i, layout[i]);
+    int64_t o = 0;
+    for (int d = 0; d < tp; ++d)
+        for (int i = 0; i < n; ++i)
+            if (layout[i] == d)
+                for (int e = 0; e < group; ++e) perm[o++] = (int32_t)((int64_t)i * group + e);
+    return SPTL_OK;
+}
+
+int permute_bf16(sptl_ctx *ctx, const void *src, void *dst, int64_t rows, int64_t cols, int dim, const int32_t *perm,
+                 void *stream) {
+    static const char *fn = "permute_bf16";
+    if (!src || !dst || !perm) return fail(SPTL_E_NULL, "%s: NULL pointer argument", fn);
+    if (rows < 0 || cols <= 0 || rows > 0x7fffffff || cols > 0x7fffffff)
+        return fail(SPTL_E_SHAPE, "%s: rows=%lld cols=%lld", fn, (long long)rows, (long long)cols);
+    if (cols % 8) return fail(SPTL_E_DIVISIBILITY, "%s: cols=%lld not a multiple of 8", fn, (long long)cols);
+    if (dim != 0 && dim != 1) return fail(SPTL_E_RANGE, "%s: dim=%d", fn, dim);
+    if (src == dst) return fail(SPTL_E_RANGE, "%s: src and dst must not be the same buffer", fn);
+    if (!aligned16(src) || !aligned16(dst)) return fail(SPTL_E_ALIGN, "%s: src and dst must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(perm) & 3u) != 0) return fail(SPTL_E_ALIGN, "%s: perm not 4-byte aligned", fn);
+    if (rows == 0) return SPTL_OK;
+    if (int rc = resolve_ctx(ctx)) return rc;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    SPTL_HIP(sptl::launch_permute(src, dst, rows, cols, dim, perm, ctx->err_dev + 1, static_cast<hipStream_t>(stream)));
     return SPTL_OK;
 }
 

@@ -118,6 +118,12 @@ hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t strea
 // join, the end counters and words of the call) and then reports the call done.
 hipError_t launch_stage_join(const ChunkPlan &plan, hipStream_t stream);
 
+// dst = src ([rows, cols] bf16, cols % 8 == 0) with rows (dim 0: dst[i, :] = src[perm[i], :]) or
+// columns (dim 1: dst[:, j] = src[:, perm[j]]) permuted; an index out of range gives zeros and
+// sets *err to 1 (sptl_copy.hip).
+hipError_t launch_permute(const void *src, void *dst, int64_t rows, int64_t cols, int dim, const int32_t *perm,
+                          int *err, hipStream_t stream);
+
 // Copies `bytes` (a multiple of 16; both pointers 16-byte aligned) with a kernel on the compute
 // units: `workgroups` workgroups of 256 threads, or a grid sized to the copy when 0 (sptl_copy.hip).
 hipError_t launch_blit(void *dst, const void *src, size_t bytes, int workgroups, hipStream_t stream);

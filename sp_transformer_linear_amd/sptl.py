@@ -55,6 +55,12 @@ _SIGS = {
                                   _int, _ptrs, _vp, _vp, _vp, _int, _vp], _int),
     "gemm_partial": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp], _int),
     "gemm_rs_chunked": ([_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _ptrs, _vp], _int),
+    "dtp_affinity_layout": ([ctypes.POINTER(ctypes.c_double), _int, _int, _int, _int, ctypes.POINTER(_int),
+                             ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)], _int),
+    "dtp_colocated_affinity": ([ctypes.POINTER(ctypes.c_double), _int, _int, _int, ctypes.POINTER(_int),
+                                ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double)], _int),
+    "dtp_layout_permutation": ([ctypes.POINTER(_int), _int, _int, _int, ctypes.POINTER(ctypes.c_int32)], _int),
+    "permute_bf16": ([_vp, _vp, _vp, _i64, _i64, _int, _vp, _vp], _int),
     "agmm_backward": ([_vp, _i64, _i64, _i64, _int, _int, _ptrs, _vp, _vp, _vp, _vp, _vp, _int, _vp], _int),
     "reduce_residual_rmsnorm": ([_vp, _i64, _i64, _int, _ptrs, _vp, _vp, ctypes.c_float, _vp, _vp,
                                  _vp], _int),
@@ -107,6 +113,55 @@ def raw_agmm_chunked_noalloc(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, 
                              y, y_dtype, compute) -> int:
     return _lib.agmm_chunked_noalloc(ctx, seq_len, hidden, n_local, tp, n_chunks, rank, _ptr_array(shard_src),
                                      x_gathered, w, y, y_dtype, compute)
+
+
+def _np_ptr(arr, ctype):
+    return arr.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def dtp_affinity_layout(affinity, tp: int, head_device=None, max_rounds: int = 100):
+    """Head and neuron layouts of largest co-located affinity by coordinate ascent (see
+    include/sptl.h).  affinity: [n_heads, n_neurons] array; head_device: the starting head layout
+    (default: contiguous).  Returns (head_device, neuron_device, score, rounds) as numpy arrays."""
+    import numpy as np
+    a = np.ascontiguousarray(affinity, dtype=np.float64)
+    n_heads, n_neurons = a.shape
+    hd = (np.arange(n_heads) // max(1, n_heads // tp) if head_device is None else np.asarray(head_device))
+    hd = np.ascontiguousarray(hd, dtype=np.intc).copy()
+    nd = np.zeros(n_neurons, dtype=np.intc)
+    score = ctypes.c_double()
+    rounds = _int()
+    _check(_lib.dtp_affinity_layout(_np_ptr(a, ctypes.c_double), n_heads, n_neurons, tp, max_rounds,
+                                    _np_ptr(hd, _int), _np_ptr(nd, _int), ctypes.byref(score), ctypes.byref(rounds)))
+    return hd, nd, score.value, rounds.value
+
+
+def dtp_colocated_affinity(affinity, tp: int, head_device, neuron_device) -> float:
+    import numpy as np
+    a = np.ascontiguousarray(affinity, dtype=np.float64)
+    hd = np.ascontiguousarray(head_device, dtype=np.intc)
+    nd = np.ascontiguousarray(neuron_device, dtype=np.intc)
+    score = ctypes.c_double()
+    _check(_lib.dtp_colocated_affinity(_np_ptr(a, ctypes.c_double), a.shape[0], a.shape[1], tp, _np_ptr(hd, _int),
+                                       _np_ptr(nd, _int), ctypes.byref(score)))
+    return score.value
+
+
+def dtp_layout_permutation(layout, tp: int, group: int = 1):
+    import numpy as np
+    lay = np.ascontiguousarray(layout, dtype=np.intc)
+    perm = np.empty(lay.size * group, dtype=np.int32)
+    _check(_lib.dtp_layout_permutation(_np_ptr(lay, _int), lay.size, tp, group, _np_ptr(perm, ctypes.c_int32)))
+    return perm
+
+
+def permute_bf16(src, dst, perm, *, dim: int, stream=None, ctx: Optional[Context] = None) -> None:
+    """dst = src with rows (dim 0) or columns (dim 1) permuted by the device int32 tensor perm."""
+    torch = _torch()
+    rows, cols = src.shape
+    _check(_lib.permute_bf16(_h(ctx), _dev_ptr(src, torch.bfloat16, "src"),
+                             _dev_ptr(dst, torch.bfloat16, "dst", (rows, cols)), rows, cols, dim,
+                             _dev_ptr(perm, torch.int32, "perm", ((rows if dim == 0 else cols),)), _stream(stream)))
 
 
 def raw_agmm_backward(ctx, seq_len, hidden, n_local, tp, rank, shard_src, x_gathered, w, dy, dx, dw, dw_dtype,

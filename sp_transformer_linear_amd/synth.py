@@ -222,3 +222,14 @@ WORKLOADS = {
         tp=4, n_chunks=4, M=32768, K=1024, N=768, K_row=768, H=1024, P=4,
         delta=1, dtp_modules=4),
 }
+
+
+def synthetic_affinity(seed: int, n_heads: int, n_neurons: int, tp: int) -> np.ndarray:
+    """Synthetic KV-head / FFN-neuron affinities [n_heads, n_neurons] float64 for the sharding
+    optimiser (real ones need a trained model): exp(N(0, 1)), times 3 where a head and a neuron
+    share a hidden group (tp balanced groups placed at random), so that there is a layout to find."""
+    rng = np.random.default_rng(seed)
+    gh = rng.permutation(np.arange(n_heads) % tp)
+    gn = rng.permutation(np.arange(n_neurons) % tp)
+    return np.exp(rng.standard_normal((n_heads, n_neurons))) * np.where(gh[:, None] == gn[None, :], 3.0, 1.0)
+
