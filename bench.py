@@ -62,6 +62,9 @@ def parse():
                     help="seconds of oracle work for the CPU baseline (0 disables it)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--no-studies", action="store_true",
+                    help="stop after the timed region and the staging check (profiler runs): no overlap, "
+                         "boundary, reduce-scatter, copy-mode, backward, graph or sharding figures")
     return ap.parse_args()
 
 
@@ -447,7 +450,8 @@ def main():
     agmm_flops = 2.0 * M * K * N
     t_agmm = float(agmm_ms.mean())
     agmm_tflops = agmm_flops / (t_agmm * 1e-3) / 1e12
-    ov = overlap(L, L.w_col, reps, wl.n_chunks)
+    studies = not args.no_studies
+    ov = overlap(L, L.w_col, reps, wl.n_chunks) if studies else {}
 
     red_bytes = epilogue_bytes(wl.P + 1, M, wl.H)
     dtp_bytes = epilogue_bytes(1 + 1 + (wd.tp - 1), wd.M, wd.H)
@@ -473,7 +477,7 @@ def main():
     # aliases it); against the same pair with y in a buffer of its own that the call copies.
     # Outside the timed region, pairs interleaved; both chains must give the same bits.
     boundary = None
-    if wl.H == wl.K:
+    if wl.H == wl.K and studies:
         R = M // wl.tp
         parts_r = [t[:R] for t in [L.own] + L.peers]
         y_own = torch.empty((R, wl.H), dtype=torch.bfloat16, device=dev)
@@ -587,7 +591,7 @@ def main():
                 "copy_hidden_frac": None if t_copy <= 0 else round(max(0.0, 1.0 - exposed / t_copy), 4),
                 "bitwise_equal_gemm_partial": same}
 
-    rs_main = reduce_scatter(L, reps) if L.a_row.shape[0] % wl.tp == 0 else None
+    rs_main = reduce_scatter(L, reps) if studies and L.a_row.shape[0] % wl.tp == 0 else None
 
     # Copy modes ("Add forward all-gather overlap", "Observations": a gather on the compute units
     # contends with the GEMM; the copy-engine gather does not).  The same agmm call with its
@@ -634,7 +638,7 @@ def main():
                          else round(max(0.0, 1.0 - ex / t_copy), 4)}
         return out_
 
-    copy_modes = copy_mode_study(L, L.w_col, reps, wl.n_chunks)
+    copy_modes = copy_mode_study(L, L.w_col, reps, wl.n_chunks) if studies else None
 
     # Backward ("Add forward all-gather overlap", "Scope": the backward gathers again): the
     # re-gather on the copy engines under the input-gradient GEMM, then the weight-gradient GEMM;
@@ -683,48 +687,50 @@ def main():
                 "ms_serial": round(t_s, 4), "copy_serial_ms": round(t_copy, 4), "copy_exposed_ms": round(exposed, 4),
                 "copy_hidden_frac": None if t_copy <= 0 else round(max(0.0, 1.0 - exposed / t_copy), 4)}
 
-    backward = backward_study(L, L.w_col, reps)
+    backward = backward_study(L, L.w_col, reps) if studies else None
 
     # Launch gaps: one step captured in a HIP graph (on a stream under capture the agmm call takes
     # the per-chunk event path, whose copies, events and launches a graph holds), replayed, against
     # the same step run eagerly on the event path and on the default staged path (the timed
     # region above).  The column GEMM's output must come out with the same bits.
-    y_staged = L.y_col.clone()
-    ctx.set_copy_mode("events")
-    step()  # also creates the context's copy stream before the capture
-    torch.cuda.synchronize()
-    n_l = max(5, args.steps)
-    t0, t1 = ev(), ev()
-    t0.record(cs)
-    for _ in range(n_l):
-        step()
-    t1.record(cs)
-    torch.cuda.synchronize()
-    ctx.check()
-    ms_events = t0.elapsed_time(t1) / n_l
-    ctx.set_copy_mode("staged")
-    cs_eager = cs
-    cap_stream = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    torch.cuda.synchronize()
-    cs = cap_stream  # the step's calls go to the capturing stream
-    with torch.cuda.graph(graph, stream=cap_stream):
-        step()
-    cs = cs_eager
-    for _ in range(3):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0.record(cs)
-    for _ in range(n_l):
-        graph.replay()
-    t1.record(cs)
-    torch.cuda.synchronize()
-    ctx.check()
-    ms_graph = t0.elapsed_time(t1) / n_l
-    launch = {"ms_step_staged_eager": round(ms_step, 4), "ms_step_events_eager": round(ms_events, 4),
-              "ms_step_events_graph": round(ms_graph, 4), "steps": n_l,
-              "y_bitwise_equal": bool(torch.equal(L.y_col.view(torch.int16), y_staged.view(torch.int16)))}
-    del graph, y_staged
+    launch = None
+    if studies:
+        y_staged = L.y_col.clone()
+        ctx.set_copy_mode("events")
+        step()  # also creates the context's copy stream before the capture
+        torch.cuda.synchronize()
+        n_l = max(5, args.steps)
+        t0, t1 = ev(), ev()
+        t0.record(cs)
+        for _ in range(n_l):
+            step()
+        t1.record(cs)
+        torch.cuda.synchronize()
+        ctx.check()
+        ms_events = t0.elapsed_time(t1) / n_l
+        ctx.set_copy_mode("staged")
+        cs_eager = cs
+        cap_stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        cs = cap_stream  # the step's calls go to the capturing stream
+        with torch.cuda.graph(graph, stream=cap_stream):
+            step()
+        cs = cs_eager
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0.record(cs)
+        for _ in range(n_l):
+            graph.replay()
+        t1.record(cs)
+        torch.cuda.synchronize()
+        ctx.check()
+        ms_graph = t0.elapsed_time(t1) / n_l
+        launch = {"ms_step_staged_eager": round(ms_step, 4), "ms_step_events_eager": round(ms_events, 4),
+                  "ms_step_events_graph": round(ms_graph, 4), "steps": n_l,
+                  "y_bitwise_equal": bool(torch.equal(L.y_col.view(torch.int16), y_staged.view(torch.int16)))}
+        del graph, y_staged
 
     def gbs(nbytes, ms):
         return nbytes / (ms * 1e-3) / 1e9
@@ -864,7 +870,7 @@ def main():
                 "permute_ms": round(ms_perm, 4), "permute_bytes": nbytes,
                 "permute_GBps": round(nbytes / (ms_perm * 1e-3) / 1e9, 1)}
 
-    out["dtp_sharding"] = dtp_sharding(wd.tp)
+    out["dtp_sharding"] = dtp_sharding(wd.tp) if studies else None
 
     # ---- other workloads, after the timed region: the same calls, fewer steps ---------------
     del L, D
