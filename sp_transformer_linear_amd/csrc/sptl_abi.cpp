@@ -390,10 +390,15 @@ int sptl_ctx_check(sptl_ctx *ctx) {
             return fail(rc == -2 ? SPTL_E_ASYNC : SPTL_E_HIP,
                         rc == -2 ? "sptl_ctx_check: the copies of a timed-out call did not complete"
                                  : "sptl_ctx_check: waiting for staged calls failed");
-    int flag[2] = {0, 0};  // [0]: a staging wait timed out; [1]: a permutation index was out of range
+    // [0]: a staging wait timed out; [1]: a permutation index was out of range; [2]: a copy-out
+    // tile ran on another XCD than the one its slice's release counted it on
+    int flag[3] = {0, 0, 0};
     SPTL_HIP(hipMemcpy(flag, ctx->err_dev, sizeof flag, hipMemcpyDeviceToHost));
-    if (flag[0] || flag[1]) SPTL_HIP(hipMemset(ctx->err_dev, 0, sizeof flag));
+    if (flag[0] || flag[1] || flag[2]) SPTL_HIP(hipMemset(ctx->err_dev, 0, sizeof flag));
     if (flag[1]) return fail(SPTL_E_ASYNC, "permute_bf16: an index was out of range (zeros written there)");
+    if (flag[2])
+        return fail(SPTL_E_ASYNC, "gemm_rs_chunked: an XCD ran more tiles of a slice than counted for it; the "
+                                  "copied slices of that call may hold stale rows");
     if (flag[0]) {
         if (ctx->stager) (void)sptl::stager_take_timeouts(ctx->stager);  // the same report
         return fail(SPTL_E_ASYNC, "a staging wait timed out; the affected agmm_chunked results are invalid");
@@ -823,7 +828,6 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
     // this rank's own last
     std::vector<sptl::CopyPiece> copies;
     sptl::ChunkPlan &plan = gp.plan;
-    int64_t slice_tiles[sptl::kMaxPlanChunks] = {};
     for (int d = 1; d <= tp; ++d) {
         const int q = (rank + d) % tp;
         plan.order[d - 1] = q;
@@ -839,16 +843,45 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
     plan.timeout_ticks = (uint64_t)ctx->wallclock_khz * ctx->wait_timeout_us / 1000u;
     plan.copy_out = true;
     std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies, 1, 1);
-    const int64_t wgs = sptl::gemm_workgroups(gp);  // the chunk-ordered launch: equal tiles per slice
-    for (const sptl::CopyPiece &pc : pieces) slice_tiles[pc.chunk] = wgs / tp;
+    const int64_t wgs = sptl::gemm_workgroups(gp);
+    // The release of a slice (see ChunkPlan): the XCD's last tile of the slice writes its L2
+    // back, which needs every XCD's share of a copied slice to be equal; else every tile does.
+    static const bool each_tile = [] {
+        const char *e = getenv("SPTL_RS_FLUSH");  // "tile": every tile writes back (measurement aid)
+        return e && !strcmp(e, "tile");
+    }();
+    static const int share_skew = [] {
+        const char *e = getenv("SPTL_RS_SHARE_SKEW");  // under-counted share (test aid: the report)
+        return e ? (int)(strtol(e, nullptr, 10) & 1) : 0;
+    }();
+    std::vector<int64_t> xt((size_t)tp * 8);
+    sptl::chunk_xcd_tiles(gp, xt.data());
+    plan.flush_each_tile = each_tile;
+    for (const sptl::CopyPiece &pc : copies) {
+        int64_t share = 0, groups = 0;
+        for (int x = 0; x < 8; ++x) {
+            const int64_t t = xt[(size_t)pc.chunk * 8 + x];
+            if (!t) continue;
+            if (share && t != share) plan.flush_each_tile = true;
+            share = t;
+            ++groups;
+        }
+        plan.slice_xcd_last[pc.chunk] = (uint32_t)(share - 1 - (share > 1 ? share_skew : 0));
+        plan.slice_last[pc.chunk] = (uint64_t)(groups - 1);
+    }
+    if (plan.flush_each_tile)
+        for (const sptl::CopyPiece &pc : copies) {
+            int64_t tiles = 0;
+            for (int x = 0; x < 8; ++x) tiles += xt[(size_t)pc.chunk * 8 + x];
+            plan.slice_last[pc.chunk] = (uint64_t)(tiles - 1);
+        }
     sptl::StageCall call;
     std::string why;
-    if (int rc = sptl::stager_begin(ctx->stager, pieces, wgs, &call, &why, nullptr, slice_tiles))
+    if (int rc = sptl::stager_begin(ctx->stager, pieces, wgs, &call, &why))
         return fail(rc == -2 ? SPTL_E_ASYNC : SPTL_E_HIP, "%s: %s", fn, why.c_str());
     for (int c = 0; c < tp; ++c) {
         plan.ready[c] = call.ready[c];  // copy-out: the slice's outgoing copies
         plan.ready_n[c] = call.ready_n[c];
-        plan.slice_last[c] = call.slice_last[c];
     }
     plan.slice_ready = call.slice_ready;
     plan.slice_count = call.slice_count;
@@ -862,7 +895,10 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
     plan.wg_count = call.wg_count;
     for (int gi = 0; gi < sptl::kEndGroups; ++gi) plan.grp_last[gi] = call.grp_last[gi];
     plan.all_last = call.all_last;
-    hipError_t he = hipEventRecord(call.fork, cs);
+    // the call's slice counters start at zero (a fill kernel rather than a memset; the set's
+    // previous call has finished, stager_begin saw to that)
+    hipError_t he = sptl::launch_fill_u64(call.slice_count, (int64_t)tp * sptl::kEndLine, 0ull, cs);
+    if (he == hipSuccess) he = hipEventRecord(call.fork, cs);
     if (he == hipSuccess) he = sptl::launch_gemm(gp, cs);
     if (he != hipSuccess) {
         sptl::stager_cancel(ctx->stager, call);

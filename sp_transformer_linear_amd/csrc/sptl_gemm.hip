@@ -299,18 +299,36 @@ __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin 
 template <bool CHUNKED>
 __device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrigin &o, int bid) {
     if (CHUNKED && p.plan.copy_out && p.plan.ready[o.chunk]) {
-        // A slice that is copied out: every wave waits until its stores of the tile have reached
-        // the L2 (vmcnt 0: the barrier's workgroup-scope fence does not wait for them), then
-        // after the barrier the first thread writes the XCD's L2 back (system-scope release: the
-        // copy engines read memory, not the L2) and counts the tile; the slice's last tile
-        // releases its copies.
+        // A slice that is copied out (see ChunkPlan): every wave waits until its stores of the
+        // tile have reached the L2 (vmcnt 0: the barrier's workgroup-scope fence does not wait
+        // for them); then the first thread counts the tile, and the XCD's last tile of the slice
+        // writes the L2 back (system-scope release: the copy engines read memory, not the L2).
+        // The slice is released once slice_last + 1 XCDs have each counted slice_xcd_last + 1
+        // tiles, which is every tile of the slice: so each tile's rows were written back after
+        // its stores, wherever it ran.  Any other placement ends in the report below or in the
+        // bounded wait for the copies, never in a release before a write-back.
         const ChunkPlan &plan = p.plan;
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0); expcnt, lgkmcnt not waited
         __syncthreads();
         if (threadIdx.x == 0) {
-            __atomic_thread_fence(__ATOMIC_RELEASE);
-            if (__hip_atomic_fetch_add(plan.slice_count + (size_t)o.chunk * kEndLine, 1ull, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT) == plan.slice_last[o.chunk])
+            uint64_t *line = plan.slice_count + (size_t)o.chunk * kEndLine;
+            bool last = true;
+            if (plan.flush_each_tile) {
+                __atomic_thread_fence(__ATOMIC_RELEASE);  // this tile's rows, from its own L2
+            } else {
+                // counted under the XCD it runs on (the hardware's XCC id): the host's per-XCD share
+                // holds for any rotation of the round-robin placement
+                unsigned xcc;
+                asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+                const uint64_t v = __hip_atomic_fetch_add(line + 1 + (xcc & 7), 1ull, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                if (v > (uint64_t)plan.slice_xcd_last[o.chunk])  // more tiles on this XCD than counted
+                    __hip_atomic_store(plan.err + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last = v == (uint64_t)plan.slice_xcd_last[o.chunk];
+                if (last) __atomic_thread_fence(__ATOMIC_RELEASE);  // every tile of the slice that ran here
+            }
+            if (last && __hip_atomic_fetch_add(line, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                            plan.slice_last[o.chunk])
                 __hip_atomic_store(plan.slice_ready + 16 * (size_t)o.chunk, plan.epoch, __ATOMIC_RELEASE,
                                    __HIP_MEMORY_SCOPE_SYSTEM);
         }
@@ -1244,6 +1262,22 @@ hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t strea
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n, v);
     return hipGetLastError();
+}
+
+void chunk_xcd_tiles(const GemmProblem &problem, int64_t *tiles) {
+    const int c = resolve(problem, GemmTile::Auto);
+    ChunkPlan plan = problem.plan;
+    const int bm = config_rows(c), bn = config_cols(c);
+    const int64_t tiles_n = (problem.n + bn - 1) / bn;
+    chunk_layout(plan, bm, tiles_n);
+    const int tpc = plan.chunk_rows / bm;
+    const int64_t nt = tiles_n * tpc * plan.n_chunks;
+    for (int64_t i = 0; i < (int64_t)plan.n_chunks * 8; ++i) tiles[i] = 0;
+    for (int64_t b = 0; b < nt; ++b) {
+        int pos, sub, tn;
+        chunk_tile(tpc, (int)tiles_n, plan.xcd_group, plan.chunk_band, (int)b, pos, sub, tn);
+        tiles[(int64_t)plan.order[pos] * 8 + (b & 7)]++;
+    }
 }
 
 int64_t gemm_workgroups(const GemmProblem &p, GemmTile tile) {

@@ -53,14 +53,23 @@ struct ChunkPlan {
     uint64_t *ts;                            // optional per-chunk timestamps (see below)
     // Copy-out mode (the reduce-scatter mirror): the chunks are output slices and no tile waits
     // for input.  ready[c] then lists the completion words of slice c's outgoing copies (null: the
-    // slice stays): the slice's tiles count themselves in slice_count (line c, kEndLine words),
-    // each after making its rows visible to the copy engines, and the last of them (it sees
-    // slice_last[c]) stores epoch to slice_ready[16 c] (pinned host memory, where the copies are
-    // released from); the launch's last workgroup waits for every copy before reporting the end.
+    // slice stays).  The copy engines read memory, so a slice is released only once every XCD
+    // that ran some of its tiles has written its L2 back after their stores: each such tile waits
+    // for its stores and counts itself in the counter of the XCD it runs on (line c of
+    // slice_count, kEndLine words: word 1 + x for XCC x), and the XCD's last tile of the slice (it
+    // sees slice_xcd_last[c], the per-XCD share less one) writes the XCD's L2 back and counts the
+    // XCD in word 0; the last XCD (it sees slice_last[c], the XCDs holding the slice less one)
+    // stores epoch to slice_ready[16 c] (pinned host memory, where the copies are released from).
+    // A count past the share sets err[2].  The counters are zeroed by the call before the launch.
+    // flush_each_tile: every tile writes back and counts in word 0 (slice_last[c] then counts
+    // tiles), for layouts whose XCDs hold unequal shares of a slice.  The launch's last workgroup
+    // waits for every copy before reporting the end.
     bool copy_out;
+    bool flush_each_tile;
     uint64_t *slice_ready;
     uint64_t *slice_count;
     uint64_t slice_last[kMaxPlanChunks];
+    uint32_t slice_xcd_last[kMaxPlanChunks];
 };
 // Waiting: a workgroup of chunk c polls its replica of c's landed flag about every
 // microsecond and, once every 16 polls (phase set by its index), c's completion words
@@ -104,6 +113,10 @@ enum class GemmTile { T256x256, T128x128, Auto };
 // Picks a tile shape for the problem (Auto) and launches.  Returns the HIP error of the
 // launch.
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream, GemmTile tile = GemmTile::Auto);
+
+// Per chunk of a chunk-ordered launch of p: the tiles each of the 8 XCDs runs under round-robin
+// placement (tiles[8 c + x], x = tile index mod 8), from the same tile map the kernel uses.
+void chunk_xcd_tiles(const GemmProblem &p, int64_t *tiles);
 
 // Workgroups launch_gemm(p, stream, tile) launches.
 int64_t gemm_workgroups(const GemmProblem &p, GemmTile tile = GemmTile::Auto);

@@ -83,7 +83,6 @@ struct SignalSet {
     hipEvent_t fork = nullptr;
     uint64_t epoch = 0;       // of the last call begun on the set (0: never used)
     int armed[kMaxPlanChunks + 1] = {};   // pieces per chunk armed by that call
-    uint64_t slice_total[kMaxPlanChunks] = {};  // copy-out tiles counted per slice, all calls
     std::atomic<uint64_t> handled{0};     // epoch of the last job the worker has handled
     uint64_t grp_total[kEndGroups] = {};  // workgroups counted per group, all calls on the set
     uint64_t all_total = 0;               // groups counted, all calls on the set
@@ -503,7 +502,7 @@ bool stager_take_timeouts(SdmaStager *s) {
 }
 
 int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t workgroups, StageCall *out,
-                 std::string *err, uint64_t *fresh_counts, const int64_t *slice_tiles) {
+                 std::string *err, uint64_t *fresh_counts) {
     int count[kMaxPlanChunks + 1] = {};
     for (const CopyPiece &p : pieces) {
         if (p.chunk < 0 || p.chunk > kMaxPlanChunks || p.piece != count[p.chunk] || p.piece >= kMaxPieces) {
@@ -563,15 +562,10 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
     out->all_first = ss.all_total;
     out->all_last = all_base + (uint64_t)groups - 1;
     if (!fresh_counts) ss.all_total += (uint64_t)groups;
-    // copy-out slices: cumulative tile counts of the set, like the end counters
+    // copy-out calls: the set's slice-ready words (pinned) and slice counters (device; the call
+    // zeroes the ones it uses on its stream before the launch)
     out->slice_ready = s->slice_words + (size_t)kSliceSetWords * set;
     out->slice_count = s->slice_counts + (size_t)kSliceSetWords * set;
-    for (int c = 0; c < kMaxPlanChunks; ++c) {
-        const int64_t t = slice_tiles ? slice_tiles[c] : 0;
-        out->slice_first[c] = ss.slice_total[c];
-        out->slice_last[c] = t > 0 ? ss.slice_total[c] + (uint64_t)t - 1 : ~0ull;
-        ss.slice_total[c] += (uint64_t)(t > 0 ? t : 0);
-    }
     return 0;
 }
 
@@ -593,7 +587,6 @@ void stager_cancel(SdmaStager *s, const StageCall &call) {
     SignalSet &ss = s->sets[call.set];
     for (int g = 0; g < kEndGroups; ++g) ss.grp_total[g] = call.grp_first[g];
     ss.all_total = call.all_first;
-    for (int c = 0; c < kMaxPlanChunks; ++c) ss.slice_total[c] = call.slice_first[c];
     for (int c = 0; c <= kMaxPlanChunks; ++c) ss.armed[c] = 0;
     ss.handled.store(call.epoch, std::memory_order_release);
     __atomic_store_n(s->host_words + 16 * call.set, call.epoch, __ATOMIC_RELEASE);

@@ -54,11 +54,10 @@ struct StageCall {
     uint64_t all_last = 0;
     uint64_t grp_first[kEndGroups] = {};  // the set's totals before this call (for a cancel)
     uint64_t all_first = 0;
-    // copy-out calls (slice_tiles given to stager_begin): see ChunkPlan
+    // copy-out calls: the set's slice-ready words (pinned host, 16 apart) and slice counter lines
+    // (device, kEndLine words apart, zeroed by the call before its launch); see ChunkPlan
     uint64_t *slice_ready = nullptr;
     uint64_t *slice_count = nullptr;
-    uint64_t slice_last[kMaxPlanChunks] = {};
-    uint64_t slice_first[kMaxPlanChunks] = {};
 };
 
 class SdmaStager;
@@ -76,15 +75,14 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
                                    int group = 0);
 
 // Reserves a completion-signal set for one call whose consuming kernel has `workgroups`
-// workgroups, and arms it with the number of pieces per chunk.  slice_tiles (copy-out calls):
-// per chunk, the tiles of the slice whose copies the kernel releases (0: not copied).  Blocks (bounded) while the
+// workgroups, and arms it with the number of pieces per chunk.  Blocks (bounded) while the
 // set's previous call is still running and, if a wait of that call timed out, until its copies
 // have completed.  Returns 0, -1 (the previous call did not finish; bad pieces) or -2 (the
 // copies of a timed-out call did not complete within the bound).  fresh_counts: null to count
 // the kernel's workgroups in the set's own cumulative counters, or kEndCounters lines of
 // counters (kEndLine words apart) that the caller zeroes on the stream before the launch.
 int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t workgroups, StageCall *out,
-                 std::string *err, uint64_t *fresh_counts = nullptr, const int64_t *slice_tiles = nullptr);
+                 std::string *err, uint64_t *fresh_counts = nullptr);
 
 // Whether a call whose chunk wait timed out has been seen (on reuse of its set, on an idle wait or
 // now, for calls that have ended) since the last time this returned true.

@@ -7,12 +7,17 @@ gemm_partial (same kernel family, one K order), every destination bit for bit eq
 and the partial against the float64 oracle.  partial and the destinations are NaN-poisoned first,
 so a copy released before its slice's rows were written and visible would leave NaN behind.
 """
+import os
+import subprocess
+import sys
+import textwrap
+
 import numpy as np
 import pytest
 
 import oracle.sptl_oracle as O
 from sp_transformer_linear_amd import synth
-from tests.util import assert_within, bf16_tol, to_bits, to_dev
+from tests.util import ROOT, assert_within, bf16_tol, to_bits, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(300)]
 
@@ -85,3 +90,59 @@ def test_rs_back_to_back(env):
     for i, r in enumerate(runs):
         print(f"call {i}", flush=True)
         check(env, *r, tp=4, rank=i % 4, oracle=(i < 2))
+
+
+CHILD = textwrap.dedent("""
+    import sys, numpy as np, torch
+    sys.path.insert(0, {root!r})
+    from sp_transformer_linear_amd import sptl
+    M, K, H, tp = 8192, 512, 1024, 8
+    R = M // tp
+    g = torch.Generator(device="cuda").manual_seed(5)
+    a = torch.randn((M, K), device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn((K, H), device="cuda", generator=g) / 32).to(torch.bfloat16)
+    ctx = sptl.Context(0)
+    ref = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    sptl.gemm_partial(a, w, ref, ctx=ctx)
+    ok = True
+    for it in range(3):
+        part = torch.full((M, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dst = [None] + [torch.full((R, H), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(tp - 1)]
+        sptl.gemm_rs_chunked(a, w, part, dst, rank=0, ctx=ctx)
+        torch.cuda.synchronize()
+        ok = ok and torch.equal(part.view(torch.int16), ref.view(torch.int16))
+        for q in range(1, tp):
+            ok = ok and torch.equal(dst[q].view(torch.int16), part[q * R:(q + 1) * R].view(torch.int16))
+    try:
+        ctx.check()
+        report = ""
+    except sptl.SptlError as e:
+        report = str(e)
+    ctx.close()
+    print("RESULT", int(ok), repr(report))
+""")
+
+
+def run_child(env_extra):
+    env = dict(os.environ)
+    env.update(env_extra)
+    r = subprocess.run([sys.executable, "-c", CHILD.format(root=ROOT)], env=env, capture_output=True, text=True,
+                       timeout=240)
+    line = [ln for ln in r.stdout.splitlines() if ln.startswith("RESULT")]
+    assert r.returncode == 0 and line, r.stdout[-2000:] + r.stderr[-2000:]
+    _, ok, report = line[0].split(" ", 2)
+    return ok == "1", eval(report)  # noqa: S307 - our own child's repr of a string
+
+
+def test_rs_release_every_tile_child():
+    """The fallback release (every tile writes its L2 back) gives the same bits."""
+    ok, report = run_child({"SPTL_RS_FLUSH": "tile"})
+    assert ok and report == ""
+
+
+def test_rs_share_overrun_is_reported_child():
+    """With the per-XCD share under-counted by one (a test aid), each XCD's last counted tile
+    releases early and the tile after it counts past the share: sptl_ctx_check reports the call
+    (its copies may be stale, so only the report is checked)."""
+    _, report = run_child({"SPTL_RS_SHARE_SKEW": "1"})
+    assert "XCD" in report
