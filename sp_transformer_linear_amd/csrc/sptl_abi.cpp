@@ -318,7 +318,25 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     const int64_t per_chunk = std::max<int64_t>(1, sptl::gemm_workgroups(wide) / n);
     const int64_t first_round = (ctx->cus + per_chunk - 1) / per_chunk;
     const int lead = (int)std::max<int64_t>(1, std::min<int64_t>(first_round - cpr, (int64_t)(n - cpr)));
-    std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies, lead);
+    // When the own chunks do not fill the first round, the lead chunks' tiles are resident from
+    // the start and would wait for the engines: they copy the lead chunks themselves (ChunkPlan,
+    // cu_n), and the engines take the later chunks.  SPTL_CU_LEAD=0 leaves every chunk to the
+    // engines (measurement aid).
+    static const bool cu_lead_on = [] {
+        const char *e = getenv("SPTL_CU_LEAD");
+        return !(e && !strcmp(e, "0"));
+    }();
+    const int cu = cu_lead_on && first_round > cpr ? std::min(lead, sptl::kMaxCuChunks) : 0;
+    plan.cu_n = cu;
+    plan.cu_mask = 0;
+    plan.cu_chunk_bytes = (int64_t)chunk_bytes;
+    for (int i = 0; i < cu; ++i) {
+        plan.cu_src[i] = copies[(size_t)i].src;
+        plan.cu_dst[i] = copies[(size_t)i].dst;
+        plan.cu_mask |= 1ull << copies[(size_t)i].chunk;
+    }
+    copies.erase(copies.begin(), copies.begin() + cu);
+    std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies, std::max(1, lead - cu));
 
     sptl::StageCall call;
     std::string why;

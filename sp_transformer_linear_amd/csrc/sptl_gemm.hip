@@ -141,10 +141,84 @@ __device__ __forceinline__ void wait_chunk(const ChunkPlan &plan, int chunk, int
     __atomic_thread_fence(__ATOMIC_ACQUIRE);
 }
 
+// Lead chunks copied by the launch's own workgroups (ChunkPlan::cu_n), run by the whole
+// workgroup: take blocks of the copies until none is left, storing with agent scope (written
+// through the L2), and once the stores have completed count the blocks done; then wait, with
+// the first wave, until every block is done, and invalidate the caches (agent-scope acquire).
+__device__ __forceinline__ bool cu_copies_done(const ChunkPlan &plan) {
+    const int64_t per_chunk = (plan.cu_chunk_bytes + kCuBlockBytes - 1) / kCuBlockBytes;
+    return __hip_atomic_load(plan.wg_count + (size_t)kCuDoneLine * kEndLine, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) >= (uint64_t)(per_chunk * plan.cu_n);
+}
+
+__device__ void cu_copy_and_wait(const ChunkPlan &plan) {
+    __shared__ uint64_t grabbed;
+    typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+    uint64_t *grab = plan.wg_count + (size_t)kCuGrabLine * kEndLine;
+    uint64_t *done = plan.wg_count + (size_t)kCuDoneLine * kEndLine;
+    const int64_t per_chunk = (plan.cu_chunk_bytes + kCuBlockBytes - 1) / kCuBlockBytes;
+    const uint64_t total = (uint64_t)(per_chunk * plan.cu_n);
+    uint64_t mine = 0;
+    for (;;) {
+        if (threadIdx.x == 0) grabbed = __hip_atomic_fetch_add(grab, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const uint64_t b = grabbed;
+        __syncthreads();
+        if (b >= total) break;
+        const int i = (int)(b / (uint64_t)per_chunk);
+        const int64_t off = (int64_t)(b % (uint64_t)per_chunk) * kCuBlockBytes;
+        const int64_t len = plan.cu_chunk_bytes - off < kCuBlockBytes ? plan.cu_chunk_bytes - off : kCuBlockBytes;
+        const char *src = static_cast<const char *>(plan.cu_src[i]) + off;
+        char *dst = static_cast<char *>(plan.cu_dst[i]) + off;
+        // a pass issues all of its loads before its stores (4 x 16 bytes per thread, which keeps the
+        // GEMM free of register spills), so each pass waits for memory once
+        constexpr int kU = 4;
+        const int64_t step = (int64_t)blockDim.x * 16;
+        for (int64_t e0 = (int64_t)threadIdx.x * 16; e0 < len; e0 += step * kU) {
+            v4u32 v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (e0 + u * step < len) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(src + e0 + u * step));
+            // relaxed agent-scope atomic stores (sc1): coherent across the XCDs without a fence,
+            // so they are written through the L2 and the copied rows reach the chip's coherence
+            // point without an L2 write-back
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (e0 + u * step < len) {
+                    uint64_t *d = reinterpret_cast<uint64_t *>(dst + e0 + u * step);
+                    const uint64_t lo = (uint64_t)v[u][0] | ((uint64_t)v[u][1] << 32);
+                    const uint64_t hi = (uint64_t)v[u][2] | ((uint64_t)v[u][3] << 32);
+                    __hip_atomic_store(d, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(d + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+        }
+        ++mine;
+    }
+    if (mine) {
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): this thread's stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(done, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (threadIdx.x < 64) {
+        const uint64_t t0 = wall_clock64();
+        while (!cu_copies_done(plan)) {
+            if (timed_out(t0, plan)) break;
+            poll_pause(plan);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+}
+
 // Non-blocking form of wait_chunk, run by a whole wave: whether chunk `chunk` has landed now
 // (setting the landed flags when this wave is the first to see it).  When it returns true the
 // copied rows are visible to the workgroup's later loads (after a barrier).
 __device__ __forceinline__ bool chunk_ready_now(const ChunkPlan &plan, int chunk, int bid) {
+    if ((plan.cu_mask >> chunk) & 1) {
+        const bool ok = cu_copies_done(plan);
+        if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        return ok;
+    }
     const int64_t *const *words = plan.ready[chunk];
     if (!words || plan.copy_out) return true;
     const int n = plan.ready_n[chunk];
@@ -216,8 +290,10 @@ __device__ __forceinline__ void tile_wait(const GemmProblem &p, const TileOrigin
         const ChunkPlan &plan = p.plan;
         const int tid = threadIdx.x;
         if (plan.ts && bid == 0 && tid == 0) plan.ts[3 * plan.n_chunks] = wall_clock64();
+        const bool cu = (plan.cu_mask >> o.chunk) & 1;
+        if (cu) cu_copy_and_wait(plan);  // the chunk is copied by the launch's own workgroups
         if (tid < 64) {
-            wait_chunk(plan, o.chunk, bid);  // this chunk's copy pieces have landed
+            if (!cu) wait_chunk(plan, o.chunk, bid);  // this chunk's copy pieces have landed
             if (plan.ts && tid == 0) {
                 const unsigned long long now = wall_clock64();
                 atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + o.chunk), now);
@@ -358,8 +434,15 @@ __device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrig
             wait_ready(plan.join, plan.join_n, plan);
             if (plan.copy_out)
                 for (int c = 0; c < plan.n_chunks; ++c) wait_ready(plan.ready[c], plan.ready_n[c], plan);
-            if (threadIdx.x == 0)
+            if (threadIdx.x == 0) {
+                if (plan.cu_n) {  // every tile has taken its last block: the set's next call starts at zero
+                    __hip_atomic_store(plan.wg_count + (size_t)kCuGrabLine * kEndLine, 0ull, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(plan.wg_count + (size_t)kCuDoneLine * kEndLine, 0ull, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
                 __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
         }
     }
 }

@@ -11,6 +11,12 @@ constexpr int kMaxPlanChunks = 64;  // chunks of one chunk-ordered GEMM launch
 constexpr int kEndGroups = 8;       // end-counter groups (workgroup index mod 8)
 constexpr int kEndLine = 32;        // 64-bit words between end counters (256 bytes)
 constexpr int kEndCounters = kEndGroups + 1;
+// A call's counter block (kCallCountLines lines of kEndLine words): the end counters, then the
+// grab and done counters of the lead chunks its own workgroups copy (ChunkPlan::cu_n).
+constexpr int kCuGrabLine = kEndCounters, kCuDoneLine = kEndCounters + 1;
+constexpr int kCallCountLines = kEndCounters + 2;
+constexpr int kMaxCuChunks = 16;         // lead chunks a launch's workgroups may copy
+constexpr int64_t kCuBlockBytes = 65536;  // one grab of such a copy
 
 // Landed flags of a chunk-ordered launch: kFlagReplicas copies per chunk, 4 KiB apart so that
 // they fall on different memory channels; replica r of chunk c is word r * kFlagStride + c.
@@ -47,7 +53,7 @@ struct ChunkPlan {
     uint64_t epoch;                          // value the end words take for this launch
     uint64_t *finished;                      // pinned host word: epoch once the launch is done
     uint64_t *timedout;                      // pinned host word: epoch if a wait of the launch timed out
-    uint64_t *wg_count;                      // end counters of the signal set (kEndCounters lines)
+    uint64_t *wg_count;                      // the call's counter block (kCallCountLines lines)
     uint64_t grp_last[kEndGroups];           // group counter value seen by a group's last workgroup
     uint64_t all_last;                       // final counter value seen by the last group
     uint64_t *ts;                            // optional per-chunk timestamps (see below)
@@ -64,6 +70,21 @@ struct ChunkPlan {
     // flush_each_tile: every tile writes back and counts in word 0 (slice_last[c] then counts
     // tiles), for layouts whose XCDs hold unequal shares of a slice.  The launch's last workgroup
     // waits for every copy before reporting the end.
+    // Lead chunks copied by the launch's own workgroups: when the own chunks do not fill the
+    // first round of tiles, the tiles of the first peer chunks would sit idle until the copy
+    // engines land them; instead each such tile takes kCuBlockBytes blocks of those chunks' copies
+    // (from the grab counter, line kCuGrabLine of wg_count) until none is left, with agent-scope
+    // stores (written through its XCD's L2), and once they have completed adds its blocks to the
+    // done counter (line kCuDoneLine);
+    // then it waits (bounded) for done to reach every block and invalidates its caches.  Any
+    // resident workgroup can do any block, so the copies finish whichever tiles run.  cu_mask has
+    // bit c set for such a chunk c; the i-th of the cu_n copies goes from cu_src[i] to cu_dst[i]
+    // (cu_chunk_bytes each).  The launch's last workgroup resets both counters.
+    int cu_n;
+    uint64_t cu_mask;
+    int64_t cu_chunk_bytes;
+    const void *cu_src[kMaxCuChunks];
+    void *cu_dst[kMaxCuChunks];
     bool copy_out;
     bool flush_each_tile;
     uint64_t *slice_ready;

@@ -17,7 +17,7 @@
 namespace sptl {
 namespace {
 constexpr size_t kFlagWords = kFlagSetWords;                         // 64 KiB of landed flags
-constexpr size_t kCountWords = (size_t)kEndCounters * kEndLine;      // end counters, 256 B apart
+constexpr size_t kCountWords = (size_t)kCallCountLines * kEndLine;  // a call's counters, 256 B apart
 constexpr size_t kErrWords = 32;                                     // the error word's line
 constexpr size_t kScratchWords = kFlagWords + kCountWords + kErrWords;
 static_assert(kScratchWords * 8 <= 80 * 1024, "scratch budget");

@@ -68,7 +68,7 @@ hsa_status_t find_agent(hsa_agent_t a, void *data) {
 // Pinned host words: set s finished at word 16 * s (one 128-byte line each).  Device
 // counters: set s's kEndCounters end counters from word kSetCountWords * s, kEndLine apart.
 constexpr int kHostWords = 16 * kStageSets;
-constexpr int kSetCountWords = kEndCounters * kEndLine;
+constexpr int kSetCountWords = kCallCountLines * kEndLine;
 constexpr int kCountWords = kSetCountWords * kStageSets;
 constexpr double kReuseWaitSeconds = 30.0;  // longest a call waits for a set to come free
 
