@@ -71,6 +71,21 @@ constexpr int kOutOfRange = 0x7ffffff0;   // an offset past any num_records used
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
+constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);  // s_waitcnt vmcnt(0); expcnt, lgkmcnt not waited
+
+// Release fences whose L2 write-back (buffer_wbl2) has completed before the caller's next memory
+// operation is issued.  The compiler follows the write-back with a wait only when some other
+// memory operation is still outstanding, so the count or flag store that publishes the data
+// could otherwise be performed while the write-back is still running.
+__device__ __forceinline__ void release_system() {
+    __atomic_thread_fence(__ATOMIC_RELEASE);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+}
+__device__ __forceinline__ void release_agent() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+}
+
 // Bounded spins on SDMA completion signals: `words` lists the value words of one chunk's copy
 // pieces (n <= 64), each 1 until its piece lands and then <= 0.  The waits are run by one whole
 // wave, lane l watching piece l, so one vector load checks every piece.  On timeout a wait sets
@@ -85,7 +100,7 @@ __device__ __forceinline__ bool timed_out(uint64_t t0, const ChunkPlan &plan) {
     if (wall_clock64() - t0 <= plan.timeout_ticks) return false;
     __hip_atomic_store(plan.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     if (plan.timedout) __hip_atomic_store(plan.timedout, plan.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __atomic_thread_fence(__ATOMIC_RELEASE);
+    release_system();
     return true;
 }
 
@@ -142,9 +157,12 @@ __device__ __forceinline__ void wait_chunk(const ChunkPlan &plan, int chunk, int
 }
 
 // Lead chunks copied by the launch's own workgroups (ChunkPlan::cu_n), run by the whole
-// workgroup: take blocks of the copies until none is left, storing with agent scope (written
-// through the L2), and once the stores have completed count the blocks done; then wait, with
-// the first wave, until every block is done, and invalidate the caches (agent-scope acquire).
+// workgroup: take blocks of the copies until none is left; once the workgroup's stores have
+// completed, count its blocks done with an agent-scope release (its XCD's L2 is written back
+// first); then wait, with the first wave, until every block is done, and invalidate the caches
+// (agent-scope acquire).  A workgroup waits only after the grab counter has run out, so every
+// block has been taken by a running workgroup that copies it without waiting for anything: the
+// wait ends whatever number of workgroups is resident.
 __device__ __forceinline__ bool cu_copies_done(const ChunkPlan &plan) {
     const int64_t per_chunk = (plan.cu_chunk_bytes + kCuBlockBytes - 1) / kCuBlockBytes;
     return __hip_atomic_load(plan.wg_count + (size_t)kCuDoneLine * kEndLine, __ATOMIC_RELAXED,
@@ -179,25 +197,22 @@ __device__ void cu_copy_and_wait(const ChunkPlan &plan) {
 #pragma unroll
             for (int u = 0; u < kU; ++u)
                 if (e0 + u * step < len) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(src + e0 + u * step));
-            // relaxed agent-scope atomic stores (sc1): coherent across the XCDs without a fence,
-            // so they are written through the L2 and the copied rows reach the chip's coherence
-            // point without an L2 write-back
 #pragma unroll
             for (int u = 0; u < kU; ++u)
-                if (e0 + u * step < len) {
-                    uint64_t *d = reinterpret_cast<uint64_t *>(dst + e0 + u * step);
-                    const uint64_t lo = (uint64_t)v[u][0] | ((uint64_t)v[u][1] << 32);
-                    const uint64_t hi = (uint64_t)v[u][2] | ((uint64_t)v[u][3] << 32);
-                    __hip_atomic_store(d, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(d + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+                if (e0 + u * step < len)
+                    __builtin_nontemporal_store(v[u], reinterpret_cast<v4u32 *>(dst + e0 + u * step));
         }
         ++mine;
     }
     if (mine) {
-        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): this thread's stores have completed
+        // vmcnt(0): this thread's stores have reached the L2 (the barrier's workgroup-scope fence
+        // does not wait for them); the release then writes the XCD's L2 back before the count
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        if (threadIdx.x == 0) __hip_atomic_fetch_add(done, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) {
+            release_agent();
+            __hip_atomic_fetch_add(done, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     if (threadIdx.x < 64) {
         const uint64_t t0 = wall_clock64();
@@ -384,13 +399,13 @@ __device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrig
         // its stores, wherever it ran.  Any other placement ends in the report below or in the
         // bounded wait for the copies, never in a release before a write-back.
         const ChunkPlan &plan = p.plan;
-        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0); expcnt, lgkmcnt not waited
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         if (threadIdx.x == 0) {
             uint64_t *line = plan.slice_count + (size_t)o.chunk * kEndLine;
             bool last = true;
             if (plan.flush_each_tile) {
-                __atomic_thread_fence(__ATOMIC_RELEASE);  // this tile's rows, from its own L2
+                release_system();  // this tile's rows, from its own L2
             } else {
                 // counted under the XCD it runs on (the hardware's XCC id): the host's per-XCD share
                 // holds for any rotation of the round-robin placement
@@ -401,12 +416,17 @@ __device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrig
                 if (v > (uint64_t)plan.slice_xcd_last[o.chunk])  // more tiles on this XCD than counted
                     __hip_atomic_store(plan.err + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 last = v == (uint64_t)plan.slice_xcd_last[o.chunk];
-                if (last) __atomic_thread_fence(__ATOMIC_RELEASE);  // every tile of the slice that ran here
+                if (last) release_system();  // every tile of the slice that ran here
             }
+            // The count that completes the slice reads every other XCD's count, each made after
+            // that XCD's release: an acquire here makes their rows happen before the ready store.
             if (last && __hip_atomic_fetch_add(line, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                            plan.slice_last[o.chunk])
-                __hip_atomic_store(plan.slice_ready + 16 * (size_t)o.chunk, plan.epoch, __ATOMIC_RELEASE,
+                            plan.slice_last[o.chunk]) {
+                __atomic_thread_fence(__ATOMIC_ACQUIRE);
+                release_system();
+                __hip_atomic_store(plan.slice_ready + 16 * (size_t)o.chunk, plan.epoch, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_SYSTEM);
+            }
         }
     }
     if (CHUNKED && threadIdx.x < 64) {
@@ -441,7 +461,8 @@ __device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrig
                     __hip_atomic_store(plan.wg_count + (size_t)kCuDoneLine * kEndLine, 0ull, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
                 }
-                __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+                release_system();
+                __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             }
         }
     }
@@ -1162,8 +1183,10 @@ __global__ void __launch_bounds__(64) stage_join_kernel(ChunkPlan plan) {
     if (__shfl(last, 0, 64)) {
         for (int c = 0; c < plan.n_chunks; ++c) wait_ready(plan.ready[c], plan.ready_n[c], plan);
         wait_ready(plan.join, plan.join_n, plan);
-        if (threadIdx.x == 0)
-            __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (threadIdx.x == 0) {
+            release_system();
+            __hip_atomic_store(plan.finished, plan.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
     }
 }
 
