@@ -163,13 +163,27 @@ __device__ __forceinline__ void wait_chunk(const ChunkPlan &plan, int chunk, int
 // (agent-scope acquire).  A workgroup waits only after the grab counter has run out, so every
 // block has been taken by a running workgroup that copies it without waiting for anything: the
 // wait ends whatever number of workgroups is resident.
+// The workgroup whose count completes the total sets one landed flag for all lead chunks (the
+// flag slot of the first of them), and the waiters poll their own replica of it (checking the
+// counter itself every kSignalPollEvery polls): up to one wave per CU polling the counter's line
+// would slow the counts and grabs next to it.
 __device__ __forceinline__ bool cu_copies_done(const ChunkPlan &plan) {
     const int64_t per_chunk = (plan.cu_chunk_bytes + kCuBlockBytes - 1) / kCuBlockBytes;
     return __hip_atomic_load(plan.wg_count + (size_t)kCuDoneLine * kEndLine, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT) >= (uint64_t)(per_chunk * plan.cu_n);
 }
 
-__device__ void cu_copy_and_wait(const ChunkPlan &plan) {
+__device__ __forceinline__ uint64_t *cu_flag(const ChunkPlan &plan, int replica) {
+    return plan.flags + (size_t)replica * kFlagStride + __builtin_ctzll(plan.cu_mask);
+}
+
+__device__ __forceinline__ bool cu_flag_set(const ChunkPlan &plan, int bid) {
+    return plan.flags &&
+           __hip_atomic_load(cu_flag(plan, bid % kFlagReplicas), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+               plan.flag_epoch;
+}
+
+__device__ void cu_copy_and_wait(const ChunkPlan &plan, int bid) {
     __shared__ uint64_t grabbed;
     typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
     uint64_t *grab = plan.wg_count + (size_t)kCuGrabLine * kEndLine;
@@ -209,14 +223,26 @@ __device__ void cu_copy_and_wait(const ChunkPlan &plan) {
         // does not wait for them); the release then writes the XCD's L2 back before the count
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        if (threadIdx.x == 0) {
-            release_agent();
-            __hip_atomic_fetch_add(done, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
     }
     if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int completed = 0;
+        if (mine && lane == 0) {
+            release_agent();
+            completed = __hip_atomic_fetch_add(done, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + mine == total;
+        }
+        if (__shfl(completed, 0, 64) && plan.flags) {
+            // this count read every other workgroup's, each made after its release: acquire them,
+            // then publish the flags
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            release_agent();
+            if (lane < kFlagReplicas)
+                __hip_atomic_store(cu_flag(plan, lane), plan.flag_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
         const uint64_t t0 = wall_clock64();
-        while (!cu_copies_done(plan)) {
+        for (unsigned it = (unsigned)bid;; ++it) {
+            if (cu_flag_set(plan, bid)) break;
+            if ((!plan.flags || it % kSignalPollEvery == 0) && cu_copies_done(plan)) break;
             if (timed_out(t0, plan)) break;
             poll_pause(plan);
         }
@@ -230,7 +256,7 @@ __device__ void cu_copy_and_wait(const ChunkPlan &plan) {
 // copied rows are visible to the workgroup's later loads (after a barrier).
 __device__ __forceinline__ bool chunk_ready_now(const ChunkPlan &plan, int chunk, int bid) {
     if ((plan.cu_mask >> chunk) & 1) {
-        const bool ok = cu_copies_done(plan);
+        const bool ok = cu_flag_set(plan, bid) || cu_copies_done(plan);
         if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         return ok;
     }
@@ -306,7 +332,7 @@ __device__ __forceinline__ void tile_wait(const GemmProblem &p, const TileOrigin
         const int tid = threadIdx.x;
         if (plan.ts && bid == 0 && tid == 0) plan.ts[3 * plan.n_chunks] = wall_clock64();
         const bool cu = (plan.cu_mask >> o.chunk) & 1;
-        if (cu) cu_copy_and_wait(plan);  // the chunk is copied by the launch's own workgroups
+        if (cu) cu_copy_and_wait(plan, bid);  // the chunk is copied by the launch's own workgroups
         if (tid < 64) {
             if (!cu) wait_chunk(plan, o.chunk, bid);  // this chunk's copy pieces have landed
             if (plan.ts && tid == 0) {
