@@ -132,6 +132,27 @@ int sptl_ctx_set_wait_timeout_us(sptl_ctx *ctx, int64_t us);
 typedef enum { SPTL_COPY_STAGED = 0, SPTL_COPY_EVENTS = 1, SPTL_COPY_BLIT = 2, SPTL_COPY_SERIAL = 3 } sptl_copy_mode;
 int sptl_ctx_set_copy_mode(sptl_ctx *ctx, int mode, int blit_workgroups);
 
+/* Chunk order and link model of agmm_chunked's gather on ctx.  [AReaL "Potential Solution"]:
+ * each chunk's matmul starts as soon as the chunk has arrived, so chunks are processed in the
+ * order in which they are meant to arrive.
+ *   order  SPTL_ORDER_RING (the default): this rank's sub-chunks, then all of peer rank+1's, then
+ *          rank+2's, ...: the order in which a ring all-gather delivers them.
+ *          SPTL_ORDER_INTERLEAVED: this rank's sub-chunks, then sub-chunk 0 of peers rank+1,
+ *          rank+2, ..., then sub-chunk 1 of each, ...: the order in which a direct gather over
+ *          point-to-point links (one per peer, all streaming at once) delivers them.  The same
+ *          as the ring order when n_chunks == tp.
+ *   engines_per_peer  0 (the default): the staged path spreads the copies over all copy
+ *          engines.  k >= 1: the link model.  Each peer's copies run only on k copy engines of
+ *          their own, engines (p*k + j) mod E for the p-th peer after this rank.  They stand in
+ *          for one link per peer with a bandwidth of its own (one engine streams about 47 GB/s).
+ *          The launch's own workgroups then copy no lead chunks, and the own slot is spread over
+ *          all engines.  The staged path only; the event paths ignore it.
+ * Applies to agmm_chunked, reduce_norm_agmm_chunked and agmm_chunked_noalloc; not to
+ * agmm_backward or gemm_rs_chunked.  Every setting gives bit-identical outputs.  SPTL_E_NULL for a
+ * NULL ctx; SPTL_E_RANGE for an order outside the enum or engines_per_peer outside [0, 16]. */
+typedef enum { SPTL_ORDER_RING = 0, SPTL_ORDER_INTERLEAVED = 1 } sptl_chunk_order;
+int sptl_ctx_set_staging(sptl_ctx *ctx, int order, int engines_per_peer);
+
 /* Short text naming how agmm_chunked stages chunks on ctx with copy == NULL (copy engines
  * driven directly with a chunk-ordered GEMM, or one copy and one GEMM launch per chunk) and,
  * for the latter, why.  Owned by ctx; valid until ctx is destroyed.  Diagnostic only. */
@@ -159,7 +180,9 @@ const char *sptl_ctx_info(sptl_ctx *ctx);
  *   shard_src  host array [tp] of device pointers; shard_src[q] is rank q's sequence shard
  *            [seq_len/tp, hidden] bf16.  shard_src[rank] may point at this rank's slot of
  *            x_gathered (then it is not copied).  For q != rank it stands in for the
- *            peer's buffer and is read by the copy engine only.
+ *            peer's buffer and is read only by the staging copies: the copy engines and, for
+ *            the lead chunks of a first round that the own chunks do not fill, the launch's own
+ *            workgroups.
  *   x_gathered [seq_len, hidden] bf16 output: rank-major concatenation of the shards.
  *   w        [hidden, n_local] bf16 weight shard (logical [in, out]).
  *   y, y_dtype  [seq_len, n_local] output, SPTL_BF16 or SPTL_F32; y = x_gathered @ w with

@@ -27,6 +27,8 @@ struct sptl_ctx {
     bool events_only = false;           // SPTL_STAGING=events: no stager, copy mode SPTL_COPY_EVENTS
     int copy_mode = SPTL_COPY_STAGED;   // sptl_ctx_set_copy_mode
     int blit_wgs = 0;                   // workgroups of a blit-mode copy (0: sized to the copy)
+    int chunk_order = SPTL_ORDER_RING;  // sptl_ctx_set_staging
+    int engines_per_peer = 0;           // sptl_ctx_set_staging (0: every copy over all engines)
     std::string staging_info;           // how agmm_chunked stages chunks, and why
     int *err_dev = nullptr;             // device flag set by a timed-out staging wait
     uint64_t *ts_dev = nullptr;         // [3 * kMaxPlanChunks + 1] chunk timestamps
@@ -244,6 +246,22 @@ hipError_t stage_copy(const sptl_ctx *ctx, void *dst, const void *src, size_t by
     return hipMemcpyAsync(dst, src, bytes, cap ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU, s);
 }
 
+// The peers' chunks of agmm_chunked in processing (and arrival) order under ctx's chunk order:
+// ring, peer by peer (rank+1's sub-chunks, then rank+2's, ...), or interleaved, sub-chunk by
+// sub-chunk (sub-chunk 0 of rank+1, rank+2, ..., then sub-chunk 1 of each, ...).
+std::vector<int> peer_chunk_order(const sptl_ctx *ctx, int rank, int tp, int cpr) {
+    std::vector<int> out;
+    out.reserve((size_t)(tp - 1) * (size_t)cpr);
+    if (ctx->chunk_order == SPTL_ORDER_INTERLEAVED) {
+        for (int s = 0; s < cpr; ++s)
+            for (int d = 1; d < tp; ++d) out.push_back(((rank + d) % tp) * cpr + s);
+    } else {
+        for (int d = 1; d < tp; ++d)
+            for (int s = 0; s < cpr; ++s) out.push_back(((rank + d) % tp) * cpr + s);
+    }
+    return out;
+}
+
 // Chunk-ordered agmm: all staging copies go to the SDMA stager (striped over the copy
 // engines, released at the fork point), and one GEMM launch processes the row tiles in
 // chunk order, each tile waiting for its chunk's completion signal.  Arguments validated.
@@ -264,22 +282,24 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     };
     const bool own_aliased = shard_src[rank] == xg + (size_t)rank * cpr * chunk_elems;
 
-    // copies in arrival order (peers rank+1, rank+2, ...), then this rank's own slot
+    // copies in arrival order (the peers' chunks in the context's chunk order), then this rank's
+    // own slot; link: each copy's peer (0 for rank+1, ...), -1 for the own slot
     std::vector<sptl::CopyPiece> copies;
+    std::vector<int> link;
     sptl::GemmProblem gp{};
     sptl::ChunkPlan &plan = gp.plan;
     int pos = 0;
     for (int s = 0; s < cpr; ++s) plan.order[pos++] = rank * cpr + s;
-    for (int d = 1; d < tp; ++d) {
-        const int q = (rank + d) % tp;
-        for (int s = 0; s < cpr; ++s) {
-            const int c = q * cpr + s;
-            plan.order[pos++] = c;
-            copies.push_back({xg + (size_t)c * chunk_elems, src_chunk(q, s), chunk_bytes, c});
-        }
+    for (const int c : peer_chunk_order(ctx, rank, tp, cpr)) {
+        const int q = c / cpr;
+        plan.order[pos++] = c;
+        copies.push_back({xg + (size_t)c * chunk_elems, src_chunk(q, c % cpr), chunk_bytes, c});
+        link.push_back((q - rank + tp) % tp - 1);
     }
-    if (!own_aliased)
+    if (!own_aliased) {
         copies.push_back({xg + (size_t)rank * cpr * chunk_elems, shard_src[rank], chunk_bytes * cpr, sptl::kJoinChunk});
+        link.push_back(-1);
+    }
     const int n = n_chunks;
     gp.a = xg;
     gp.b = static_cast<const uint16_t *>(w);
@@ -320,13 +340,14 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     const int lead = (int)std::max<int64_t>(1, std::min<int64_t>(first_round - cpr, (int64_t)(n - cpr)));
     // When the own chunks do not fill the first round, the lead chunks' tiles are resident from
     // the start and would wait for the engines: they copy the lead chunks themselves (ChunkPlan,
-    // cu_n), and the engines take the later chunks.  SPTL_CU_LEAD=0 leaves every chunk to the
-    // engines (measurement aid).
+    // cu_n), and the engines take the later chunks.  Not under the link model, whose point is a
+    // rate per peer.  SPTL_CU_LEAD=0 leaves every chunk to the engines (measurement aid).
     static const bool cu_lead_on = [] {
         const char *e = getenv("SPTL_CU_LEAD");
         return !(e && !strcmp(e, "0"));
     }();
-    const int cu = cu_lead_on && first_round > cpr ? std::min(lead, sptl::kMaxCuChunks) : 0;
+    const bool links = ctx->engines_per_peer > 0;
+    const int cu = cu_lead_on && !links && first_round > cpr ? std::min(lead, sptl::kMaxCuChunks) : 0;
     plan.cu_n = cu;
     plan.cu_mask = 0;
     plan.cu_chunk_bytes = (int64_t)chunk_bytes;
@@ -336,7 +357,9 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
         plan.cu_mask |= 1ull << copies[(size_t)i].chunk;
     }
     copies.erase(copies.begin(), copies.begin() + cu);
-    std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies, std::max(1, lead - cu));
+    std::vector<sptl::CopyPiece> pieces =
+        links ? sptl::stager_plan_links(ctx->stager, copies, link, ctx->engines_per_peer)
+              : sptl::stager_plan(ctx->stager, copies, std::max(1, lead - cu));
 
     sptl::StageCall call;
     std::string why;
@@ -446,6 +469,18 @@ int sptl_ctx_set_copy_mode(sptl_ctx *ctx, int mode, int blit_workgroups) {
         return fail(SPTL_E_RANGE, "sptl_ctx_set_copy_mode: blit_workgroups=%d not in [0, 65535]", blit_workgroups);
     ctx->copy_mode = mode;
     ctx->blit_wgs = blit_workgroups;
+    return SPTL_OK;
+}
+
+int sptl_ctx_set_staging(sptl_ctx *ctx, int order, int engines_per_peer) {
+    if (!ctx) return fail(SPTL_E_NULL, "sptl_ctx_set_staging: ctx is NULL");
+    if (order != SPTL_ORDER_RING && order != SPTL_ORDER_INTERLEAVED)
+        return fail(SPTL_E_RANGE, "sptl_ctx_set_staging: order=%d", order);
+    if (engines_per_peer < 0 || engines_per_peer > sptl::kMaxPieces)
+        return fail(SPTL_E_RANGE, "sptl_ctx_set_staging: engines_per_peer=%d not in [0, %d]", engines_per_peer,
+                    sptl::kMaxPieces);
+    ctx->chunk_order = order;
+    ctx->engines_per_peer = engines_per_peer;
     return SPTL_OK;
 }
 
@@ -592,21 +627,18 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
     SPTL_HIP(hipStreamWaitEvent(ps, ctx->fork, 0));
 
     // ---- copy stream: every staging copy is enqueued before any GEMM ------------------
-    // Peers in ring order rank+1, rank+2, ... so the order matches arrival in a real ring.
-    // hipMemcpyDeviceToDeviceNoCU keeps the copies on the SDMA engines (a plain
-    // device-to-device copy may run as a copy kernel on the compute units); the blit mode
-    // runs them as a copy kernel on purpose.
-    for (int d = 1; d < tp; ++d) {
-        const int q = (rank + d) % tp;
-        for (int s = 0; s < cpr; ++s) {
-            const int c = q * cpr + s;
-            if (timing) {
-                SPTL_HIP(hipEventRecord(ctx->t_copy_start[c], ps));
-                ctx->t_has_copy[c] = 1;
-            }
-            SPTL_HIP(stage_copy(ctx, xg + (size_t)c * chunk_elems, src_chunk(q, s), chunk_bytes, ps, cap));
-            SPTL_HIP(hipEventRecord(ctx->ready[c], ps));
+    // Peers in the context's chunk order (ring by default: rank+1, rank+2, ..., the order of
+    // arrival in a real ring).  hipMemcpyDeviceToDeviceNoCU keeps the copies on the SDMA engines
+    // (a plain device-to-device copy may run as a copy kernel on the compute units); the blit
+    // mode runs them as a copy kernel on purpose.
+    const std::vector<int> peers = peer_chunk_order(ctx, rank, tp, cpr);
+    for (const int c : peers) {
+        if (timing) {
+            SPTL_HIP(hipEventRecord(ctx->t_copy_start[c], ps));
+            ctx->t_has_copy[c] = 1;
         }
+        SPTL_HIP(stage_copy(ctx, xg + (size_t)c * chunk_elems, src_chunk(c / cpr, c % cpr), chunk_bytes, ps, cap));
+        SPTL_HIP(hipEventRecord(ctx->ready[c], ps));
     }
     if (!own_aliased) {
         // this rank's own slot; its GEMMs read the source directly and do not wait for it
@@ -645,13 +677,9 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
     };
     for (int s = 0; s < cpr; ++s)
         if (int rc = run_chunk(rank * cpr + s, src_chunk(rank, s))) return rc;
-    for (int d = 1; d < tp; ++d) {
-        const int q = (rank + d) % tp;
-        for (int s = 0; s < cpr; ++s) {
-            const int c = q * cpr + s;
-            SPTL_HIP(hipStreamWaitEvent(cs, ctx->ready[c], 0));
-            if (int rc = run_chunk(c, xg + (size_t)c * chunk_elems)) return rc;
-        }
+    for (const int c : peers) {
+        SPTL_HIP(hipStreamWaitEvent(cs, ctx->ready[c], 0));
+        if (int rc = run_chunk(c, xg + (size_t)c * chunk_elems)) return rc;
     }
     // ---- join: later work on the compute stream sees x_gathered complete ---------------
     SPTL_HIP(hipStreamWaitEvent(cs, ctx->join, 0));

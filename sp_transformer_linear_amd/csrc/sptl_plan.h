@@ -17,6 +17,9 @@
 //     kMaxPieces pieces and no piece below kMinPiece / split bytes;
 //   * pieces are equal and rounded up to 256 bytes; the last piece of a copy takes the rest.
 // Each engine takes its pieces in the order returned.
+//
+// plan_pieces_links is the link model: each peer's copies run on engines of their own, as each
+// peer's chunks would come over a point-to-point link of their own on a node.
 #pragma once
 
 #include <stddef.h>
@@ -57,25 +60,28 @@ inline int later_group(int engines, size_t chunk_bytes) {
 // splits the later copies together in successive groups of `group` copies, like the leading
 // group (1: each later copy striped over all engines on its own); a last group shorter than
 // `group` is merged into the one before when both fit on the engines.
+// Appends copy i cut into equal pieces rounded to 256 bytes (the last takes the remainder, so
+// at most n pieces), on engines first, first + 1, ... (mod engines).
+inline void cut_copy(std::vector<PlanPiece> &out, const std::vector<PlanCopy> &copies, int i, size_t n, int first,
+                     int engines) {
+    const PlanCopy &c = copies[(size_t)i];
+    const size_t step = ((c.bytes / n) + 255) & ~(size_t)255;
+    size_t off = 0;
+    int piece = 0;
+    while (off < c.bytes) {
+        const size_t b = c.bytes - off < step ? c.bytes - off : step;
+        out.push_back({i, off, b, c.chunk, piece, (first + piece) % engines});
+        off += b;
+        ++piece;
+    }
+}
+
 inline std::vector<PlanPiece> plan_pieces(const std::vector<PlanCopy> &copies, int lead, int engines, size_t split,
                                           int group = 1) {
     std::vector<PlanPiece> out;
     size_t E = (size_t)engines * split;
     if (E > (size_t)kMaxPieces) E = kMaxPieces;
-    // equal pieces of copy i rounded to 256 bytes (the last takes the remainder, so at most n
-    // pieces), on engines first, first + 1, ...
-    auto cut = [&](int i, size_t n, int first) {
-        const PlanCopy &c = copies[(size_t)i];
-        const size_t step = ((c.bytes / n) + 255) & ~(size_t)255;
-        size_t off = 0;
-        int piece = 0;
-        while (off < c.bytes) {
-            const size_t b = c.bytes - off < step ? c.bytes - off : step;
-            out.push_back({i, off, b, c.chunk, piece, (first + piece) % engines});
-            off += b;
-            ++piece;
-        }
-    };
+    auto cut = [&](int i, size_t n, int first) { cut_copy(out, copies, i, n, first, engines); };
     // copies [b, e) (e - b <= engines) split together: each takes a run of distinct engines, about
     // in proportion to its size, and the runs cover every engine
     auto joint = [&](int b, int e) {
@@ -116,6 +122,29 @@ inline std::vector<PlanPiece> plan_pieces(const std::vector<PlanCopy> &copies, i
             cut(i, n, 0);
             ++i;
         }
+    }
+    return out;
+}
+
+// Link model.  link[i] is the peer of copy i (0 for the first peer after this rank, 1 for the
+// next, ...; -1 for a copy that crosses no link, such as this rank's own slot).  Peer p's copies
+// run only on its `per` engines (p * per + j) mod engines, j < per, each copy striped over them in
+// the order given (no piece below kMinPiece unless the copy is smaller); the other copies are
+// striped over every engine.  Each engine takes its pieces in the order returned, so a peer's
+// copies land in their order, at the rate of its engines alone.
+inline std::vector<PlanPiece> plan_pieces_links(const std::vector<PlanCopy> &copies, const std::vector<int> &link,
+                                                int engines, int per) {
+    std::vector<PlanPiece> out;
+    if (per < 1) per = 1;
+    if (per > engines) per = engines;
+    for (int i = 0; i < (int)copies.size(); ++i) {
+        const bool peer = link[(size_t)i] >= 0;
+        size_t n = (size_t)(peer ? per : engines);
+        if (n > (size_t)kMaxPieces) n = kMaxPieces;
+        const size_t by_size = copies[(size_t)i].bytes / kMinPiece;
+        if (n > by_size) n = by_size < 1 ? 1 : by_size;
+        cut_copy(out, copies, i, n, peer ? (int)(((size_t)link[(size_t)i] * (size_t)per) % (size_t)engines) : 0,
+                 engines);
     }
     return out;
 }

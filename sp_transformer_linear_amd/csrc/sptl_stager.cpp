@@ -492,6 +492,22 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
     return out;
 }
 
+std::vector<CopyPiece> stager_plan_links(const SdmaStager *s, const std::vector<CopyPiece> &copies,
+                                         const std::vector<int> &link, int per) {
+    std::vector<PlanCopy> pc;
+    pc.reserve(copies.size());
+    for (const CopyPiece &c : copies) pc.push_back({c.bytes, c.chunk});
+    std::vector<CopyPiece> out;
+    for (const PlanPiece &q : plan_pieces_links(pc, link, (int)s->engines.size(), per)) {
+        const CopyPiece &c = copies[(size_t)q.copy];
+        CopyPiece piece{static_cast<char *>(c.dst) + q.offset, static_cast<const char *>(c.src) + q.offset, q.bytes,
+                        q.chunk, q.piece};
+        piece.engine = q.engine;
+        out.push_back(piece);
+    }
+    return out;
+}
+
 bool stager_take_timeouts(SdmaStager *s) {
     for (int set = 0; set < kSets; ++set)
         if (s->sets[set].epoch && __atomic_load_n(s->finished(set), __ATOMIC_ACQUIRE) == s->sets[set].epoch)

@@ -74,6 +74,12 @@ int stager_engine_count(const SdmaStager *s);
 std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPiece> &copies, int lead = 1,
                                    int group = 0);
 
+// The link model (plan_pieces_links, sptl_plan.h): link[i] is copy i's peer (0, 1, ... after this
+// rank; -1 for a copy that crosses no link), and each peer's copies run only on `per` engines of
+// their own.  Returned in submission order with chunk and piece ids, like stager_plan.
+std::vector<CopyPiece> stager_plan_links(const SdmaStager *s, const std::vector<CopyPiece> &copies,
+                                         const std::vector<int> &link, int per);
+
 // Reserves a completion-signal set for one call whose consuming kernel has `workgroups`
 // workgroups, and arms it with the number of pieces per chunk.  Blocks (bounded) while the
 // set's previous call is still running and, if a wait of that call timed out, until its copies

@@ -32,6 +32,8 @@ MAX_PARTIALS, MAX_TP, MAX_CHUNKS = 16, 64, 512
 MAX_K, MAX_N = 2097152, 8388608
 COPY_STAGED, COPY_EVENTS, COPY_BLIT, COPY_SERIAL = 0, 1, 2, 3
 COPY_MODES = {"staged": COPY_STAGED, "events": COPY_EVENTS, "blit": COPY_BLIT, "serial": COPY_SERIAL}
+ORDER_RING, ORDER_INTERLEAVED = 0, 1
+CHUNK_ORDERS = {"ring": ORDER_RING, "interleaved": ORDER_INTERLEAVED}
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -47,6 +49,7 @@ _SIGS = {
     "sptl_ctx_info": ([_vp], ctypes.c_char_p),
     "sptl_ctx_set_wait_timeout_us": ([_vp, _i64], _int),
     "sptl_ctx_set_copy_mode": ([_vp, _int, _int], _int),
+    "sptl_ctx_set_staging": ([_vp, _int, _int], _int),
     "agmm_chunked": ([_vp, _i64, _i64, _i64, _int, _int, _int, _ptrs, _vp, _vp, _vp, _int, _vp, _vp,
                       _int], _int),
     "agmm_chunked_noalloc": ([_vp, _i64, _i64, _i64, _int, _int, _int, _ptrs, _vp, _vp, _vp, _int, _vp], _int),
@@ -234,6 +237,12 @@ class Context:
         "serial" (or the COPY_* value); blit_workgroups sizes the blit mode's copy kernels."""
         m = COPY_MODES[mode] if isinstance(mode, str) else int(mode)
         _check(_lib.sptl_ctx_set_copy_mode(self.handle, m, int(blit_workgroups)))
+
+    def set_staging(self, order="ring", engines_per_peer: int = 0) -> None:
+        """Chunk order of the gather ("ring" or "interleaved", or the ORDER_* value) and the link
+        model (engines_per_peer > 0: each peer's copies on that many copy engines of their own)."""
+        o = CHUNK_ORDERS[order] if isinstance(order, str) else int(order)
+        _check(_lib.sptl_ctx_set_staging(self.handle, o, int(engines_per_peer)))
 
     def info(self) -> str:
         """How agmm_chunked stages chunks on this context (diagnostic)."""

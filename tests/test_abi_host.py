@@ -127,6 +127,11 @@ def test_copy_mode_option_rejects_null_ctx(sptl):
     assert set(sptl.COPY_MODES.values()) == {0, 1, 2, 3}
 
 
+def test_staging_option_rejects_null_ctx(sptl):
+    assert sptl._lib.sptl_ctx_set_staging(None, sptl.ORDER_INTERLEAVED, 2) == 1
+    assert set(sptl.CHUNK_ORDERS.values()) == {0, 1}
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(ctx=None), 1),                                   # the set-up lives in the context
     (dict(tp=0), 6), (dict(y_dtype=3), 5), (dict(w=A + 4), 4),

@@ -156,3 +156,40 @@ def test_edge_cases(driver, engines, split, lead, sizes):
     assert all(0 <= e < engines for _, _, _, e in (p for ps in by_copy.values() for p in ps))
     if split == 16:
         assert all(len(ps) == MAX_PIECES for ps in by_copy.values())
+
+
+def plan_links(driver, engines, per, sizes, links):
+    args = [f"{n}:{l}" if l is not None else str(n) for n, l in zip(sizes, links)]
+    out = subprocess.run([driver, "links", str(engines), str(per), *args], check=True, capture_output=True,
+                         text=True, timeout=30).stdout.splitlines()
+    assert out[0] == "group 0"
+    return [tuple(int(v) for v in line.split()) for line in out[1:]]
+
+
+@pytest.mark.parametrize("engines,per,sizes,links", [
+    # 8192 x 4096 rows, tp = 8, two sub-chunks per rank in the interleaved order, then the own slot
+    (14, 2, [4 * MiB] * 14 + [8 * MiB], [0, 1, 2, 3, 4, 5, 6] * 2 + [None]),
+    (14, 1, [64 * MiB] * 7 + [64 * MiB], list(range(7)) + [None]),   # M-sweep top, one engine per peer
+    (14, 4, [16 * MiB] * 6, [0, 1, 2, 0, 1, 2]),                     # tp = 4, engines 0-11
+    (4, 2, [8 * MiB] * 7, list(range(7))),                            # more peers than engine pairs: shared
+    (14, 2, [1000, 300 * 1024], [0, 1]),                              # copies below a piece: one piece
+])
+def test_link_model(driver, engines, per, sizes, links):
+    pieces = plan_links(driver, engines, per, sizes, links)
+    by_copy = check_cover(pieces, sizes, 1)
+    for c, l in enumerate(links):
+        used = [e for _, _, _, e in by_copy[c]]
+        if l is None:  # no link: striped over every engine
+            assert used == list(range(len(used))) and len(used) == min(engines, MAX_PIECES, max(1, sizes[c] // MIN_PIECE))
+        else:  # a peer's copies only on its own engines, in order
+            own = [(l * per + j) % engines for j in range(min(per, engines))]
+            assert used == own[:len(used)]
+            assert len(used) == min(per, engines, max(1, sizes[c] // MIN_PIECE))
+    # pieces in copy order, so each engine takes a peer's copies in the order given
+    order = [c for c, *_ in pieces]
+    assert order == sorted(order)
+    if engines >= per * (max(l for l in links if l is not None) + 1):  # disjoint engine sets
+        for a in range(len(links)):
+            for b in range(len(links)):
+                if links[a] is not None and links[b] is not None and links[a] != links[b]:
+                    assert not {e for *_, e in by_copy[a]} & {e for *_, e in by_copy[b]}
