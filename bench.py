@@ -640,6 +640,67 @@ def main():
 
     copy_modes = copy_mode_study(L, L.w_col, reps, wl.n_chunks) if studies else None
 
+    # Node model (how the gather would run on a node of point-to-point links): each peer's copies
+    # on copy engines of their own (one engine streams about 47 GB/s, near one xGMI link's rate
+    # in one direction), the ring order (peer by peer) against the interleaved order (sub-chunk
+    # by sub-chunk, every link streaming at once), with one and four sub-chunks per rank.  Each
+    # configuration: agmm paired with the pre-staged GEMM (exposed time) and its staging alone
+    # (8-column weight, last landing), on a context of its own.
+    ctx_node = sptl.Context(0)
+
+    def node_model_study(T, w, reps):
+        M_, K_ = T.xg.shape
+        N_ = w.shape[1]
+        tp_ = len(T.shards)
+        fl = 2.0 * M_ * K_ * N_
+        y_tmp = torch.empty((M_, N_), dtype=torch.bfloat16, device=dev)
+        w_thin = torch.zeros((K_, 8), dtype=torch.bfloat16, device=dev)
+        y_thin = torch.empty((M_, 8), dtype=torch.bfloat16, device=dev)
+        configs = [("shared_ring", "ring", 0, 1), ("links2_ring", "ring", 2, 1), ("links2_ring_x4", "ring", 2, 4),
+                   ("links2_interleaved_x4", "interleaved", 2, 4), ("links1_ring", "ring", 1, 1),
+                   ("links1_interleaved_x4", "interleaved", 1, 4)]
+        res = {"staged_bytes": (tp_ - 1) * (M_ // tp_) * K_ * 2}
+        try:
+            for name, order, per, sub in configs:
+                n = tp_ * sub
+                if M_ % n:
+                    continue
+                ctx_node.set_staging(order, per)
+                for _ in range(3):
+                    agmm(T, w, T.y_col, n_chunks=n, c=ctx_node)
+                pairs = []
+                for _ in range(2 * reps):
+                    e = [ev() for _ in range(3)]
+                    e[0].record(cs)
+                    agmm(T, w, T.y_col, n_chunks=n, c=ctx_node)
+                    e[1].record(cs)
+                    sptl.gemm_partial(T.xg, w, y_tmp, stream=cs, ctx=ctx)
+                    e[2].record(cs)
+                    pairs.append(e)
+                torch.cuda.synchronize()
+                ctx_node.check()
+                a = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in pairs])
+                copy_runs = []
+                for _ in range(reps):
+                    agmm(T, w_thin, y_thin, n_chunks=n, c=ctx_node)
+                    agmm(T, w_thin, y_thin, timing=True, n_chunks=n, c=ctx_node)
+                    copy_runs.append(max(r[1] for r in ctx_node.timeline(n)))
+                ctx_node.check()
+                t_copy = float(np.median(copy_runs))
+                ex = max(0.0, float(np.median(a[:, 0] - a[:, 1])))
+                res[name] = {"n_chunks": n, "order": order, "engines_per_peer": per, "path": ctx_node.info(),
+                             "ms": round(float(np.median(a[:, 0])), 4),
+                             "tflops": round(fl / (float(np.median(a[:, 0])) * 1e-3) / 1e12, 2),
+                             "exposed_ms": round(ex, 4), "copy_alone_ms": round(t_copy, 4),
+                             "copy_alone_GBps": round(res["staged_bytes"] / (t_copy * 1e-3) / 1e9, 1),
+                             "copy_hidden_frac": None if t_copy <= 0 else round(max(0.0, 1.0 - ex / t_copy), 4)}
+        finally:
+            ctx_node.set_staging("ring", 0)
+        del y_tmp, w_thin, y_thin
+        return res
+
+    node_model = node_model_study(L, L.w_col, reps) if studies else None
+
     # Backward ("Add forward all-gather overlap", "Scope": the backward gathers again): the
     # re-gather on the copy engines under the input-gradient GEMM, then the weight-gradient GEMM;
     # against the same call with every shard already in place (the two GEMMs alone) and the
@@ -780,6 +841,7 @@ def main():
             "staging_check": staging_check,
             "boundary": boundary,
             "copy_modes": copy_modes,
+            "node_model": node_model,
             "launch": launch,
             "backward": backward,
         },
@@ -911,6 +973,7 @@ def main():
             "reduce_GBps": round(gbs(rb, ms[2]), 1), "reduce_frac_hbm": round(gbs(rb, ms[2]) / PEAK_HBM_GBS, 4),
             "reduce_GBps_cold": round(gbs(rb, rc), 1), "reduce_frac_hbm_cold": round(gbs(rb, rc) / PEAK_HBM_GBS, 4),
             "reduce_scatter": reduce_scatter(T, reps) if wo.M % wo.tp == 0 else None,
+            "node_model": node_model_study(T, T.w_col, reps),
         }
         del T, fns
         torch.cuda.empty_cache()
@@ -920,6 +983,7 @@ def main():
 
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    ctx_node.close()
     ctx_serial.close()
     ctx.close()
     print(json.dumps(out), flush=True)
