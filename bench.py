@@ -694,6 +694,41 @@ def main():
                              "exposed_ms": round(ex, 4), "copy_alone_ms": round(t_copy, 4),
                              "copy_alone_GBps": round(res["staged_bytes"] / (t_copy * 1e-3) / 1e9, 1),
                              "copy_hidden_frac": None if t_copy <= 0 else round(max(0.0, 1.0 - ex / t_copy), 4)}
+            # the reduce-scatter mirror's pushes, each peer slice on its peer's engines: paired with
+            # gemm_partial, the exposed time of the copies released slice by slice
+            if T.own.shape[0] % tp_ == 0:
+                R_ = T.own.shape[0] // tp_
+                dst = [None] + [torch.empty((R_, T.own.shape[1]), dtype=torch.bfloat16, device=dev)
+                                for _ in range(tp_ - 1)]
+                part = torch.empty_like(T.own)
+                for name, order, per, sub in (("rs_shared", "ring", 0, 1), ("rs_links2", "ring", 2, 1),
+                                              ("rs_links2_interleaved_x4", "interleaved", 2, 4),
+                                              ("rs_links1", "ring", 1, 1),
+                                              ("rs_links1_interleaved_x4", "interleaved", 1, 4)):
+                    if T.own.shape[0] % (tp_ * sub):
+                        continue
+                    ctx_node.set_staging(order, per)
+                    for _ in range(3):
+                        sptl.gemm_rs_chunked(T.a_row, T.w_row, part, dst, rank=0, n_chunks=tp_ * sub, stream=cs,
+                                             ctx=ctx_node)
+                    pairs = []
+                    for _ in range(2 * reps):
+                        e = [ev() for _ in range(3)]
+                        e[0].record(cs)
+                        sptl.gemm_rs_chunked(T.a_row, T.w_row, part, dst, rank=0, n_chunks=tp_ * sub, stream=cs,
+                                             ctx=ctx_node)
+                        e[1].record(cs)
+                        gemm_p(T)
+                        e[2].record(cs)
+                        pairs.append(e)
+                    torch.cuda.synchronize()
+                    ctx_node.check()
+                    a = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in pairs])
+                    res[name] = {"n_chunks": tp_ * sub, "order": order, "engines_per_peer": per,
+                                 "ms": round(float(np.median(a[:, 0])), 4),
+                                 "ms_gemm_partial": round(float(np.median(a[:, 1])), 4),
+                                 "exposed_ms": round(max(0.0, float(np.median(a[:, 0] - a[:, 1]))), 4)}
+                del dst, part
         finally:
             ctx_node.set_staging("ring", 0)
         del y_tmp, w_thin, y_thin

@@ -147,8 +147,9 @@ int sptl_ctx_set_copy_mode(sptl_ctx *ctx, int mode, int blit_workgroups);
  *          for one link per peer with a bandwidth of its own (one engine streams about 47 GB/s).
  *          The launch's own workgroups then copy no lead chunks, and the own slot is spread over
  *          all engines.  The staged path only; the event paths ignore it.
- * Applies to agmm_chunked, reduce_norm_agmm_chunked and agmm_chunked_noalloc; not to
- * agmm_backward or gemm_rs_chunked.  Every setting gives bit-identical outputs.  SPTL_E_NULL for a
+ * Both apply to agmm_chunked, reduce_norm_agmm_chunked, agmm_chunked_noalloc and gemm_rs_chunked
+ * (its send order; each peer sub-slice pushed on its peer's engines); the link model also to the
+ * staged path of agmm_backward (the re-gather).  Every setting gives bit-identical outputs.  SPTL_E_NULL for a
  * NULL ctx; SPTL_E_RANGE for an order outside the enum or engines_per_peer outside [0, 16]. */
 typedef enum { SPTL_ORDER_RING = 0, SPTL_ORDER_INTERLEAVED = 1 } sptl_chunk_order;
 int sptl_ctx_set_staging(sptl_ctx *ctx, int order, int engines_per_peer);
@@ -283,27 +284,34 @@ int gemm_partial(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden
  *
  * [AReaL "Potential Solution"]: the partial sums of a row-parallel linear are reduce-scattered
  * at the end of the sub-layer (each rank keeps the sum over ranks of its own sequence slice);
- * [MLM "Scope"] leaves that half of the overlap out.  Here the partial is computed slice by
- * slice in send order (the slices of ranks rank+1, ..., rank+tp-1, then this rank's own), and
- * each peer's slice is copied out by the SDMA copy engines (striped over all of them) as soon as
- * its rows are written, while the following slices are computed.
- *   seq_len, k_local, hidden, a, w: as gemm_partial; seq_len % tp == 0; slice q is rows
+ * [MLM "Scope"] leaves that half of the overlap out.  Here the partial is computed sub-slice by
+ * sub-slice in send order, and each peer's sub-slice is copied out by the SDMA copy engines as
+ * soon as its rows are written, while the following sub-slices are computed.
+ *   seq_len, k_local, hidden, a, w: as gemm_partial; slice q is rows
  *            [q seq_len/tp, (q+1) seq_len/tp) of partial
+ *   n_chunks sub-slice count: n_chunks % tp == 0, seq_len % n_chunks == 0, n_chunks <= 64.  Each
+ *            slice is n_chunks/tp sub-slices of seq_len/n_chunks rows.  Send order: the peers'
+ *            sub-slices in the context's chunk order (sptl_ctx_set_staging; the ring order takes
+ *            all of rank+1's, then rank+2's, ...; the interleaved order takes sub-slice 0 of
+ *            every peer, then sub-slice 1, ...), then this rank's own.  n_chunks == tp: one
+ *            slice at a time, peers rank+1, ..., rank+tp-1, then the own.
  *   partial  [seq_len, hidden] bf16: this rank's whole partial sum, the same bits as gemm_partial
  *   dst      host array [tp] of device pointers: dst[q] ([seq_len/tp, hidden] bf16) receives slice q
  *            for q != rank (it stands in for rank q's receive buffer); dst[rank] is not used and
  *            may be NULL.  A dst[q] that is slice q of partial itself is left as is.
  *   tp in [1, 64].  One GEMM launch on `compute`; the launch ends after every copy has landed, so
  *   later work on `compute` sees partial and every dst complete.  The copies are released by the
- *   context's worker thread as the kernel reports each slice done.  Slices of a height that fits
- *   no chunk tile (a multiple of 128 rows), or a context without copy engines: the GEMM, then
- *   the copies, on `compute`.
- * Errors: SPTL_E_NULL (a, w, partial, dst or a peer's dst[q] NULL), SPTL_E_RANGE (tp, rank),
- * SPTL_E_SHAPE / SPTL_E_DIVISIBILITY (sizes, seq_len % tp), SPTL_E_ALIGN (any pointer not 16-byte
- * aligned), SPTL_E_ASYNC (an earlier call's copies timed out and are still draining); nothing is
- * launched then.  The kernel's bounded wait for the copies reports through sptl_ctx_check.
+ *   context's worker thread as the kernel reports each sub-slice done.  Sub-slices of a height
+ *   that fits no chunk tile (a multiple of 128 rows), a context without copy engines or a stream
+ *   under capture: one GEMM launch per sub-slice in send order, each peer sub-slice copied on the
+ *   context's copy stream after its event.
+ * Errors: SPTL_E_NULL (a, w, partial, dst or a peer's dst[q] NULL), SPTL_E_RANGE (tp, n_chunks,
+ * rank), SPTL_E_SHAPE / SPTL_E_DIVISIBILITY (sizes, n_chunks % tp, seq_len % n_chunks),
+ * SPTL_E_ALIGN (any pointer not 16-byte aligned), SPTL_E_ASYNC (an earlier call's copies timed
+ * out and are still draining); nothing is launched then.  The kernel's bounded wait for the
+ * copies reports through sptl_ctx_check.
  */
-int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden, int tp, int rank,
+int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden, int tp, int n_chunks, int rank,
                     const void *a, const void *w, void *partial, void *const *dst, void *compute);
 
 /*

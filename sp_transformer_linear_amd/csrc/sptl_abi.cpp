@@ -795,16 +795,23 @@ int gemm_partial(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden
     return SPTL_OK;
 }
 
-int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden, int tp, int rank,
-                    const void *a, const void *w, void *partial, void *const *dst, void *compute) {
+int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hidden, int tp, int n_chunks,
+                    int rank, const void *a, const void *w, void *partial, void *const *dst, void *compute) {
     static const char *fn = "gemm_rs_chunked";
     if (!a || !w || !partial || !dst) return fail(SPTL_E_NULL, "%s: NULL pointer argument", fn);
     if (tp < 1 || tp > sptl::kMaxPlanChunks)
         return fail(SPTL_E_RANGE, "%s: tp=%d not in [1, %d]", fn, tp, sptl::kMaxPlanChunks);
+    if (n_chunks < 1 || n_chunks > sptl::kMaxPlanChunks)
+        return fail(SPTL_E_RANGE, "%s: n_chunks=%d not in [1, %d]", fn, n_chunks, sptl::kMaxPlanChunks);
     if (rank < 0 || rank >= tp) return fail(SPTL_E_RANGE, "%s: rank=%d not in [0, %d)", fn, rank, tp);
+    if (n_chunks % tp) return fail(SPTL_E_DIVISIBILITY, "%s: n_chunks=%d not a multiple of tp=%d", fn, n_chunks, tp);
     if (seq_len < 0) return fail(SPTL_E_SHAPE, "%s: seq_len=%lld", fn, (long long)seq_len);
-    if (seq_len % tp) return fail(SPTL_E_DIVISIBILITY, "%s: seq_len=%lld not a multiple of tp=%d", fn, (long long)seq_len, tp);
+    if (seq_len % n_chunks)
+        return fail(SPTL_E_DIVISIBILITY, "%s: seq_len=%lld not a multiple of n_chunks=%d", fn, (long long)seq_len,
+                    n_chunks);
     const int64_t R = seq_len / tp;
+    const int sub = n_chunks / tp;              // sub-slices per slice
+    const int64_t Rc = seq_len / n_chunks;      // rows per sub-slice
     if (int rc = check_gemm_dims(R, k_local, hidden)) return rc;
     for (int q = 0; q < tp; ++q) {
         if (q != rank && !dst[q]) return fail(SPTL_E_NULL, "%s: dst[%d] is NULL", fn, q);
@@ -820,6 +827,8 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
     auto *pb = static_cast<uint16_t *>(partial);
     const size_t slice_elems = (size_t)R * (size_t)hidden;
     const size_t slice_bytes = slice_elems * 2;
+    const size_t sub_elems = (size_t)Rc * (size_t)hidden;
+    const size_t sub_bytes = sub_elems * 2;
     sptl::GemmProblem gp{};
     gp.a = static_cast<const uint16_t *>(a);
     gp.b = static_cast<const uint16_t *>(w);
@@ -832,6 +841,14 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
     gp.ldc = hidden;
     gp.c_f32 = false;
     auto in_place = [&](int q) { return q == rank || dst[q] == pb + (size_t)q * slice_elems; };
+    // sub-slice c (rows [c Rc, (c+1) Rc) of partial) is sub-slice c % sub of slice c / sub
+    auto sub_dst = [&](int c) {
+        return static_cast<uint16_t *>(dst[c / sub]) + (size_t)(c % sub) * sub_elems;
+    };
+    // send order: the peers' sub-slices in the context's chunk order (copied out while later
+    // sub-slices compute), this rank's own last
+    std::vector<int> order = peer_chunk_order(ctx, rank, tp, sub);
+    for (int j = 0; j < sub; ++j) order.push_back(rank * sub + j);
     if (ctx->copy_mode == SPTL_COPY_SERIAL) {
         // no overlap (the baseline the overlap is measured against): the GEMM, then the copies
         const bool cap = capturing(cs);
@@ -842,25 +859,24 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
         }
         return SPTL_OK;
     }
-    if (!staged_path(ctx, R, tp, cs)) {
-        // per-slice events: one GEMM launch per slice on `compute` in send order, each peer slice
-        // then copied on the copy stream after its event while the next slices compute
+    if (!staged_path(ctx, Rc, n_chunks, cs)) {
+        // per-sub-slice events: one GEMM launch per sub-slice on `compute` in send order, each
+        // peer sub-slice then copied on the copy stream after its event while the next compute
         const bool cap = capturing(cs);
         hipStream_t ps;
         if (int rc = copy_stream_of(ctx, &ps)) return rc;
-        if (int rc = grow_events(ctx->ready, tp)) return rc;
+        if (int rc = grow_events(ctx->ready, n_chunks)) return rc;
         sptl::GemmProblem sp = gp;
-        sp.m = R;
+        sp.m = Rc;
         bool copied = false;
-        for (int d = 1; d <= tp; ++d) {
-            const int q = (rank + d) % tp;
-            sp.a = gp.a + (size_t)q * (size_t)R * (size_t)k_local;
-            sp.c = pb + (size_t)q * slice_elems;
+        for (const int c : order) {
+            sp.a = gp.a + (size_t)c * (size_t)Rc * (size_t)k_local;
+            sp.c = pb + (size_t)c * sub_elems;
             SPTL_HIP(sptl::launch_gemm(sp, cs));
-            if (in_place(q)) continue;
-            SPTL_HIP(hipEventRecord(ctx->ready[q], cs));
-            SPTL_HIP(hipStreamWaitEvent(ps, ctx->ready[q], 0));
-            SPTL_HIP(stage_copy(ctx, dst[q], pb + (size_t)q * slice_elems, slice_bytes, ps, cap));
+            if (in_place(c / sub)) continue;
+            SPTL_HIP(hipEventRecord(ctx->ready[c], cs));
+            SPTL_HIP(hipStreamWaitEvent(ps, ctx->ready[c], 0));
+            SPTL_HIP(stage_copy(ctx, sub_dst(c), pb + (size_t)c * sub_elems, sub_bytes, ps, cap));
             copied = true;
         }
         if (copied) {
@@ -870,25 +886,27 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
         }
         return SPTL_OK;
     }
-    // slices in send order: the peers' r + 1, r + 2, ... (copied out while later slices compute),
-    // this rank's own last
     std::vector<sptl::CopyPiece> copies;
+    std::vector<int> link;  // each sub-slice's peer (0 for rank+1, ...), for the link model
     sptl::ChunkPlan &plan = gp.plan;
-    for (int d = 1; d <= tp; ++d) {
-        const int q = (rank + d) % tp;
-        plan.order[d - 1] = q;
-        if (q == rank || dst[q] == pb + (size_t)q * slice_elems) continue;  // stays in place
-        copies.push_back({dst[q], pb + (size_t)q * slice_elems, slice_bytes, q});
+    for (int i = 0; i < n_chunks; ++i) {
+        const int c = order[(size_t)i], q = c / sub;
+        plan.order[i] = c;
+        if (in_place(q)) continue;  // stays in place
+        copies.push_back({sub_dst(c), pb + (size_t)c * sub_elems, sub_bytes, c});
+        link.push_back((q - rank + tp) % tp - 1);
     }
-    plan.chunk_rows = (int)R;
-    plan.n_chunks = tp;
+    plan.chunk_rows = (int)Rc;
+    plan.n_chunks = n_chunks;
     plan.own_first = 0;
     plan.own_count = 0;
     plan.own_a = gp.a;
     plan.err = ctx->err_dev;
     plan.timeout_ticks = (uint64_t)ctx->wallclock_khz * ctx->wait_timeout_us / 1000u;
     plan.copy_out = true;
-    std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies, 1, 1);
+    std::vector<sptl::CopyPiece> pieces = ctx->engines_per_peer > 0
+                                              ? sptl::stager_plan_links(ctx->stager, copies, link, ctx->engines_per_peer)
+                                              : sptl::stager_plan(ctx->stager, copies, 1, 1);
     const int64_t wgs = sptl::gemm_workgroups(gp);
     // The release of a slice (see ChunkPlan): the XCD's last tile of the slice writes its L2
     // back, which needs every XCD's share of a copied slice to be equal; else every tile does.
@@ -900,7 +918,7 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
         const char *e = getenv("SPTL_RS_SHARE_SKEW");  // under-counted share (test aid: the report)
         return e ? (int)(strtol(e, nullptr, 10) & 1) : 0;
     }();
-    std::vector<int64_t> xt((size_t)tp * 8);
+    std::vector<int64_t> xt((size_t)n_chunks * 8);
     sptl::chunk_xcd_tiles(gp, xt.data());
     plan.flush_each_tile = each_tile;
     for (const sptl::CopyPiece &pc : copies) {
@@ -925,8 +943,8 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
     std::string why;
     if (int rc = sptl::stager_begin(ctx->stager, pieces, wgs, &call, &why))
         return fail(rc == -2 ? SPTL_E_ASYNC : SPTL_E_HIP, "%s: %s", fn, why.c_str());
-    for (int c = 0; c < tp; ++c) {
-        plan.ready[c] = call.ready[c];  // copy-out: the slice's outgoing copies
+    for (int c = 0; c < n_chunks; ++c) {
+        plan.ready[c] = call.ready[c];  // copy-out: the sub-slice's outgoing copies
         plan.ready_n[c] = call.ready_n[c];
     }
     plan.slice_ready = call.slice_ready;
@@ -943,7 +961,7 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
     plan.all_last = call.all_last;
     // the call's slice counters start at zero (a fill kernel rather than a memset; the set's
     // previous call has finished, stager_begin saw to that)
-    hipError_t he = sptl::launch_fill_u64(call.slice_count, (int64_t)tp * sptl::kEndLine, 0ull, cs);
+    hipError_t he = sptl::launch_fill_u64(call.slice_count, (int64_t)n_chunks * sptl::kEndLine, 0ull, cs);
     if (he == hipSuccess) he = hipEventRecord(call.fork, cs);
     if (he == hipSuccess) he = sptl::launch_gemm(gp, cs);
     if (he != hipSuccess) {
@@ -1011,10 +1029,13 @@ int agmm_backward(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_loca
     gw.layout = sptl::kLayoutAKMajor;
     // the copies, peers in arrival order (rank+1, rank+2, ...) then the own slot unless aliased
     std::vector<sptl::CopyPiece> copies;
+    std::vector<int> link;  // each copy's peer (0 for rank+1, ...; -1 for the own slot), for the link model
     for (int d = 1; d <= tp; ++d) {
         const int q = (rank + d) % tp;
-        if (shard_src[q] != xg + (size_t)q * shard_elems)
+        if (shard_src[q] != xg + (size_t)q * shard_elems) {
             copies.push_back({xg + (size_t)q * shard_elems, shard_src[q], shard_elems * 2, q});
+            link.push_back(q == rank ? -1 : d - 1);
+        }
     }
     const bool cap = capturing(cs);
     if (ctx->copy_mode == SPTL_COPY_SERIAL) {
@@ -1044,7 +1065,9 @@ int agmm_backward(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_loca
     }
     // staged: the copy engines take the re-gather at the fork point, dx's GEMM runs meanwhile (it
     // does not read x), a one-wave kernel then waits for every piece, and dw's GEMM follows it
-    std::vector<sptl::CopyPiece> pieces = sptl::stager_plan(ctx->stager, copies, 1, 1);
+    std::vector<sptl::CopyPiece> pieces = ctx->engines_per_peer > 0
+                                              ? sptl::stager_plan_links(ctx->stager, copies, link, ctx->engines_per_peer)
+                                              : sptl::stager_plan(ctx->stager, copies, 1, 1);
     sptl::StageCall call;
     std::string why;
     if (int rc = sptl::stager_begin(ctx->stager, pieces, 1, &call, &why))

@@ -57,7 +57,7 @@ _SIGS = {
     "reduce_norm_agmm_chunked": ([_vp, _int, _ptrs, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i64, _int, _int,
                                   _int, _ptrs, _vp, _vp, _vp, _int, _vp], _int),
     "gemm_partial": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp], _int),
-    "gemm_rs_chunked": ([_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _ptrs, _vp], _int),
+    "gemm_rs_chunked": ([_vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _ptrs, _vp], _int),
     "dtp_affinity_layout": ([ctypes.POINTER(ctypes.c_double), _int, _int, _int, _int, ctypes.POINTER(_int),
                              ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)], _int),
     "dtp_colocated_affinity": ([ctypes.POINTER(ctypes.c_double), _int, _int, _int, ctypes.POINTER(_int),
@@ -173,8 +173,9 @@ def raw_agmm_backward(ctx, seq_len, hidden, n_local, tp, rank, shard_src, x_gath
                               dw, dw_dtype, compute)
 
 
-def raw_gemm_rs_chunked(ctx, seq_len, k_local, hidden, tp, rank, a, w, partial, dst, compute) -> int:
-    return _lib.gemm_rs_chunked(ctx, seq_len, k_local, hidden, tp, rank, a, w, partial, _ptr_array(dst), compute)
+def raw_gemm_rs_chunked(ctx, seq_len, k_local, hidden, tp, n_chunks, rank, a, w, partial, dst, compute) -> int:
+    return _lib.gemm_rs_chunked(ctx, seq_len, k_local, hidden, tp, n_chunks, rank, a, w, partial, _ptr_array(dst),
+                                compute)
 
 
 def raw_reduce_norm_agmm_chunked(ctx, n_partials, partials, residual, gamma, eps, residual_out, seq_len, hidden,
@@ -352,9 +353,11 @@ def agmm_backward(shards, x_gathered, w, dy, dx, dw, *, rank: int = 0, compute=N
                              _out_dtype(dw), _stream(compute)))
 
 
-def gemm_rs_chunked(a, w, partial, dst, *, rank: int = 0, stream=None, ctx: Optional[Context] = None) -> None:
-    """partial = a @ w, slice by slice in send order, each peer slice q copied to dst[q] by the copy
-    engines while later slices compute (dst[rank] is ignored; see include/sptl.h)."""
+def gemm_rs_chunked(a, w, partial, dst, *, rank: int = 0, n_chunks: Optional[int] = None, stream=None,
+                    ctx: Optional[Context] = None) -> None:
+    """partial = a @ w, sub-slice by sub-slice in send order, each peer sub-slice copied into dst[q]
+    by the copy engines while later ones compute (n_chunks sub-slices in all, default one per
+    slice; dst[rank] is ignored; see include/sptl.h)."""
     torch = _torch()
     M, K = a.shape
     H = w.shape[1]
@@ -362,7 +365,7 @@ def gemm_rs_chunked(a, w, partial, dst, *, rank: int = 0, stream=None, ctx: Opti
     rows = M // tp if tp else 0
     d = [None if (q == rank or t is None) else _dev_ptr(t, torch.bfloat16, f"dst[{q}]", (rows, H))
          for q, t in enumerate(dst)]
-    _check(raw_gemm_rs_chunked(_h(ctx), M, K, H, tp, rank, _dev_ptr(a, torch.bfloat16, "a"),
+    _check(raw_gemm_rs_chunked(_h(ctx), M, K, H, tp, n_chunks or tp, rank, _dev_ptr(a, torch.bfloat16, "a"),
                                _dev_ptr(w, torch.bfloat16, "w", (K, H)),
                                _dev_ptr(partial, torch.bfloat16, "partial", (M, H)), d, _stream(stream)))
 

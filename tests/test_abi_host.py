@@ -165,10 +165,11 @@ def test_boundary_validation(sptl, kw, status):
     (dict(a=None), 1), (dict(w=None), 1), (dict(partial=None), 1), (dict(dst=None), 1),
     (dict(dst=[None, None]), 1), (dict(tp=0), 6), (dict(tp=65), 6), (dict(rank=2), 6), (dict(seq_len=-2), 2),
     (dict(seq_len=513), 3), (dict(hidden=12), 3), (dict(partial=A + 4), 4), (dict(dst=[None, A + 8]), 4),
+    (dict(n_chunks=0), 6), (dict(n_chunks=65), 6), (dict(n_chunks=3), 3), (dict(n_chunks=6), 3),
 ])
 def test_gemm_rs_validation(sptl, kw, status):
-    d = dict(ctx=None, seq_len=512, k_local=256, hidden=256, tp=2, rank=0, a=A, w=A, partial=A, dst=[None, A],
-             compute=None)
+    d = dict(ctx=None, seq_len=512, k_local=256, hidden=256, tp=2, n_chunks=2, rank=0, a=A, w=A, partial=A,
+             dst=[None, A], compute=None)
     d.update(kw)
     assert sptl.raw_gemm_rs_chunked(**d) == status, sptl.last_error()
 

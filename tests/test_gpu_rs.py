@@ -38,7 +38,7 @@ def gen(seed, key, rows, cols, var=1.0):
     return synth.normal_bf16(seed, key, rows, cols, float(np.sqrt(var)))
 
 
-def run_rs(env, M, K, H, tp, rank, seed, oracle=True, in_place=()):
+def run_rs(env, M, K, H, tp, rank, seed, oracle=True, in_place=(), n_chunks=None):
     torch, sptl, ctx = env
     a_b = gen(seed, (3,), M, K)
     w_b = gen(seed, (2,), K, H, 1.0 / K)
@@ -48,7 +48,7 @@ def run_rs(env, M, K, H, tp, rank, seed, oracle=True, in_place=()):
     dst = [None if q == rank else (partial[q * R:(q + 1) * R] if q in in_place else
                                    torch.full((R, H), float("nan"), dtype=torch.bfloat16, device="cuda"))
            for q in range(tp)]
-    sptl.gemm_rs_chunked(a, w, partial, dst, rank=rank, ctx=ctx)
+    sptl.gemm_rs_chunked(a, w, partial, dst, rank=rank, n_chunks=n_chunks, ctx=ctx)
     ref = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
     sptl.gemm_partial(a, w, ref, ctx=ctx)
     return a_b, w_b, partial, dst, ref
@@ -81,6 +81,26 @@ def test_rs_matches_gemm_partial_and_oracle(env, M, K, H, tp, rank, in_place):
     print(f"gemm_rs_chunked M={M} K={K} H={H} tp={tp} rank={rank} in_place={in_place}", flush=True)
     a_b, w_b, partial, dst, ref = run_rs(env, M, K, H, tp, rank, 400 + M % 97, in_place=in_place)
     check(env, a_b, w_b, partial, dst, ref, tp, rank)
+
+
+@pytest.mark.parametrize("M,K,H,tp,rank,n_chunks,order,in_place", [
+    (8192, 4096, 4096, 8, 3, 32, "interleaved", ()),   # four 256-row sub-slices per slice
+    (8192, 4096, 4096, 8, 3, 32, "ring", ()),
+    (2048, 768, 1024, 4, 1, 8, "interleaved", ()),       # short K, two sub-slices per slice
+    (2048, 512, 512, 4, 2, 16, "interleaved", (0,)),     # 128-row sub-slices; one slice left in place
+    (1024, 256, 512, 4, 2, 16, "interleaved", ()),       # 64-row sub-slices fit no chunk tile: event path
+])
+def test_rs_sub_slices(env, M, K, H, tp, rank, n_chunks, order, in_place):
+    """Sub-slices in either send order give gemm_partial's bits, every destination whole."""
+    torch, sptl, ctx = env
+    print(f"gemm_rs_chunked M={M} K={K} H={H} tp={tp} rank={rank} n_chunks={n_chunks} {order}", flush=True)
+    ctx.set_staging(order, 0)
+    try:
+        a_b, w_b, partial, dst, ref = run_rs(env, M, K, H, tp, rank, 450 + n_chunks, in_place=in_place,
+                                             n_chunks=n_chunks)
+        check(env, a_b, w_b, partial, dst, ref, tp, rank, oracle=M <= 2048)
+    finally:
+        ctx.set_staging("ring", 0)
 
 
 def test_rs_back_to_back(env):

@@ -125,3 +125,50 @@ def test_interleaved_event_path_and_timeline(env):
     finally:
         alt.set_copy_mode("staged")
         alt.set_staging("ring", 0)
+
+
+def test_links_reduce_scatter_and_backward_bitwise(env):
+    """The link model on the reduce-scatter mirror (each peer slice pushed on its peer's engines)
+    and on the backward's re-gather gives the default context's bits."""
+    torch, sptl, ref, alt = env
+    tp, M, K, H, rank = 4, 2048, 512, 512, 2
+    a = to_dev(synth.normal_bf16(991, (0,), M, K, 1.0))
+    w = to_dev(synth.normal_bf16(991, (1,), K, H, float(np.sqrt(1.0 / K))))
+    R = M // tp
+
+    def rs(ctx):
+        part = torch.full((M, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dst = [None if q == rank else torch.full((R, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+               for q in range(tp)]
+        sptl.gemm_rs_chunked(a, w, part, dst, rank=rank, ctx=ctx)
+        torch.cuda.synchronize()
+        ctx.check()
+        return [to_bits(part)] + [to_bits(d) for d in dst if d is not None]
+
+    tpb, rows, Kb, N, rb = 4, 256, 512, 384, 1
+    shards = [to_dev(synth.normal_bf16(992, (0, q), rows, Kb, 1.0)) for q in range(tpb)]
+    wb = to_dev(synth.normal_bf16(992, (1,), Kb, N, float(np.sqrt(1.0 / Kb))))
+    dy = to_dev(synth.normal_bf16(992, (2,), tpb * rows, N, float(np.sqrt(1.0 / N))))
+
+    def bwd(ctx):
+        xg = torch.full((tpb * rows, Kb), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dx = torch.full((tpb * rows, Kb), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dw = torch.full((Kb, N), float("nan"), dtype=torch.float32, device="cuda")
+        sptl.agmm_backward(shards, xg, wb, dy, dx, dw, rank=rb, ctx=ctx)
+        torch.cuda.synchronize()
+        ctx.check()
+        return [to_bits(xg), to_bits(dx), to_bits(dw)]
+
+    want_rs, want_bwd = rs(ref), bwd(ref)
+    for q in range(tp):
+        if q != rank:  # each pushed slice is the partial's rows of that peer
+            assert np.array_equal(want_rs[1 + q - (q > rank)], want_rs[0][q * R:(q + 1) * R])
+    try:
+        for per in (2, 1, 16):
+            alt.set_staging("ring", per)
+            for i, (g, w_) in enumerate(zip(rs(alt), want_rs)):
+                assert np.array_equal(g, w_), f"reduce-scatter output {i}, {per} engines per peer"
+            for i, (g, w_) in enumerate(zip(bwd(alt), want_bwd)):
+                assert np.array_equal(g, w_), f"backward output {i}, {per} engines per peer"
+    finally:
+        alt.set_staging("ring", 0)
