@@ -15,6 +15,10 @@
 //     streams a small piece at about half its rate); copies large enough for that on their own
 //     are striped over all engines one after another (piece p on engine p), at most
 //     kMaxPieces pieces and no piece below kMinPiece / split bytes;
+//   * the trailing copies that no tile waits for (this rank's own slot, which only the end of
+//     the call waits for) join the peers' last group only when they add at most a quarter of
+//     its bytes; otherwise they come last, striped over the engines in pieces of at least
+//     kGroupPiece bytes, so they do not hold back chunks that tiles wait for;
 //   * pieces are equal and rounded up to 256 bytes; the last piece of a copy takes the rest.
 // Each engine takes its pieces in the order returned.
 //
@@ -56,10 +60,6 @@ inline int later_group(int engines, size_t chunk_bytes) {
     return g < 1 ? 1 : g > (size_t)engines ? engines : (int)g;
 }
 
-// `split` (>= 1) allows up to split pieces per engine and copy; `engines` >= 1.  `group` (>= 1)
-// splits the later copies together in successive groups of `group` copies, like the leading
-// group (1: each later copy striped over all engines on its own); a last group shorter than
-// `group` is merged into the one before when both fit on the engines.
 // Appends copy i cut into equal pieces rounded to 256 bytes (the last takes the remainder, so
 // at most n pieces), on engines first, first + 1, ... (mod engines).
 inline void cut_copy(std::vector<PlanPiece> &out, const std::vector<PlanCopy> &copies, int i, size_t n, int first,
@@ -76,8 +76,14 @@ inline void cut_copy(std::vector<PlanPiece> &out, const std::vector<PlanCopy> &c
     }
 }
 
+// `split` (>= 1) allows up to split pieces per engine and copy; `engines` >= 1.  `group` (>= 1)
+// splits the later copies together in successive groups of `group` copies, like the leading
+// group (1: each later copy striped over all engines on its own); a last group shorter than
+// `group` is merged into the one before when both fit on the engines.  The last `trailing`
+// copies join the last group when they add at most a quarter of its bytes and all fit on the
+// engines; otherwise they are striped one after another, in pieces of at least kGroupPiece bytes.
 inline std::vector<PlanPiece> plan_pieces(const std::vector<PlanCopy> &copies, int lead, int engines, size_t split,
-                                          int group = 1) {
+                                          int group = 1, int trailing = 0) {
     std::vector<PlanPiece> out;
     size_t E = (size_t)engines * split;
     if (E > (size_t)kMaxPieces) E = kMaxPieces;
@@ -101,19 +107,35 @@ inline std::vector<PlanPiece> plan_pieces(const std::vector<PlanCopy> &copies, i
             first += (int)n;
         }
     };
-    const int count = (int)copies.size();
+    const int total = (int)copies.size();
+    if (trailing < 0) trailing = 0;
+    if (trailing > total) trailing = total;
+    const int count = total - trailing;  // the copies that tiles wait for
     if (lead > count) lead = count;
     if (lead > engines) lead = engines;
     if (lead < 1) lead = 1;
     if (group > engines) group = engines;
     if (group < 1) group = 1;
     if (lead > 1) joint(0, lead);
+    auto bytes_of = [&](int b, int e) {
+        size_t n = 0;
+        for (int i = b; i < e; ++i) n += copies[(size_t)i].bytes;
+        return n;
+    };
+    bool merged = false;  // the trailing copies went into the last group
     for (int i = lead > 1 ? lead : 0; i < count;) {
         if (group > 1) {
             int e = i + group < count ? i + group : count;
             // a short last group joins this one when they fit on the engines together, so no
             // copy is left to run alone at the end
             if (e < count && count - e < group && count - i <= engines) e = count;
+            // the trailing copies join the last group when they add at most a quarter of its bytes
+            // (its chunks then land at most a quarter later, and no copy runs on alone while the
+            // tiles of the next chunks compute)
+            if (e == count && trailing && total - i <= engines && 4 * bytes_of(count, total) <= bytes_of(i, e)) {
+                e = total;
+                merged = true;
+            }
             joint(i, e);
             i = e;
         } else {
@@ -122,6 +144,11 @@ inline std::vector<PlanPiece> plan_pieces(const std::vector<PlanCopy> &copies, i
             cut(i, n, 0);
             ++i;
         }
+    }
+    for (int i = merged ? total : count; i < total; ++i) {  // pieces of at least kGroupPiece
+        size_t n = copies[(size_t)i].bytes / kGroupPiece;
+        n = n < 1 ? 1 : n > E ? E : n;
+        cut(i, n, 0);
     }
     return out;
 }

@@ -30,6 +30,7 @@
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <chrono>
 #include <condition_variable>
 #include <deque>
@@ -481,8 +482,16 @@ std::vector<CopyPiece> stager_plan(const SdmaStager *s, const std::vector<CopyPi
     const int group = group_in > 0     ? group_in
                       : forced_group ? forced_group
                                      : later_group(engines, copies.empty() ? 0 : copies[0].bytes);
+    // the own slot's copies (kJoinChunk), which only the end of the call waits for, come last on
+    // their own; SPTL_SDMA_JOIN_GROUPED=1 groups them with the peers' chunks (measurement aid)
+    static const bool join_grouped = [] {
+        const char *e = getenv("SPTL_SDMA_JOIN_GROUPED");
+        return e && !strcmp(e, "1");
+    }();
+    int trailing = 0;
+    for (size_t i = copies.size(); !join_grouped && i > 0 && copies[i - 1].chunk == kJoinChunk; --i) ++trailing;
     std::vector<CopyPiece> out;
-    for (const PlanPiece &q : plan_pieces(pc, lead, engines, split, group)) {
+    for (const PlanPiece &q : plan_pieces(pc, lead, engines, split, group, trailing)) {
         const CopyPiece &c = copies[(size_t)q.copy];
         CopyPiece piece{static_cast<char *>(c.dst) + q.offset, static_cast<const char *>(c.src) + q.offset, q.bytes,
                         q.chunk, q.piece};

@@ -193,3 +193,25 @@ def test_link_model(driver, engines, per, sizes, links):
             for b in range(len(links)):
                 if links[a] is not None and links[b] is not None and links[a] != links[b]:
                     assert not {e for *_, e in by_copy[a]} & {e for *_, e in by_copy[b]}
+
+
+def test_trailing_copies_stay_out_of_groups(driver):
+    """The own slot (the trailing copy, which no tile waits for) joins the peers' last group only
+    when it adds at most a quarter of the group's bytes: at 8192 x 4096, tp = 8, peers 4-7 and the
+    own slot are split together (8 MiB next to 32 MiB); with a 12 MiB own slot it follows on its
+    own in 2 MiB pieces; at 32768 x 1024, tp = 4, peers 2 and 3 are split together and the own
+    slot (16 MiB next to 32 MiB) follows them."""
+    def run(sizes, lead):
+        out = subprocess.run([driver, "14", "1", str(lead), "0:1", *map(str, sizes)], check=True,
+                             capture_output=True, text=True, timeout=30).stdout.splitlines()
+        pieces = [tuple(int(v) for v in line.split()) for line in out[1:]]
+        assert [c for c, *_ in pieces] == sorted(c for c, *_ in pieces)
+        return check_cover(pieces, sizes, 1)
+    by_copy = run([8 * MiB] * 8, 3)
+    check_group(by_copy, [3, 4, 5, 6, 7], 14)
+    by_copy = run([8 * MiB] * 7 + [12 * MiB], 3)
+    check_group(by_copy, [3, 4, 5, 6], 14)
+    assert [e for _, _, _, e in by_copy[7]] == [0, 1, 2, 3, 4, 5]
+    by_copy = run([16 * MiB] * 3, 1)
+    check_group(by_copy, [0, 1], 14)
+    assert [e for _, _, _, e in by_copy[2]] == list(range(8))
