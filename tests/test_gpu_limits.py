@@ -5,7 +5,9 @@
 - more chunks than that launch takes, which the per-chunk event path serves;
 - the most chunks a call takes (SPTL_MAX_CHUNKS), one row each;
 - the most copy pieces per chunk (16), forced in a child process by striping each chunk
-  more finely than the engine count.
+  more finely than the engine count;
+- the interleaved order and the link model with the most ranks, and the reduce-scatter with the
+  most sub-slices.
 
 Each case checks the gathered rows bit for bit against the concatenated shards and y against
 the float64 oracle (fp32 tolerance: 1e-3 * ||oracle row||_2 / sqrt(N) + 1e-5).
@@ -68,6 +70,49 @@ def test_staged_at_max_tp_and_max_staged_chunks(env):
     # the per-chunk event path gives the same bits
     y2 = run_and_check(env, tp, n_chunks, rows, K, N, rank, seed=41, copy=torch.cuda.Stream())
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
+def test_interleaved_links_at_max_tp(env):
+    """The interleaved order and the link model with the most ranks: 63 peers share the copy
+    engines round-robin (one each), and the bits are the default's."""
+    torch, sptl, ctx = env
+    from sp_transformer_linear_amd.sptl import MAX_TP
+    tp, n_chunks, rows, K, N, rank = MAX_TP, 64, 128, 128, 256, 17
+    y0 = run_and_check(env, tp, n_chunks, rows, K, N, rank, seed=44)
+    ctx.set_staging("interleaved", 1)
+    try:
+        y1 = run_and_check(env, tp, n_chunks, rows, K, N, rank, seed=44)
+    finally:
+        ctx.set_staging("ring", 0)
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+
+
+@pytest.mark.parametrize("tp,n_chunks,order,per", [(64, 64, "ring", 0), (8, 64, "interleaved", 0),
+                                                   (8, 64, "interleaved", 2)])
+def test_reduce_scatter_at_most_sub_slices(env, tp, n_chunks, order, per):
+    """gemm_rs_chunked with the most sub-slices a call takes (64): 128-row sub-slices, the partial
+    equal to gemm_partial bit for bit and every destination to its slice."""
+    torch, sptl, ctx = env
+    M, K, H, rank = 8192, 256, 256, 5
+    a = to_dev(synth.normal_bf16(45, (0,), M, K, 1.0))
+    w = to_dev(synth.normal_bf16(45, (1,), K, H, float(np.sqrt(1.0 / K))))
+    R = M // tp
+    part = torch.full((M, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dst = [None if q == rank else torch.full((R, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+           for q in range(tp)]
+    ref = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ctx.set_staging(order, per)
+    try:
+        sptl.gemm_rs_chunked(a, w, part, dst, rank=rank, n_chunks=n_chunks, ctx=ctx)
+    finally:
+        ctx.set_staging("ring", 0)
+    sptl.gemm_partial(a, w, ref, ctx=ctx)
+    torch.cuda.synchronize()
+    ctx.check()
+    assert torch.equal(part.view(torch.int16), ref.view(torch.int16))
+    for q in range(tp):
+        if q != rank:
+            assert torch.equal(dst[q].view(torch.int16), part[q * R:(q + 1) * R].view(torch.int16)), f"dst[{q}]"
 
 
 def test_more_chunks_than_the_staged_launch_takes(env):
