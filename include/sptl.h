@@ -24,7 +24,7 @@
  *     flags), an SDMA stager (4160 HSA completion signals, about 40 KiB of device counters
  *     and tables, one page of pinned host memory and one worker thread), all created with
  *     the context, and the copy stream of the per-chunk path, created on its first use.
- *     The library also holds one 80 KiB device array per GPU (agmm_chunked_noalloc).
+ *     The library also holds one 67 KiB device array per GPU (agmm_chunked_noalloc).
  *     Inputs must stay valid until the stream work of the call completes.
  *   - Every call is asynchronous (stream-ordered) and returns an sptl_status.  All
  *     arguments are validated BEFORE anything is enqueued: on any non-OK status nothing
