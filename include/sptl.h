@@ -240,9 +240,9 @@ int agmm_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local
  * allocating routine.
  *   ctx      required (not NULL): sptl_create does this call's set-up, once per device (it
  *            resolves the device's scratch array) and once per context (its copy engines).
- *   The chunk-ordered GEMM keeps its state (landed flags, end counters, error word) in a fixed
- *   80 KiB device array, one per GPU, held until the process ends; the end counters are zeroed
- *   by a small kernel on `compute` before each launch (no memset).
+ *   The chunk-ordered GEMM keeps its state (landed flags, end and lead-copy counters, error
+ *   word) in a fixed 67 KiB device array (at most 80 KiB), one per GPU, held until the process
+ *   ends; the counters are zeroed by a small kernel on `compute` before each launch (no memset).
  * Limits: n_chunks <= 64 (the chunks the scratch holds: SPTL_E_SHAPE beyond) and
  * seq_len / n_chunks a multiple of 128 (SPTL_E_UNSUPPORTED otherwise); SPTL_E_UNSUPPORTED also
  * when the context has no working copy engines.  Every call on a GPU shares that GPU's
