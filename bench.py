@@ -688,7 +688,7 @@ def main():
                 ctx_node.check()
                 t_copy = float(np.median(copy_runs))
                 ex = max(0.0, float(np.median(a[:, 0] - a[:, 1])))
-                res[name] = {"n_chunks": n, "order": order, "engines_per_peer": per, "path": ctx_node.info(),
+                res[name] = {"n_chunks": n, "order": order, "engines_per_peer": per,
                              "ms": round(float(np.median(a[:, 0])), 4),
                              "tflops": round(fl / (float(np.median(a[:, 0])) * 1e-3) / 1e12, 2),
                              "exposed_ms": round(ex, 4), "copy_alone_ms": round(t_copy, 4),
