@@ -36,6 +36,10 @@
  *   - Sizes are element counts.  Empty work (seq_len == 0) is valid and enqueues nothing.
  *   - A context serves one host thread at a time; different contexts (and the default
  *     contexts of different devices) may be used from different threads concurrently.
+ *   - Calls on one context may be issued on different compute streams and run at the same time
+ *     on the GPU: each staged call has a signal set of its own (4 per context), and the per-chunk
+ *     paths share the context's copy stream.  Timed calls (timing != 0) and
+ *     agmm_chunked_noalloc are the exceptions: their GPU work must not overlap another call's.
  */
 #ifndef SPTL_H
 #define SPTL_H
