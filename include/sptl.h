@@ -38,8 +38,9 @@
  *     contexts of different devices) may be used from different threads concurrently.
  *   - Calls on one context may be issued on different compute streams and run at the same time
  *     on the GPU: each staged call has a signal set of its own (4 per context), and the per-chunk
- *     paths share the context's copy stream.  Timed calls (timing != 0) and
- *     agmm_chunked_noalloc are the exceptions: their GPU work must not overlap another call's.
+ *     paths share the context's copy stream.  The exceptions: two timed calls (timing != 0) on
+ *     one context must not overlap (they share its timestamps), nor may two agmm_chunked_noalloc
+ *     calls on one GPU (they share its scratch array).
  */
 #ifndef SPTL_H
 #define SPTL_H
