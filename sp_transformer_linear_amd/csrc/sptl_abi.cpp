@@ -383,8 +383,10 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
     hipError_t he = hipSuccess;
     if (na) he = sptl::launch_fill_u64(na->counts, na->count_words, 0ull, cs);  // a kernel, not a memset
     if (he == hipSuccess && timing) {
+        // first landings and tile starts (minima), last tile ends (maxima), the origin (a minimum)
         he = sptl::launch_fill_u64(ctx->ts_dev, 2 * n, ~0ull, cs);
-        if (he == hipSuccess) he = sptl::launch_fill_u64(ctx->ts_dev + 2 * n, n + 1, 0ull, cs);
+        if (he == hipSuccess) he = sptl::launch_fill_u64(ctx->ts_dev + 2 * n, n, 0ull, cs);
+        if (he == hipSuccess) he = sptl::launch_fill_u64(ctx->ts_dev + 3 * n, 1, ~0ull, cs);
     }
     if (he == hipSuccess) he = hipEventRecord(call.fork, cs);
     if (he == hipSuccess && pre) he = sptl::launch_epilogue(*pre, cs);  // the copies run meanwhile
