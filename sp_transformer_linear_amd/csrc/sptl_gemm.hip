@@ -71,6 +71,10 @@ constexpr int kOutOfRange = 0x7ffffff0;   // an offset past any num_records used
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
+// The ring kernel's chunk swizzle of a 64-byte row form (A, or an n-major B): 16-byte chunk c of
+// row r sits at chunk c ^ ring_aswz(r).  Both the direct-to-LDS loads and the fragment reads use it.
+__device__ __forceinline__ int ring_aswz(int r) { return (r >> 1) & 3; }
+
 constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);  // s_waitcnt vmcnt(0); expcnt, lgkmcnt not waited
 
 // Release fences whose L2 write-back (buffer_wbl2) has completed before the caller's next memory
@@ -330,7 +334,11 @@ __device__ __forceinline__ void tile_wait(const GemmProblem &p, const TileOrigin
     if constexpr (CHUNKED) {
         const ChunkPlan &plan = p.plan;
         const int tid = threadIdx.x;
-        if (plan.ts && bid == 0 && tid == 0) plan.ts[3 * plan.n_chunks] = wall_clock64();
+        // the timeline's origin: the earliest tile start of the launch (every tile takes part, so
+        // no landing can be seen before it)
+        if (plan.ts && tid == 0)
+            atomicMin(reinterpret_cast<unsigned long long *>(plan.ts + 3 * plan.n_chunks),
+                      (unsigned long long)wall_clock64());
         const bool cu = (plan.cu_mask >> o.chunk) & 1;
         if (cu) cu_copy_and_wait(plan, bid);  // the chunk is copied by the launch's own workgroups
         if (tid < 64) {
@@ -884,8 +892,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // those stages read zeros and the next tile waits and loads as the first one does.
 //
 // The per-lane global addresses apply the LDS swizzles in reverse:
-//   A slot: 256 rows of 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
-//           (a ds_read_b128 by 16 lanes then covers all 16 bank groups once);
+//   A slot: 256 rows of 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 1) & 3): a fragment
+//           read (16 rows x 4 chunks per ds_read_b128) then runs without bank conflicts, 4 LDS
+//           cycles per instruction (measured by SQ_LDS_BANK_CONFLICT; c ^ ((r >> 2) & 3) and
+//           the other row-bit swizzles took 8, half of them conflict stalls);
 //   B slot: 32 rows (k) of 512 bytes; 32-byte unit u of row k at u ^ ((k & 3) << 1 | (k >> 3) & 1)
 //           (the transposing reads of a fragment take rows 8 g .. 8 g + 3 in lane group g; bit 3
 //           of k keeps groups 0 and 1, which the LDS serves together, on different banks).
@@ -932,7 +942,7 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     for (int t = 0; t < NBLK; ++t) {
         const int blk = wave * NBLK + t;
         const int row = blk * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        const int c = (lane & 3) ^ ring_aswz(row);
         r_kc[t] = c * 8;
         a_off[t] = (int)((row * p.lda + c * 8) * 2);
         if constexpr (B_NM) b_off[t] = (int)((row * p.ldb + c * 8) * 2);
@@ -1011,7 +1021,7 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     const int b_sw = ((b_k0 & 3) << 1) | ((b_k0 >> 3) & 1);
     auto row_addr = [&](int half, int x0) {
         const int r = x0 + (lane & 15);
-        return half + r * (kDmaBK * 2) + (((lane >> 4) ^ ((r >> 2) & 3)) << 4);
+        return half + r * (kDmaBK * 2) + (((lane >> 4) ^ ring_aswz(r)) << 4);
     };
     auto kmajor_addr = [&](int half, int x0) {
         const int x = x0 + 4 * (rr & 3);
