@@ -75,6 +75,27 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 // row r sits at chunk c ^ ring_aswz(r).  Both the direct-to-LDS loads and the fragment reads use it.
 __device__ __forceinline__ int ring_aswz(int r) { return (r >> 1) & 3; }
 
+// The ring kernel's swizzle of a k-major stage (32 rows of 512 bytes): 16-byte piece h of row k
+// sits at piece h ^ ring_kswz(k, is_b).  Bits 2-3 take k & 3 and one more bit takes bit 3 of k:
+// bit 0 for B (whose fragment reads follow ring_bcol), bit 1 for a k-major A (plain column order).
+// Either way the transposing fragment reads of the two lane groups that the LDS serves together
+// (rows 8 g .. 8 g + 3, g = 0, 1) fall on different banks: no conflict cycles in a read probe
+// (SQ_LDS_BANK_CONFLICT), where the permuted B reads with A's form took 2 per instruction.
+__device__ __forceinline__ int ring_kswz(int k, bool is_b) {
+    return ((k & 3) << 2) | (((k >> 3) & 1) << (is_b ? 0 : 1));
+}
+
+// The ring kernel's B column order.  Block j (16 columns) of a wave's 16 x 16 blocks carries, in
+// its MFMA column c, the wave's output column ring_bcol(j, c).  Columns come in runs of 4 (the
+// transposing read gives each group of 4 result lanes 4 consecutive columns), and lane group
+// g = c / 4 of blocks 2 s and 2 s + 1 together holds the 8 consecutive columns 32 s + 8 g .. + 7,
+// which the tile store writes as one 16-byte vector per lane.  Which block of the pair holds the
+// first 4 alternates with g, so that a fragment read uses both halves of every 16-byte piece.
+__device__ __forceinline__ int ring_bcol(int j, int c) {
+    const int g = c >> 2;
+    return 32 * (j >> 1) + 8 * g + 4 * ((j + g) & 1) + (c & 3);
+}
+
 constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);  // s_waitcnt vmcnt(0); expcnt, lgkmcnt not waited
 
 // Release fences whose L2 write-back (buffer_wbl2) has completed before the caller's next memory
@@ -502,52 +523,48 @@ __device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrig
     }
 }
 
-// Stores the accumulators of a tile computed with v_mfma_f32_16x16x32_bf16, then as tile_end.
-// 16 x 16 result layout: lane l holds column l % 16, register e holds row 4 (l / 16) + e.
+// Stores the accumulators of a ring-kernel tile, then as tile_end.  The ring kernel computes each
+// 16 x 16 block transposed (B's fragment is the MFMA's first operand: the same products, summed
+// over the same k, so the same bits), and in the 16 x 16 result layout lane l then holds output
+// row 16 i + l % 16 of block row i, register e of block j its column ring_bcol(j, 4 (l / 16) + e).
+// So lane group g = l / 16 holds, over blocks 2 s and 2 s + 1, the 8 consecutive columns
+// 32 s + 8 g .. + 7 of its row: one 16-byte store per lane (two for fp32) writes 64 contiguous
+// bytes of each of 16 rows, a quarter of the store instructions of one 4-byte store per
+// adjacent pair of columns.  Block 2 s + (g & 1) holds the first 4 of them.
 template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED>
 __device__ __forceinline__ void tile_end16(const GemmProblem &p, const TileOrigin &o,
                                            const f32x4_t (&acc)[BM / WGM / 16][BN / WGN / 16], int bid) {
     constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
+    static_assert(TN % 2 == 0, "column pairs of blocks");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm0 = (wave / WGN) * (BM / WGM), wn0 = (wave % WGN) * (BN / WGN);
-    const int64_t m0 = o.m0, n0 = o.n0;
-    if constexpr (OUT_F32) {
+    const int g = lane >> 4;
+    const bool second = g & 1;  // the pair's second block holds the first 4 columns
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
+        const int64_t row = o.m0 + wm0 + i * 16 + (lane & 15);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int64_t col = n0 + wn0 + j * 16 + (lane & 15);
-                if (col >= p.n) continue;
+        for (int s = 0; s < TN / 2; ++s) {
+            const int64_t col = o.n0 + wn0 + 32 * s + 8 * g;  // N is a multiple of 8: all 8 or none
+            f32x4_t lo, hi;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t row = m0 + wm0 + i * 16 + (lane >> 4) * 4 + e;
-                    if (row < p.m) static_cast<float *>(p.c)[row * p.ldc + col] = acc[i][j][e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                lo[e] = second ? acc[i][2 * s + 1][e] : acc[i][2 * s][e];
+                hi[e] = second ? acc[i][2 * s][e] : acc[i][2 * s + 1][e];
             }
-        }
-    } else {
-        // bf16: lanes 2 q and 2 q + 1 hold adjacent columns; one DPP swap per pair of values
-        // gives the even lane both columns of rows e = 0, 1 and the odd lane both columns of
-        // rows e = 2, 3, so every store writes two columns (4 bytes; N is a multiple of 8).
-        const bool odd = lane & 1;
+            if (row < p.m && col < p.n) {
+                if constexpr (OUT_F32) {
+                    float *c = static_cast<float *>(p.c) + row * p.ldc + col;
+                    *reinterpret_cast<f32x4_t *>(c) = lo;
+                    *reinterpret_cast<f32x4_t *>(c + 4) = hi;
+                } else {
+                    bf16x8_t v;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int64_t col = n0 + wn0 + j * 16 + (lane & 15 & ~1);
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const float send = odd ? acc[i][j][k] : acc[i][j][k + 2];
-                    const float recv = __builtin_bit_cast(
-                        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
-                    const float mine = odd ? acc[i][j][k + 2] : acc[i][j][k];
-                    const int e = odd ? k + 2 : k;
-                    const int64_t row = m0 + wm0 + i * 16 + (lane >> 4) * 4 + e;
-                    bf16x2_t v;
-                    v[0] = (__bf16)(odd ? recv : mine);
-                    v[1] = (__bf16)(odd ? mine : recv);
-                    if (row < p.m && col < p.n)
-                        *reinterpret_cast<bf16x2_t *>(static_cast<uint16_t *>(p.c) + row * p.ldc + col) = v;
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] = (__bf16)lo[e];
+                        v[4 + e] = (__bf16)hi[e];
+                    }
+                    *reinterpret_cast<bf16x8_t *>(static_cast<uint16_t *>(p.c) + row * p.ldc + col) = v;
                 }
             }
         }
@@ -871,7 +888,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // sums are those of two v_mfma_f32_32x32x16_bf16 steps over the same 32 k (bit-identical
 // results, checked against every other configuration), and it moves less accumulator data per
 // flop, which at the chip's power limit lets the clock run higher (about 10 % more GEMM
-// throughput with random operands).
+// throughput with random operands).  Each block is computed transposed, B's fragment as the
+// first operand, and B's columns are taken in the order ring_bcol: a lane then ends the tile
+// holding runs of 8 consecutive output columns of one row, which it stores as 16-byte vectors
+// (tile_end16).
 //
 // Four waves (WGM = WGN = 2): each wave owns 128 x 128 (8 x 8 blocks), so a stage's fragment
 // reads are a third fewer bytes per MFMA than with eight waves of 64 x 128.  Its 256
@@ -896,9 +916,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 //           read (16 rows x 4 chunks per ds_read_b128) then runs without bank conflicts, 4 LDS
 //           cycles per instruction (measured by SQ_LDS_BANK_CONFLICT; c ^ ((r >> 2) & 3) and
 //           the other row-bit swizzles took 8, half of them conflict stalls);
-//   B slot: 32 rows (k) of 512 bytes; 32-byte unit u of row k at u ^ ((k & 3) << 1 | (k >> 3) & 1)
-//           (the transposing reads of a fragment take rows 8 g .. 8 g + 3 in lane group g; bit 3
-//           of k keeps groups 0 and 1, which the LDS serves together, on different banks).
+//   B slot: 32 rows (k) of 512 bytes; 16-byte piece h of row k at h ^ ring_kswz(k) (the
+//           transposing reads of a fragment take rows 8 g .. 8 g + 3 in lane group g; bit 3 of k
+//           keeps groups 0 and 1, which the LDS serves together, on different banks).
 // Same K order as every other configuration.
 //
 // Operand layouts (LAYOUT, GemmProblem::layout): kLayoutRowMajor as above; kLayoutAKMajor, A
@@ -953,27 +973,27 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         __attribute__((always_inline)) {
         load_to_lds(r, l + t * 1024, (k_tail && k0 + r_kc[t] >= p.k) ? kOutOfRange : off[t]);
     };
-    // Load t of a stage's k-major blocks: k-rows 2 blk, 2 blk + 1 (lane / 32); lanes q, q + 1
-    // read the two halves of the swizzled 32-byte unit (q / 2) of that row (recomputed here
-    // rather than kept in registers across the tiles).  x0: the tile's first column (of B, or
-    // with A_KM the tile's first row of the output), x_end: the operand's column count, ld: its
-    // row stride.
-    auto load_kmajor = [&](const u32x4_t &r, uint32_t l, int t, int64_t x0, int64_t x_end, int64_t ld)
+    // Load t of a stage's k-major blocks: k-rows 2 blk, 2 blk + 1 (lane / 32); lane q writes
+    // 16-byte piece q of that row, which holds piece q ^ ring_kswz(k) of the operand's row
+    // (recomputed here rather than kept in registers across the tiles).  x0: the tile's first
+    // column (of B, or with A_KM the tile's first row of the output), x_end: the operand's column
+    // count, ld: its row stride.
+    auto load_kmajor = [&](const u32x4_t &r, uint32_t l, int t, int64_t x0, int64_t x_end, int64_t ld, bool is_b)
         __attribute__((always_inline)) {
         const int krow = (wave * NBLK + t) * 2 + (lane >> 5);
         const int q = lane & 31;
-        const int64_t x = x0 + (((q >> 1) ^ (((krow & 3) << 1) | ((krow >> 3) & 1))) * 16 + (q & 1) * 8);
+        const int64_t x = x0 + 8 * (q ^ ring_kswz(krow, is_b));
         load_to_lds(r, l + t * 1024, x < x_end ? (int)((krow * ld + x) * 2) : kOutOfRange);
     };
     auto load_a = [&](const u32x4_t &ar, uint32_t la, int t, bool k_tail, int64_t k0, const TileOrigin &o)
         __attribute__((always_inline)) {
-        if constexpr (A_KM) load_kmajor(ar, la, t, o.m0, p.m, p.lda);
+        if constexpr (A_KM) load_kmajor(ar, la, t, o.m0, p.m, p.lda, false);
         else load_rows(ar, la, t, k_tail, k0, a_off);
     };
     auto load_b = [&](const u32x4_t &br, uint32_t lb, int t, bool k_tail, int64_t k0, const TileOrigin &o)
         __attribute__((always_inline)) {
         if constexpr (B_NM) load_rows(br, lb, t, k_tail, k0, b_off);
-        else load_kmajor(br, lb, t, o.n0, p.n, p.ldb);
+        else load_kmajor(br, lb, t, o.n0, p.n, p.ldb, true);
     };
     // Buffer ranges of stage k0 (k_rows of its 32 k exist; 0 for an empty stage).  Row form:
     // from the tile's first row at k0 to the end of its last valid row (rows and k past the end
@@ -1010,29 +1030,28 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 
     // Fragment read addresses within a slot.  A block i (16 rows): lane l reads row
     // wm0 + 16 i + l % 16, k 8 (l / 16) .. + 7 (one ds_read_b128).  B block j (16 columns): lane
-    // l holds column wn0 + 16 j + l % 16, k 8 (l / 16) .. + 7, from two transposing reads; per 16
-    // lanes source lane s supplies row kb + s / 4 at columns nb + 4 (s % 4) and result lane i
-    // gets B[kb .. kb + 3][nb + i], with kb = 8 (l / 16) and 8 (l / 16) + 4.
-    // Row form, block x of the slot half at `half`: lane l reads row x0 + l % 16 (x0 = the
-    // block's first row) at k 8 (l / 16) .. + 7.  k-major form: lane l holds column x0 + l % 16
-    // from two transposing reads.
+    // l holds column wn0 + ring_bcol(j, l % 16), k 8 (l / 16) .. + 7, from two transposing reads;
+    // per 16 lanes source lane s supplies row kb + s / 4 at columns x + 0 .. 3, x = the column of
+    // result lanes 4 (s % 4) .. + 3, and result lane i gets B[kb .. kb + 3][x + i % 4], with
+    // kb = 8 (l / 16) and 8 (l / 16) + 4.
+    // Row form, at `half`: lane l reads row r (its block's row or column for lane l % 16) at
+    // k 8 (l / 16) .. + 7.  k-major form: source lane group s % 4 points at column x.
     const int rr = lane & 15;
     const int b_k0 = 8 * (lane >> 4) + (rr >> 2);
-    const int b_sw = ((b_k0 & 3) << 1) | ((b_k0 >> 3) & 1);
-    auto row_addr = [&](int half, int x0) {
-        const int r = x0 + (lane & 15);
+    auto row_addr = [&](int half, int r) {
         return half + r * (kDmaBK * 2) + (((lane >> 4) ^ ring_aswz(r)) << 4);
     };
-    auto kmajor_addr = [&](int half, int x0) {
-        const int x = x0 + 4 * (rr & 3);
-        return half + b_k0 * B_ROW + (((x >> 4) ^ b_sw) << 5) + (x & 15) * 2;
+    auto kmajor_addr = [&](int half, int x, bool is_b) {
+        return half + b_k0 * B_ROW + (((x >> 3) ^ ring_kswz(b_k0, is_b)) << 4) + (x & 7) * 2;
     };
     int a_addr[TM], b_addr[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a_addr[i] = A_KM ? kmajor_addr(0, wm0 + i * 16) : row_addr(0, wm0 + i * 16);
+    for (int i = 0; i < TM; ++i)
+        a_addr[i] = A_KM ? kmajor_addr(0, wm0 + i * 16 + 4 * (rr & 3), false) : row_addr(0, wm0 + i * 16 + rr);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-        b_addr[j] = B_NM ? row_addr(kDmaSlotBytes, wn0 + j * 16) : kmajor_addr(kDmaSlotBytes, wn0 + j * 16);
+        b_addr[j] = B_NM ? row_addr(kDmaSlotBytes, wn0 + ring_bcol(j, rr))
+                         : kmajor_addr(kDmaSlotBytes, wn0 + ring_bcol(j, 4 * (rr & 3)), true);
     auto read_rows = [&](const char *at) __attribute__((always_inline)) {
         return *reinterpret_cast<const bf16x8_t *>(at);
     };
@@ -1067,7 +1086,7 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     };
     // Order within a stage: the next stage's A fragment reads after the first TM MFMAs, its B
     // fragment j's two reads after the last MFMA of column block j, and the stage's global loads
@@ -1142,7 +1161,7 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
                 for (int i = 0; i < TM; ++i)
                     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
                                  : "+a"(acc[i][j])
-                                 : "v"(fa[S0][i]), "v"(fb[S0][j]));
+                                 : "v"(fb[S0][j]), "v"(fa[S0][i]));
                 asm volatile("" ::: "memory");
                 if (j == 0) {
                     wait_vmcnt<2 * NBLK * (SLOTS - 3)>();  // SLOTS - 3 later stages may stay in flight
