@@ -380,8 +380,16 @@ __device__ __forceinline__ void tile_begin(const GemmProblem &p, int tiles_m, in
     tile_wait<CHUNKED>(p, o, blockIdx.x);
 }
 
-template <bool CHUNKED>
-__device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrigin &o, int bid);
+// The end count of workgroup bid (lane 0): its end group's counter value before the count, low 32
+// bits (a call's counts on a set lie within 2^32 below grp_last, so they compare exactly).
+__device__ __forceinline__ uint32_t end_count(const ChunkPlan &plan, int bid) {
+    return (uint32_t)__hip_atomic_fetch_add(plan.wg_count + (bid % kEndGroups) * kEndLine, 1ull, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// EARLY: the workgroup counted itself already (end_count's value grp_v, wave-uniform).
+template <bool CHUNKED, bool EARLY = false>
+__device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrigin &o, int bid, uint32_t grp_v = 0);
 
 // Stores the tile's accumulators (32 x 32 MFMA result layout) and, for a chunk-ordered launch,
 // records the tile's end and completes the call when this is its last tile.
@@ -442,8 +450,8 @@ __device__ __forceinline__ void tile_end(const GemmProblem &p, const TileOrigin 
 
 // Chunk-ordered launches: records the tile's end and completes the call when this is its last
 // tile.
-template <bool CHUNKED>
-__device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrigin &o, int bid) {
+template <bool CHUNKED, bool EARLY>
+__device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrigin &o, int bid, uint32_t grp_v) {
     if (CHUNKED && p.plan.copy_out && p.plan.ready[o.chunk]) {
         // A slice that is copied out (see ChunkPlan): every wave waits until its stores of the
         // tile have reached the L2 (vmcnt 0: the barrier's workgroup-scope fence does not wait
@@ -500,8 +508,8 @@ __device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrig
                 atomicMax(reinterpret_cast<unsigned long long *>(plan.ts + 2 * plan.n_chunks + chunk),
                           (unsigned long long)wall_clock64());
             const int g = bid % kEndGroups;
-            last = __hip_atomic_fetch_add(plan.wg_count + g * kEndLine, 1ull, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) == plan.grp_last[g] &&
+            const uint32_t v = EARLY ? grp_v : end_count(plan, bid);
+            last = v == (uint32_t)plan.grp_last[g] &&
                    __hip_atomic_fetch_add(plan.wg_count + kEndGroups * kEndLine, 1ull, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT) == plan.all_last;
         }
@@ -531,9 +539,10 @@ __device__ __forceinline__ void tile_finish(const GemmProblem &p, const TileOrig
 // 32 s + 8 g .. + 7 of its row: one 16-byte store per lane (two for fp32) writes 64 contiguous
 // bytes of each of 16 rows, a quarter of the store instructions of one 4-byte store per
 // adjacent pair of columns.  Block 2 s + (g & 1) holds the first 4 of them.
-template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED>
+template <int BM, int BN, int WGM, int WGN, bool OUT_F32, bool CHUNKED, bool EARLY = false>
 __device__ __forceinline__ void tile_end16(const GemmProblem &p, const TileOrigin &o,
-                                           const f32x4_t (&acc)[BM / WGM / 16][BN / WGN / 16], int bid) {
+                                           const f32x4_t (&acc)[BM / WGM / 16][BN / WGN / 16], int bid,
+                                           uint32_t grp_v = 0) {
     constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
     static_assert(TN % 2 == 0, "column pairs of blocks");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -569,7 +578,7 @@ __device__ __forceinline__ void tile_end16(const GemmProblem &p, const TileOrigi
             }
         }
     }
-    tile_finish<CHUNKED>(p, o, bid);
+    tile_finish<CHUNKED, EARLY>(p, o, bid, grp_v);
 }
 
 template <int BM, int BN, int WGM, int WGN, int BK>
@@ -1122,6 +1131,17 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #pragma unroll
             for (int st = 0; st < SLOTS - 1; ++st) issue(o, true, st, slot_of(slot0 + st));
         }
+        // The four-wave form reads none of the set's signals or flags after its one chunk wait,
+        // so it counts itself for the call's end here, behind its first stages' loads: the
+        // count's round trip then overlaps their latency (the wait for its value also waits for
+        // stages 1 and 2, issued with stage 0) instead of holding the workgroup, and its CU's
+        // next tile, at the tile's end.
+        uint32_t grp_v = 0;
+        if constexpr (kFour && CHUNKED) {
+            uint32_t v = 0;
+            if (threadIdx.x == 0) v = end_count(p.plan, vb);
+            grp_v = __builtin_amdgcn_readfirstlane(v);
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -1215,7 +1235,7 @@ gemm_ring_kernel(GemmProblem p, int tiles_m, int tiles_n) {
         // the accumulators are read next; the compiler does not know the inline-assembly MFMAs
         // wrote them, so their result latency is waited out here (32 wait states)
         if constexpr (kFour) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-        tile_end16<BM, BN, WGM, WGN, OUT_F32, CHUNKED>(p, o, acc, vb);
+        tile_end16<BM, BN, WGM, WGN, OUT_F32, CHUNKED, kFour && CHUNKED>(p, o, acc, vb, grp_v);
         prefetched = has_next && next_ok;
         slot0 = slot_of(slot0 + nk);
     }
