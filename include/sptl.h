@@ -220,7 +220,8 @@ const char *sptl_ctx_info(sptl_ctx *ctx);
  *     compute unit, each taking its tiles in that order.
  *     The launch ends only after every copy of the call (own slot included) has landed.
  *   - The waiting tiles depend on the context's worker thread: the copies start only once it
- *     has seen the fork event and submitted them.  A worker kept off the CPU for longer than
+ *     has seen the call's fork (the GEMM's start, or an event recorded before it when a tile of
+ *     the first round waits for an engine copy) and submitted them.  A worker kept off the CPU for longer than
  *     the wait bound (sptl_ctx_set_wait_timeout_us) makes the waits time out; the call's
  *     results are then invalid and sptl_ctx_check reports SPTL_E_ASYNC.  Until then the
  *     waiting workgroups hold their compute units.

@@ -388,14 +388,25 @@ int agmm_staged(sptl_ctx *ctx, int64_t seq_len, int64_t hidden, int64_t n_local,
         if (he == hipSuccess) he = sptl::launch_fill_u64(ctx->ts_dev + 2 * n, n, 0ull, cs);
         if (he == hipSuccess) he = sptl::launch_fill_u64(ctx->ts_dev + 3 * n, 1, ~0ull, cs);
     }
-    if (he == hipSuccess) he = hipEventRecord(call.fork, cs);
+    // The copies start once every earlier operation on the stream has completed.  When no tile
+    // of the GEMM's first round waits for an engine copy (the own chunks fill the round, or the
+    // launch's own workgroups copy its peer chunks), they start at the GEMM's start, which its
+    // tile 0 reports: the worker sees that a little later than a fork event, but the event's
+    // marker on the stream costs several microseconds of GPU time before the launch.  Otherwise
+    // (and ahead of an epilogue launched before the GEMM, `pre`, whose run the copies overlap)
+    // at a fork event recorded before the launch.
+    const int first_peers = (int)std::max<int64_t>(0, std::min<int64_t>(first_round - cpr, (int64_t)(n - cpr)));
+    const bool by_start = !pre && cu >= first_peers;
+    plan.started = by_start ? call.started : nullptr;
+    if (he == hipSuccess && !by_start) he = hipEventRecord(call.fork, cs);
     if (he == hipSuccess && pre) he = sptl::launch_epilogue(*pre, cs);  // the copies run meanwhile
     if (he == hipSuccess) he = sptl::launch_gemm(gp, cs);
     if (he != hipSuccess) {
         sptl::stager_cancel(ctx->stager, call);
         return hip_fail(he, "agmm_chunked: kernel launch");
     }
-    if (sptl::stager_submit(ctx->stager, call, std::move(pieces), &why))
+    if (sptl::stager_submit(ctx->stager, call, std::move(pieces), &why, false,
+                            by_start ? sptl::ForkWait::Started : sptl::ForkWait::Event))
         return fail(SPTL_E_HIP, "agmm_chunked: %s", why.c_str());
     if (timing) {
         ctx->t_mode = 1;
@@ -963,8 +974,8 @@ int gemm_rs_chunked(sptl_ctx *ctx, int64_t seq_len, int64_t k_local, int64_t hid
     plan.all_last = call.all_last;
     // the call's slice counters start at zero (a fill kernel rather than a memset; the set's
     // previous call has finished, stager_begin saw to that)
+    // (no fork event: the copies are released slice by slice by the kernel itself)
     hipError_t he = sptl::launch_fill_u64(call.slice_count, (int64_t)n_chunks * sptl::kEndLine, 0ull, cs);
-    if (he == hipSuccess) he = hipEventRecord(call.fork, cs);
     if (he == hipSuccess) he = sptl::launch_gemm(gp, cs);
     if (he != hipSuccess) {
         sptl::stager_cancel(ctx->stager, call);

@@ -355,6 +355,10 @@ __device__ __forceinline__ void tile_wait(const GemmProblem &p, const TileOrigin
     if constexpr (CHUNKED) {
         const ChunkPlan &plan = p.plan;
         const int tid = threadIdx.x;
+        // the launch has started, so every earlier operation on its stream has completed: the
+        // staging worker may start the copies (ForkWait::Started)
+        if (plan.started && bid == 0 && tid == 0)
+            __hip_atomic_store(plan.started, plan.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         // the timeline's origin: the earliest tile start of the launch (every tile takes part, so
         // no landing can be seen before it)
         if (plan.ts && tid == 0)

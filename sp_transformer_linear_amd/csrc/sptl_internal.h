@@ -53,6 +53,7 @@ struct ChunkPlan {
     uint64_t epoch;                          // value the end words take for this launch
     uint64_t *finished;                      // pinned host word: epoch once the launch is done
     uint64_t *timedout;                      // pinned host word: epoch if a wait of the launch timed out
+    uint64_t *started;                       // pinned host word (or null): tile 0 stores epoch at its start
     uint64_t *wg_count;                      // the call's counter block (kCallCountLines lines)
     uint64_t grp_last[kEndGroups];           // group counter value seen by a group's last workgroup
     uint64_t all_last;                       // final counter value seen by the last group

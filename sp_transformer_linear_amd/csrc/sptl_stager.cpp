@@ -8,13 +8,20 @@
 // signals, whose values live in device memory where the chunk-ordered GEMM polls them.
 //
 // Ordering: copies must not overwrite the gathered buffer while earlier work on the compute
-// stream still reads it.  A HIP event recorded at the call's fork point (right before the
-// consuming kernel) is waited for by a worker thread, which then submits the pieces with no
-// HSA dependencies.  The event's completion is signalled by the command processor, so the
-// copies start while the kernel is being dispatched; a store from the kernel itself would
-// queue behind the kernel's own memory traffic.  (A dependency on a signal written by a
-// kernel is resolved by the runtime's host thread with millisecond latency, because a
-// kernel store raises no interrupt.)
+// stream still reads it, nor read sources that work still writes.  A worker thread submits the
+// pieces, with no HSA dependencies, once it has seen the call's fork: either a HIP event
+// recorded on the stream right before the consuming kernel, or that kernel's start, which its
+// tile 0 reports by storing the call's epoch to a pinned host word before anything else (the
+// kernel starts only once every earlier operation on the stream has completed).  The event
+// completes earlier (the command processor signals it while the kernel is being dispatched; the
+// kernel's store queues behind its own loads, about 20 us later), but the marker it adds costs
+// several microseconds of GPU time before the launch.  So the start is used where no tile of the
+// first round waits for an engine copy (M = 8192 with the lead copy: agmm 33-34 against 37-40 us
+// over the pre-staged GEMM), the event where one does, ahead of an epilogue launched between the
+// fork and the GEMM, and under the backward's GEMMs.  A copy-out call's pieces wait for the
+// kernel's slice words, which imply its start.  (A dependency on a signal written by a kernel is
+// resolved by the runtime's host thread with millisecond latency, because a kernel store raises
+// no interrupt: so the worker polls the word itself.)
 //
 // Reuse: completion-signal sets form a ring; a set is re-armed only after the kernel that
 // waited on it has reported its end through a pinned host word.  By then every piece of the
@@ -95,7 +102,11 @@ struct Job {
     hipEvent_t fork;
     std::vector<CopyPiece> pieces;
     const volatile uint64_t *gates = nullptr;  // copy-out: chunk c's pieces wait for gates[16 c] == epoch
+    ForkWait wait = ForkWait::Event;
+    const volatile uint64_t *started = nullptr;  // ForkWait::Started: the kernel stores epoch here
+    bool fork_wait = true;                       // false for a gated call (its slice words imply the kernel ran)
 };
+constexpr double kStartWaitSeconds = 30.0;
 constexpr double kGateWaitSeconds = 10.0;
 
 // Spins (with pauses, yielding now and then) until *word == value; false after `seconds`.
@@ -135,6 +146,7 @@ class SdmaStager {
     uint64_t *slice_counts = nullptr;  // device: per set, kMaxPlanChunks slice counters kEndLine apart
 
     volatile uint64_t *finished(int set) const { return host_words + 16 * set; }
+    volatile uint64_t *started(int set) const { return host_words + 16 * set + 4; }
     volatile uint64_t *timedout(int set) const { return host_words + 16 * set + 8; }
 
     // Whether the last call begun on `set` may have left copies in flight: a wait of its
@@ -217,12 +229,31 @@ class SdmaStager {
         }
     }
 
-    // Submits a job's pieces once its fork event has completed, then records the job handled.
+    // A kernel start (ForkWait::Started) is seen by polling its word, as the fork event is: spin
+    // for kForkSpin, then poll with short sleeps, up to kStartWaitSeconds.
+    static bool wait_started(const volatile uint64_t *word, uint64_t epoch) {
+        const auto t0 = std::chrono::steady_clock::now();
+        for (unsigned i = 1;; ++i) {
+            if (__atomic_load_n(word, __ATOMIC_ACQUIRE) == epoch) return true;
+            __builtin_ia32_pause();
+            if ((i & 255) == 0) {
+                const auto dt = std::chrono::steady_clock::now() - t0;
+                if (dt > kForkSpin) {
+                    if (std::chrono::duration<double>(dt).count() > kStartWaitSeconds) return false;
+                    std::this_thread::sleep_for(std::chrono::microseconds(20));
+                }
+            }
+        }
+    }
+
+    // Submits a job's pieces once its fork has been seen, then records the job handled.
     void submit(const Job &job) {
         SignalSet &ss = sets[job.set];
         static const bool trace = getenv("SPTL_STAGER_TRACE") != nullptr;
         const auto tq = std::chrono::steady_clock::now();
-        bool ok = wait_fork(job.fork);
+        bool ok = !job.fork_wait               ? true
+                  : job.wait == ForkWait::Event ? wait_fork(job.fork)
+                                                : wait_started(job.started, job.epoch);
         const auto tf = std::chrono::steady_clock::now();
         int last_chunk = -2;
         for (const CopyPiece &pc : job.pieces) {
@@ -572,6 +603,7 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
     out->fork = ss.fork;
     out->finished = const_cast<uint64_t *>(s->finished(set));
     out->timedout = const_cast<uint64_t *>(s->timedout(set));
+    out->started = const_cast<uint64_t *>(s->started(set));
     // Cumulative counters of the set, or counters the caller zeroes before the launch.
     out->wg_count = fresh_counts ? fresh_counts : s->counts + (size_t)kSetCountWords * set;
     int groups = 0;
@@ -595,11 +627,12 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
 }
 
 int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> pieces, std::string *err,
-                  bool gated) {
+                  bool gated, ForkWait fork) {
     (void)err;
     {
         std::lock_guard<std::mutex> lk(s->mu);
-        s->queue.push_back(Job{call.set, call.epoch, call.fork, std::move(pieces), gated ? call.slice_ready : nullptr});
+        s->queue.push_back(Job{call.set, call.epoch, call.fork, std::move(pieces), gated ? call.slice_ready : nullptr,
+                               fork, call.started, !gated});
         s->queued.fetch_add(1, std::memory_order_release);
     }
     s->cv.notify_one();

@@ -32,9 +32,10 @@ static_assert(kMaxPieces <= 64, "the GEMM watches a chunk's pieces with one lane
 // 1 to <= 0 when its piece has landed.  join / join_n likewise for the kJoinChunk pieces.  One
 // signal per copy, not one signal per chunk counted down by its pieces: under a tool that
 // intercepts the copies (rocprofv3 --memory-copy-trace), a signal shared by several copies
-// read as complete before all of them had landed, while a signal of one copy stays exact.  `fork` is recorded on the
-// compute stream right before the consuming kernel: once it completes, every earlier
-// operation on the stream has, so the copies may overwrite the gathered buffer.  The kernel
+// read as complete before all of them had landed, while a signal of one copy stays exact.  `fork`, when
+// the caller records it on the compute stream right before the consuming kernel, completes
+// once every earlier operation on the stream has, so the copies may overwrite the gathered
+// buffer; `started` says the same from the kernel's start (ForkWait).  The kernel
 // reports its own end through a word of pinned host memory: the end counters at wg_count
 // count finished workgroups in groups (see ChunkPlan), and the workgroup that completes the
 // count waits for the join and then stores `epoch` to *finished.  (No marker follows the
@@ -49,6 +50,7 @@ struct StageCall {
     uint64_t epoch = 0;
     uint64_t *finished = nullptr;
     uint64_t *timedout = nullptr;   // pinned host word: the kernel stores epoch here if a wait timed out
+    uint64_t *started = nullptr;    // pinned host word: the consuming kernel's tile 0 stores epoch here first
     uint64_t *wg_count = nullptr;
     uint64_t grp_last[kEndGroups] = {};
     uint64_t all_last = 0;
@@ -94,12 +96,19 @@ int stager_begin(SdmaStager *s, const std::vector<CopyPiece> &pieces, int64_t wo
 // now, for calls that have ended) since the last time this returned true.
 bool stager_take_timeouts(SdmaStager *s);
 
-// Queues the pieces; a worker thread submits them to the engines as soon as `call.fork`
-// has completed.  gated: a copy-out call, whose pieces of chunk c are submitted only once the
-// kernel has stored the call's epoch to call.slice_ready[16 c] (bounded wait: after 10 s the
-// stager fails and releases the call's waiters).
+// What the worker waits for before a call's first piece: the fork event recorded on the compute
+// stream (Event), or the consuming kernel's start (Started: its tile 0 stores the call's epoch
+// to call.started before anything else; the kernel starts only once every earlier operation on
+// the stream has completed, as the event would).
+enum class ForkWait { Event, Started };
+
+// Queues the pieces; a worker thread submits them to the engines once the fork (`fork`) has been
+// seen (bounded: after 30 s the stager fails and releases the call's waiters).  gated: a copy-out
+// call, whose pieces of chunk c are submitted only once the kernel has stored the call's epoch to
+// call.slice_ready[16 c] (bounded wait: 10 s); it waits for no fork, because a slice is ready
+// only once the kernel runs.
 int stager_submit(SdmaStager *s, const StageCall &call, std::vector<CopyPiece> pieces, std::string *err,
-                  bool gated = false);
+                  bool gated = false, ForkWait fork = ForkWait::Event);
 
 // Gives back a set reserved by stager_begin whose kernel was never launched.
 void stager_cancel(SdmaStager *s, const StageCall &call);
