@@ -227,9 +227,10 @@ __device__ void cu_copy_and_wait(const ChunkPlan &plan, int bid) {
         const int64_t len = plan.cu_chunk_bytes - off < kCuBlockBytes ? plan.cu_chunk_bytes - off : kCuBlockBytes;
         const char *src = static_cast<const char *>(plan.cu_src[i]) + off;
         char *dst = static_cast<char *>(plan.cu_dst[i]) + off;
-        // a pass issues all of its loads before its stores (4 x 16 bytes per thread, which keeps the
-        // GEMM free of register spills), so each pass waits for memory once
-        constexpr int kU = 4;
+        // a pass issues all of its loads before its stores (8 x 16 bytes per thread: 4 was slower by
+        // about 1 us per call at M = 8192, 16 no faster; neither spills in the four-wave form), so
+        // each pass waits for memory once
+        constexpr int kU = 8;
         const int64_t step = (int64_t)blockDim.x * 16;
         for (int64_t e0 = (int64_t)threadIdx.x * 16; e0 < len; e0 += step * kU) {
             v4u32 v[kU];
